@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark: Hogwild! concurrent-attention decode step on one MI355X.
+
+Workload (synthetic, seeded): QwQ-32B-shaped full decode step — 64 layers,
+4 workers, 40 query / 8 KV heads, head_dim 128, bf16 KV pool, RoPE theta 1e6,
+common cache 16384 tokens, one in-progress block per worker of U[256, 1024]
+tokens (drawn once from the seed).  K, V ~ N(0,1) + a per-channel offset
+N(0, 0.5); q ~ N(0,1).
+
+One step = one pass of the whole path over the resident inputs:
+  build the combined-layout tables on the device from the block lengths,
+  64 x concurrent-attention decode (rotation prologue, split-K loop, merge),
+  append one worker's finished block into the common history (round robin),
+then the harness restores the block lengths so every step sees the same
+workload (the appended tokens sit past the restored common length).
+The step is captured once in a HIP graph and replayed.
+
+Metric: worker-tokens/s per layer = W * layers / step time.  The roofline
+object reports the decode kernel's algorithmic HBM bytes per launch divided
+by its average duration (HIP events around each launch, eager replay of the
+same step) against MI355X's 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--units", type=int, default=0, help="split-K units per kv head (0 = auto)")
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=96,
+                    help="(worker, q-head) pairs of one layer timed on the CPU oracle")
+    ap.add_argument("--kernel-timing-steps", type=int, default=10)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, pool_block_start, K, V, q, pairs):
+    """Time the fp64 oracle (definition form) on a sample of one layer's (worker, head) pairs."""
+    import numpy as np
+    import oracle
+
+    tb, to, ne = oracle.build_combined_tables(wl.common_block, wl.worker_block, wl.lens)
+    lens = np.asarray(wl.lens, np.int32)
+    starts = np.asarray(pool_block_start, np.int64)
+    Kd = K.double().numpy()
+    Vd = V.double().numpy()
+    qd = q.double().numpy()
+    all_pairs = [(w, h) for w in range(wl.W) for h in range(wl.Hq)]
+    step = max(1, len(all_pairs) // pairs)
+    sample = all_pairs[::step][:pairs]
+    t0 = time.perf_counter()
+    for (w, h) in sample:
+        g = h // wl.G
+        _, rc = oracle.attn_one(oracle.FORM_DEFINITION, qd[w, h], Kd[g], Vd[g], tb[w], to[w],
+                                lens, starts, wl.theta)
+        assert rc == 0
+    dt = time.perf_counter() - t0
+    per_pair = dt / len(sample)
+    layer_s = per_pair * wl.W * wl.Hq  # whole layer, single thread
+    return {
+        "value": wl.W / layer_s, "unit": "worker-tokens/s per layer", "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 definition form, {len(sample)} of {wl.W * wl.Hq} (worker, q-head) pairs "
+                  f"of layer 0 ({wl.tokens} tokens each), {dt:.1f} s; scaled to the full layer",
+        "seconds_per_layer": layer_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(multi-GPU sharding is design-only, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_shared_hw_amd import hogwild_attn as hw
+    from decode_attention_shared_hw_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    hw.lib()  # fail loudly if the library is missing
+    path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
+    hw.hw_set_tuning(path, args.units)
+
+    wl = workloads.qwq_step(layers=args.layers)
+    L, W = wl.layers, wl.W
+    pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
+    pool.set_lengths(wl.lens)
+    saved_lens = pool.block_len.clone()
+    host_layer0 = None
+    for layer in range(L):
+        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+        pool.store_layer(layer, K, V)
+        if layer == 0 and not args.no_cpu_baseline:
+            host_layer0 = (K.cpu(), V.cpu())
+        del K, V
+    q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
+    out = torch.zeros(L, W, wl.Hq, wl.D, dtype=torch.float32, device="cuda")
+    tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(W, dtype=torch.int32, device="cuda")
+    ws = hw.alloc_workspace(pool, W, wl.Hq)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    counter = [0]
+
+    def step(events=None):
+        k = counter[0]
+        counter[0] += 1
+        hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, stream)
+        for layer in range(L):
+            if events is not None:
+                events["dec"][layer][0].record(stream)
+            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, stream)
+            if events is not None:
+                events["dec"][layer][1].record(stream)
+        src = wl.worker_block[k % W]
+        if events is not None:
+            events["app"][0].record(stream)
+        hw.hw_block_append(pool, src, wl.common_block, wl.theta, stream)
+        if events is not None:
+            events["app"][1].record(stream)
+        # harness: restore the lengths (an elementwise kernel, graph-safe)
+        torch.add(saved_lens, 0, out=pool.block_len)
+
+    use_graph = not args.no_graph
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        graph = None
+        if use_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step()
+            for _ in range(2):
+                graph.replay()
+            stream.synchronize()
+
+        # ---- timed region: K steps
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            if use_graph:
+                graph.replay()
+            else:
+                step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+
+        # ---- per-launch kernel durations (HIP events around each launch on
+        # the launch stream; a GPU spin first lets the host enqueue ahead)
+        dec_us, app_us = [], []
+        for _ in range(args.kernel_timing_steps):
+            evs = {"dec": [(torch.cuda.Event(enable_timing=True),
+                            torch.cuda.Event(enable_timing=True)) for _ in range(L)],
+                   "app": (torch.cuda.Event(enable_timing=True),
+                           torch.cuda.Event(enable_timing=True))}
+            torch.cuda._sleep(20_000_000)
+            step(evs)
+            stream.synchronize()
+            dec_us += [a.elapsed_time(b) * 1e3 for a, b in evs["dec"]]
+            app_us.append(evs["app"][0].elapsed_time(evs["app"][1]) * 1e3)
+    torch.cuda.synchronize()
+    flags = hw.hw_pool_status(pool)
+
+    ms_per_step = gpu_ms / args.steps
+    step_s = ms_per_step / 1e3
+    value = W * L / step_s  # worker-tokens/s per layer
+    dec_avg = float(np.mean(dec_us))
+    bytes_per_launch = wl.algorithmic_bytes_per_layer()
+    achieved = bytes_per_launch / (dec_avg * 1e-6) / 1e9
+    result = {
+        "metric": "worker-tokens/s per layer + achieved HBM GB/s (% of peak), 4 workers, 16K",
+        "value": value,
+        "unit": "worker-tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q; K,V N(0,1) + per-channel N(0,0.5) offset)",
+        "config": {**workloads.summary(wl), "parallelism": "single GPU",
+                   "step": "tables + 64 x decode + 1 block append (graph replay)"
+                   if use_graph else "tables + 64 x decode + 1 block append (eager)"},
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "decode_mfma<128,2>" if path != hw.PATH_VALU else "decode_valu<bf16>",
+            "bytes_per_launch": bytes_per_launch,
+            "avg_launch_us": dec_avg,
+            "p10_us": float(np.percentile(dec_us, 10)),
+            "p90_us": float(np.percentile(dec_us, 90)),
+        },
+        "us_per_layer": ms_per_step * 1e3 / L,
+        "append_us": float(np.mean(app_us)),
+        "wall_s": wall,
+        "device_status": flags,
+    }
+    if not args.no_cpu_baseline:
+        K0, V0 = host_layer0
+        result["cpu_baseline"] = cpu_baseline(wl, pool.block_start, K0, V0, q[0].cpu(),
+                                              args.cpu_pairs)
+        result["cpu_baseline"]["host"] = platform.processor() or platform.machine()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,280 @@
+// hw_api.hip — the C ABI of libhogwild_attn: argument validation, launch
+// geometry, workspace layout.  Every host-visible error is returned before
+// anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "hw_internal.h"
+
+namespace hw {
+namespace {
+
+constexpr int kMaxUnitsPerHead = 256;
+constexpr int kTargetWorkgroups = 512;  // 2 resident workgroups on each of 256 CUs
+
+int g_path = 0;            // 0 auto, 1 VALU, 2 MFMA
+int g_units_per_head = 0;  // 0 automatic
+
+struct DeviceInfo {
+  int cus = 0;
+  int occ[3][2][2][2] = {};  // [path][dtype][D==128][rows>16] resident workgroups per CU
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+bool g_dev_ready[64] = {};
+
+hw_status device_info(DeviceInfo** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return HW_EHIP;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_dev_ready[dev]) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return HW_EHIP;
+    DeviceInfo& d = g_dev[dev];
+    d.cus = p.multiProcessorCount;
+    for (int path = 1; path <= 2; ++path)
+      for (int dt = 0; dt < 2; ++dt)
+        for (int dd = 0; dd < 2; ++dd)
+          for (int rr = 0; rr < 2; ++rr) {
+            if (path == 2 && dt != HW_BF16) continue;
+            d.occ[path][dt][dd][rr] = decode_blocks_per_cu(path, dt, dd ? 128 : 64, rr ? 32 : 16);
+          }
+    g_dev_ready[dev] = true;
+  }
+  *out = &g_dev[dev];
+  return HW_OK;
+}
+
+hw_status check_pool(const hw_pool* p) {
+  if (!p) return HW_EINVAL;
+  if (p->dtype != HW_F32 && p->dtype != HW_BF16) return HW_EUNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return HW_EUNSUPPORTED;
+  if (p->num_layers < 1 || p->num_kv_heads < 1 || p->reserved != 0) return HW_EINVAL;
+  if (p->num_blocks < 1 || p->num_blocks > HW_MAX_BLOCKS) return HW_ERANGE;
+  if (p->num_slots <= 0 || p->num_slots % HW_TILE_TOKENS != 0) return HW_EINVAL;
+  if (!p->k || !p->v || !p->block_len || !p->status || !p->block_start || !p->block_cap)
+    return HW_EINVAL;
+  for (int b = 0; b < p->num_blocks; ++b) {
+    const int64_t s = p->block_start[b];
+    const int32_t c = p->block_cap[b];
+    if (s < 0 || c < 0 || s % HW_TILE_TOKENS != 0 || c % HW_TILE_TOKENS != 0) return HW_EINVAL;
+    if (s + c > p->num_slots) return HW_EINVAL;
+    for (int o = 0; o < b; ++o) {
+      const int64_t so = p->block_start[o];
+      const int32_t co = p->block_cap[o];
+      if (c > 0 && co > 0 && s < so + co && so < s + c) return HW_EINVAL;  // overlap
+    }
+  }
+  return HW_OK;
+}
+
+int select_path(const hw_pool* p, int rows) {
+  if (g_path == 1) return 1;
+  if (g_path == 2) return 2;
+  return (p->dtype == HW_BF16 && rows <= 32) ? 2 : 1;
+}
+
+int units_per_head_setting(int num_kv_heads) {
+  if (g_units_per_head > 0) return g_units_per_head;
+  int u = kTargetWorkgroups / num_kv_heads;
+  if (u < 1) u = 1;
+  if (u > kMaxUnitsPerHead) u = kMaxUnitsPerHead;
+  return u;
+}
+
+struct WsLayout {
+  size_t sync_off, ml_off, acc_off, total;
+};
+
+WsLayout ws_layout(int hkv, int units, int rows, int D) {
+  WsLayout w;
+  w.sync_off = 0;
+  w.ml_off = 256 * ((2 * static_cast<size_t>(hkv) * 4 + 255) / 256);
+  const size_t ml = static_cast<size_t>(hkv) * units * rows * sizeof(float2);
+  w.acc_off = w.ml_off + 256 * ((ml + 255) / 256);
+  const size_t acc = static_cast<size_t>(hkv) * units * rows * D * sizeof(float);
+  w.total = w.acc_off + acc;
+  return w;
+}
+
+}  // namespace
+}  // namespace hw
+
+using namespace hw;
+
+extern "C" {
+
+int32_t hw_abi_version(void) { return HW_ABI_VERSION; }
+
+const char* hw_status_str(hw_status s) {
+  switch (s) {
+    case HW_OK: return "ok";
+    case HW_EINVAL: return "invalid argument";
+    case HW_ERANGE: return "value outside supported limits";
+    case HW_ECAPACITY: return "block capacity exceeded";
+    case HW_EUNSUPPORTED: return "unsupported dtype or head_dim";
+    case HW_EWORKSPACE: return "workspace missing or too small";
+    case HW_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+hw_status hw_set_tuning(int32_t path, int32_t units_per_head) {
+  if (path < 0 || path > 2 || units_per_head < 0 || units_per_head > kMaxUnitsPerHead)
+    return HW_EINVAL;
+  g_path = path;
+  g_units_per_head = units_per_head;
+  return HW_OK;
+}
+
+size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t num_q_heads) {
+  if (check_pool(pool) != HW_OK) return 0;
+  if (num_workers < 1 || num_workers > HW_MAX_WORKERS || num_q_heads < 1 ||
+      num_q_heads % pool->num_kv_heads != 0)
+    return 0;
+  const int rows = num_workers * (num_q_heads / pool->num_kv_heads);
+  if (rows > HW_MAX_ROWS) return 0;
+  return ws_layout(pool->num_kv_heads, units_per_head_setting(pool->num_kv_heads), rows,
+                   pool->head_dim)
+      .total;
+}
+
+hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                         int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
+                         const int32_t* num_entries, double rope_theta, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  if (!q || !tables || !num_entries || !out) return HW_EINVAL;
+  if (layer < 0 || layer >= pool->num_layers) return HW_EINVAL;
+  if (num_workers < 1 || num_workers > HW_MAX_WORKERS) return HW_ERANGE;
+  if (num_q_heads < 1 || num_q_heads % pool->num_kv_heads != 0) return HW_EINVAL;
+  if (max_entries < 1 || max_entries > HW_MAX_ENTRIES) return HW_ERANGE;
+  if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return HW_EINVAL;
+  const int G = num_q_heads / pool->num_kv_heads;
+  const int rows = num_workers * G;
+  if (rows > HW_MAX_ROWS) return HW_ERANGE;
+  const int path = select_path(pool, rows);
+  if (path == 2 && (pool->dtype != HW_BF16 || rows > 32)) return HW_EUNSUPPORTED;
+  const int P_ws = units_per_head_setting(pool->num_kv_heads);
+  const WsLayout wl = ws_layout(pool->num_kv_heads, P_ws, rows, pool->head_dim);
+  if (!workspace || workspace_bytes < wl.total) return HW_EWORKSPACE;
+
+  DeviceInfo* di = nullptr;
+  st = device_info(&di);
+  if (st != HW_OK) return st;
+  const int occ = di->occ[path][pool->dtype][pool->head_dim == 128][rows > 16];
+  const int64_t capacity = static_cast<int64_t>(occ) * di->cus;
+  if (capacity < pool->num_kv_heads) return HW_ERANGE;
+  // units per head: the setting, bounded by residency (the per-head barrier
+  // needs every workgroup resident) and by the tiles the blocks can hold
+  int64_t max_tiles = 0;
+  for (int b = 0; b < pool->num_blocks; ++b) max_tiles += pool->block_cap[b] / HW_TILE_TOKENS;
+  int64_t P = P_ws;
+  if (P > capacity / pool->num_kv_heads) P = capacity / pool->num_kv_heads;
+  if (P > max_tiles) P = max_tiles;
+  if (P < 1) P = 1;
+
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  const size_t esz = pool->dtype == HW_F32 ? 4 : 2;
+  const int64_t plane = pool->num_slots * pool->head_dim;
+  a.q = q;
+  a.k = static_cast<const char*>(pool->k) +
+        static_cast<int64_t>(layer) * pool->num_kv_heads * plane * esz;
+  a.v = static_cast<const char*>(pool->v) +
+        static_cast<int64_t>(layer) * pool->num_kv_heads * plane * esz;
+  a.block_len = pool->block_len;
+  a.tables = tables;
+  a.num_entries = num_entries;
+  a.out = out;
+  a.status = pool->status;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_sync = reinterpret_cast<uint32_t*>(ws + wl.sync_off);
+  a.ws_ml = reinterpret_cast<float2*>(ws + wl.ml_off);
+  a.ws_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+  a.plane_elems = plane;
+  a.W = num_workers;
+  a.Hq = num_q_heads;
+  a.Hkv = pool->num_kv_heads;
+  a.G = G;
+  a.R = rows;
+  a.E = max_entries;
+  a.NB = pool->num_blocks;
+  a.P = static_cast<int32_t>(P);
+  a.D = pool->head_dim;
+  a.dtype = pool->dtype;
+  const int64_t grid = P * pool->num_kv_heads;
+  a.xcd_map = (grid % 8 == 0) ? 1 : 0;
+  a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
+  for (int b = 0; b < pool->num_blocks; ++b) {
+    a.block_start[b] = pool->block_start[b];
+    a.block_cap[b] = pool->block_cap[b];
+  }
+  for (int i = 0; i < pool->head_dim / 2; ++i)
+    a.inv_freq[i] = pow(rope_theta, -2.0 * i / static_cast<double>(pool->head_dim));
+  const hipError_t e = path == 2
+                           ? launch_decode_mfma(a, static_cast<int>(grid), static_cast<hipStream_t>(stream))
+                           : launch_decode_valu(a, static_cast<int>(grid), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HW_OK : HW_EHIP;
+}
+
+hw_status hw_block_append(const hw_pool* pool, int32_t src_block, int32_t dst_block,
+                          double rope_theta, void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  if (src_block < 0 || src_block >= pool->num_blocks || dst_block < 0 ||
+      dst_block >= pool->num_blocks || src_block == dst_block)
+    return HW_EINVAL;
+  if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return HW_EINVAL;
+  const hipError_t e = launch_append(*pool, src_block, dst_block, rope_theta,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HW_OK : HW_EHIP;
+}
+
+hw_status hw_block_reset(const hw_pool* pool, int32_t block, void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  if (block < 0 || block >= pool->num_blocks) return HW_EINVAL;
+  return launch_reset(pool->block_len, block, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? HW_OK
+             : HW_EHIP;
+}
+
+hw_status hw_build_combined_tables(const hw_pool* pool, int32_t num_workers, int32_t common_block,
+                                   const int32_t* worker_block, hw_entry* tables,
+                                   int32_t* num_entries, void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  if (!worker_block || !tables || !num_entries) return HW_EINVAL;
+  if (num_workers < 1 || num_workers > HW_MAX_WORKERS) return HW_ERANGE;
+  if (num_workers + 1 > HW_MAX_ENTRIES) return HW_ERANGE;
+  if (common_block < 0 || common_block >= pool->num_blocks) return HW_EINVAL;
+  for (int w = 0; w < num_workers; ++w) {
+    const int32_t b = worker_block[w];
+    if (b < 0 || b >= pool->num_blocks || b == common_block) return HW_EINVAL;
+    for (int v = 0; v < w; ++v)
+      if (worker_block[v] == b) return HW_EINVAL;
+  }
+  const hipError_t e = launch_build_tables(pool->block_len, num_workers, common_block, worker_block,
+                                           tables, num_entries, pool->num_blocks,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HW_OK : HW_EHIP;
+}
+
+hw_status hw_pool_status(const hw_pool* pool, int32_t* flags, int32_t clear) {
+  if (!pool || !pool->status || !flags) return HW_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess) return HW_EHIP;
+  if (hipMemcpy(flags, pool->status, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return HW_EHIP;
+  if (clear) {
+    const int32_t zero = 0;
+    if (hipMemcpy(pool->status, &zero, sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess)
+      return HW_EHIP;
+  }
+  return HW_OK;
+}
+
+}  // extern "C"

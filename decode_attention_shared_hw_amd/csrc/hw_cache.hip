@@ -1,0 +1,220 @@
+// hw_cache.hip — cache-manager kernels: combined-layout tables, step append,
+// block reset.  (Hogwild! Inference notes, key design 2.)
+#include <math.h>
+
+#include "hw_internal.h"
+
+namespace hw {
+namespace {
+
+// ------------------------------------------------------------- tables (a1)
+struct TableArgs {
+  const int32_t* block_len;
+  hw_entry* tables;  // [W][W+1]
+  int32_t* num_entries;
+  int32_t W, common, num_blocks;
+  int32_t worker_block[HW_MAX_WORKERS];
+};
+
+// Thread w writes worker w's view: common cache, the other workers' blocks in
+// increasing worker id, its own block last; view_offset = running length sum.
+__global__ void build_tables_kernel(TableArgs a) {
+  const int w = threadIdx.x;
+  if (w >= a.W) return;
+  const int E = a.W + 1;
+  hw_entry* row = a.tables + static_cast<int64_t>(w) * E;
+  int e = 0;
+  int32_t off = 0;
+  auto put = [&](int32_t b) {
+    row[e].block_id = b;
+    row[e].view_offset = off;
+    const int32_t len = a.block_len[b];
+    off += len > 0 ? len : 0;
+    ++e;
+  };
+  put(a.common);
+  for (int v = 0; v < a.W; ++v)
+    if (v != w) put(a.worker_block[v]);
+  put(a.worker_block[w]);
+  a.num_entries[w] = e;
+}
+
+// ------------------------------------------------------------- append (a5)
+struct AppendArgs {
+  void* k;
+  void* v;
+  int32_t* block_len;
+  int64_t plane_elems;  // num_slots * D
+  int64_t start_src, start_dst;
+  int32_t cap_src, cap_dst;
+  int32_t src, dst;
+  int32_t D, dtype;
+  int32_t tiles_per_plane;  // dst tiles a run of up to cap_src tokens can touch
+  double inv_freq[kMaxHalf];
+};
+
+// Correctly rounded double -> bf16 (ties to even), as raw bits.
+__device__ uint16_t f64_to_bf16_bits(double x) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t e = static_cast<uint32_t>((u >> 52) & 0x7ffu);
+  if (e == 0x7ffu) return static_cast<uint16_t>(__float_as_uint(static_cast<float>(x)) >> 16);
+  double y;
+  if (e < 1023u - 126u) {
+    // below the smallest normal bf16: the grid step is 2^-133
+    y = rint(x * 0x1p133) * 0x1p-133;
+  } else {
+    // keep 8 significant bits: drop 45 of the 52 fraction bits, ties to even
+    const uint64_t lsb = (u >> 45) & 1u;
+    u += 0x00000FFFFFFFFFFFull + lsb;  // 2^44 - 1 + lsb
+    u &= ~0x00001FFFFFFFFFFFull;       // clear the 45 dropped bits
+    y = __longlong_as_double(static_cast<long long>(u));
+  }
+  // y is a bf16 value (or beyond its range, which float turns into inf)
+  return static_cast<uint16_t>(__float_as_uint(static_cast<float>(y)) >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ double load_f64(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ double load_f64<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ double load_f64<uint16_t>(const uint16_t* p, int64_t i) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[i]) << 16));
+}
+__device__ __forceinline__ void store_rounded(float* p, int64_t i, double x) {
+  p[i] = static_cast<float>(x);
+}
+__device__ __forceinline__ void store_rounded(uint16_t* p, int64_t i, double x) {
+  p[i] = f64_to_bf16_bits(x);
+}
+
+// One workgroup per (layer*kv head plane, destination tile).  A src key at
+// local position j moves to dst position len_dst + j: rotating it by len_dst
+// re-encodes it there (rho(rho(x, j), n) = rho(x, j + n)).
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+#pragma clang fp contract(off)
+  const int tid = threadIdx.x;
+  const int64_t plane = blockIdx.x / a.tiles_per_plane;
+  const int k = blockIdx.x - static_cast<int>(plane * a.tiles_per_plane);
+  const int32_t ls = a.block_len[a.src];
+  const int32_t ld = a.block_len[a.dst];
+  if (ls <= 0 || ld < 0 || ls > a.cap_src || static_cast<int64_t>(ld) + ls > a.cap_dst) return;
+  const int64_t first = a.start_dst + ld;  // first destination slot
+  const int64_t last = first + ls;
+  const int64_t t0 = ((first >> 5) + k) << 5;
+  const int64_t s_begin = first > t0 ? first : t0;
+  const int64_t s_end = last < t0 + 32 ? last : t0 + 32;
+  if (s_begin >= s_end) return;
+  const int D = a.D, half = D / 2;
+  __shared__ double cs[2 * kMaxHalf];
+  if (tid < half) {
+    double s, c;
+    sincos(static_cast<double>(ld) * a.inv_freq[tid], &s, &c);
+    cs[2 * tid] = c;
+    cs[2 * tid + 1] = s;
+  }
+  __syncthreads();
+  T* kp = static_cast<T*>(a.k) + plane * a.plane_elems;
+  T* vp = static_cast<T*>(a.v) + plane * a.plane_elems;
+  const int n = static_cast<int>(s_end - s_begin);
+  for (int x = tid; x < n * half; x += 256) {
+    const int64_t sd = s_begin + x / half;
+    const int i = x % half;
+    const int64_t ss = a.start_src + (sd - first);
+    const double x0 = load_f64(kp, key_offset(ss, i, D));
+    const double x1 = load_f64(kp, key_offset(ss, i + half, D));
+    const double c = cs[2 * i], s = cs[2 * i + 1];
+    const double y0 = x0 * c - x1 * s;
+    const double y1 = x1 * c + x0 * s;
+    store_rounded(kp, key_offset(sd, i, D), y0);
+    store_rounded(kp, key_offset(sd, i + half, D), y1);
+  }
+  for (int x = tid; x < n * D; x += 256) {
+    const int64_t sd = s_begin + x / D;
+    const int d = x % D;
+    const int64_t ss = a.start_src + (sd - first);
+    vp[value_offset(sd, d, D)] = vp[value_offset(ss, d, D)];
+  }
+}
+
+// Runs after the copy on the same stream: moves the lengths, or reports.
+__global__ void append_finish_kernel(int32_t* block_len, int32_t* status, int32_t src,
+                                     int32_t dst, int32_t cap_src, int32_t cap_dst) {
+  if (threadIdx.x != 0) return;
+  const int32_t ls = block_len[src];
+  const int32_t ld = block_len[dst];
+  if (ls < 0 || ld < 0 || ls > cap_src || ld > cap_dst) {
+    atomicOr(status, HW_DEV_BAD_LENGTH);
+    return;
+  }
+  if (static_cast<int64_t>(ld) + ls > cap_dst) {
+    atomicOr(status, HW_DEV_APPEND_OVERFLOW);
+    return;
+  }
+  block_len[dst] = ld + ls;
+  block_len[src] = 0;
+}
+
+__global__ void reset_kernel(int32_t* block_len, int32_t block) {
+  if (threadIdx.x == 0) block_len[block] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_build_tables(int32_t* block_len, int32_t W, int32_t common,
+                               const int32_t* worker_block, hw_entry* tables,
+                               int32_t* num_entries, int32_t num_blocks, hipStream_t s) {
+  TableArgs a{};
+  a.block_len = block_len;
+  a.tables = tables;
+  a.num_entries = num_entries;
+  a.W = W;
+  a.common = common;
+  a.num_blocks = num_blocks;
+  for (int w = 0; w < W; ++w) a.worker_block[w] = worker_block[w];
+  hipLaunchKernelGGL(build_tables_kernel, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double theta,
+                         hipStream_t s) {
+  AppendArgs a{};
+  a.k = pool.k;
+  a.v = pool.v;
+  a.block_len = pool.block_len;
+  a.plane_elems = pool.num_slots * pool.head_dim;
+  a.start_src = pool.block_start[src];
+  a.start_dst = pool.block_start[dst];
+  a.cap_src = pool.block_cap[src];
+  a.cap_dst = pool.block_cap[dst];
+  a.src = src;
+  a.dst = dst;
+  a.D = pool.head_dim;
+  a.dtype = pool.dtype;
+  a.tiles_per_plane = a.cap_src / kTile + 1;
+  for (int i = 0; i < pool.head_dim / 2; ++i)
+    a.inv_freq[i] = pow(theta, -2.0 * i / static_cast<double>(pool.head_dim));
+  const int64_t planes = static_cast<int64_t>(pool.num_layers) * pool.num_kv_heads;
+  const int64_t grid = planes * a.tiles_per_plane;
+  if (a.cap_src > 0 && grid > 0) {
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (pool.dtype == HW_F32)
+      hipLaunchKernelGGL(append_kernel<float>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                         a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(append_finish_kernel, dim3(1), dim3(64), 0, s, pool.block_len, pool.status,
+                     src, dst, a.cap_src, a.cap_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(int32_t* block_len, int32_t block, hipStream_t s) {
+  hipLaunchKernelGGL(reset_kernel, dim3(1), dim3(64), 0, s, block_len, block);
+  return hipGetLastError();
+}
+
+}  // namespace hw

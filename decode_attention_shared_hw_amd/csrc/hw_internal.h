@@ -1,0 +1,72 @@
+// hw_internal.h — shared definitions of libhogwild_attn's HIP sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hogwild_attn.h"
+
+namespace hw {
+
+constexpr int kTile = HW_TILE_TOKENS;  // tokens per pool tile
+constexpr int kThreads = 256;          // threads per decode workgroup (4 waves)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxHalf = 64;           // head_dim / 2 upper bound
+
+// Extra sticky bit (internal): a workgroup waited too long at the per-head
+// barrier; the workspace sync words must be zeroed again.
+constexpr int32_t kDevSyncTimeout = 16;
+
+// Element offset of key (slot, d) inside one (layer, kv head) plane.  Tiles of
+// 32 slots; inside a tile: [half t/16][chunk d/8][token t%16][d%8].
+__host__ __device__ inline int64_t key_offset(int64_t slot, int d, int D) {
+  const int64_t tile = slot >> 5;
+  const int t = static_cast<int>(slot & 31);
+  return tile * 32 * D + (t >> 4) * 16 * D + (d >> 3) * 128 + (t & 15) * 8 + (d & 7);
+}
+
+// Element offset of value (slot, d): [group (t%16)/4][d][8 tokens], token
+// order inside a group (t/16)*4 + t%4.
+__host__ __device__ inline int64_t value_offset(int64_t slot, int d, int D) {
+  const int64_t tile = slot >> 5;
+  const int t = static_cast<int>(slot & 31);
+  return tile * 32 * D + ((t & 15) >> 2) * 8 * D + d * 8 + ((t >> 4) << 2) + (t & 3);
+}
+
+// Kernel arguments of the fused decode kernels (passed by value).
+struct DecodeArgs {
+  const void* q;            // [W][Hq][D] pool dtype
+  const void* k;            // plane of (layer, kv head 0)
+  const void* v;
+  const int32_t* block_len; // [NB]
+  const hw_entry* tables;   // [W][E]
+  const int32_t* num_entries;
+  float* out;               // [W][Hq][D]
+  int32_t* status;
+  float2* ws_ml;            // [Hkv][P][R] (m, l) partials
+  float* ws_acc;            // [Hkv][P][R][D] partial accumulators
+  uint32_t* ws_sync;        // [2][Hkv] arrival / departure counters
+  int64_t plane_elems;      // num_slots * D
+  int32_t W, Hq, Hkv, G, R, E, NB, P, D;
+  int32_t dtype;            // HW_F32 / HW_BF16
+  int32_t xcd_map;          // 1: map consecutive work units to one XCD
+  float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
+  int64_t block_start[HW_MAX_BLOCKS];
+  int32_t block_cap[HW_MAX_BLOCKS];
+  double inv_freq[kMaxHalf];  // theta^(-2i/D), i < D/2
+};
+
+// Launchers (hw_decode.hip).
+hipError_t launch_decode_valu(const DecodeArgs& a, int grid, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s);
+int decode_blocks_per_cu(int path, int dtype, int D, int rows);
+
+// Launchers (hw_cache.hip).
+hipError_t launch_build_tables(int32_t* block_len, int32_t W, int32_t common,
+                               const int32_t* worker_block, hw_entry* tables,
+                               int32_t* num_entries, int32_t num_blocks, hipStream_t s);
+hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double theta,
+                         hipStream_t s);
+hipError_t launch_reset(int32_t* block_len, int32_t block, hipStream_t s);
+
+}  // namespace hw

@@ -1,0 +1,231 @@
+"""Python binding of libhogwild_attn (ctypes): the C ABI's calls under the same names.
+
+Argument marshalling only: torch tensors are passed as device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the shared library is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import layout
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhogwild_attn.so")
+
+HW_OK, HW_EINVAL, HW_ERANGE, HW_ECAPACITY, HW_EUNSUPPORTED, HW_EWORKSPACE, HW_EHIP = range(7)
+HW_DEV_BAD_ENTRY, HW_DEV_BAD_LENGTH, HW_DEV_NO_TOKENS, HW_DEV_APPEND_OVERFLOW = 1, 2, 4, 8
+HW_DEV_SYNC_TIMEOUT = 16
+HW_F32, HW_BF16 = 0, 1
+HW_TILE_TOKENS = 32
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+
+
+class HWError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {hw_status_str(code)} (code {code})")
+
+
+class hw_entry(ctypes.Structure):
+    _fields_ = [("block_id", ctypes.c_int32), ("view_offset", ctypes.c_int32)]
+
+
+class hw_pool(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("num_slots", ctypes.c_int64),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("block_len", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+        ("block_start", ctypes.c_void_p),
+        ("block_cap", ctypes.c_void_p),
+    ]
+
+
+EXPORTED = [
+    "hw_abi_version", "hw_status_str", "hw_attn_workspace_bytes", "hw_attn_decode",
+    "hw_block_append", "hw_block_reset", "hw_build_combined_tables", "hw_pool_status",
+    "hw_set_tuning",
+]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not built: run decode_attention_shared_hw_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, d, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
+                              ctypes.c_size_t)
+        PP = ctypes.POINTER(hw_pool)
+        L.hw_abi_version.restype = i32
+        L.hw_abi_version.argtypes = []
+        L.hw_status_str.restype = ctypes.c_char_p
+        L.hw_status_str.argtypes = [i32]
+        L.hw_attn_workspace_bytes.restype = sz
+        L.hw_attn_workspace_bytes.argtypes = [PP, i32, i32]
+        L.hw_attn_decode.restype = i32
+        L.hw_attn_decode.argtypes = [PP, i32, P, i32, i32, P, i32, P, d, P, P, sz, P]
+        L.hw_block_append.restype = i32
+        L.hw_block_append.argtypes = [PP, i32, i32, d, P]
+        L.hw_block_reset.restype = i32
+        L.hw_block_reset.argtypes = [PP, i32, P]
+        L.hw_build_combined_tables.restype = i32
+        L.hw_build_combined_tables.argtypes = [PP, i32, i32, P, P, P, P]
+        L.hw_pool_status.restype = i32
+        L.hw_pool_status.argtypes = [PP, P, i32]
+        L.hw_set_tuning.restype = i32
+        L.hw_set_tuning.argtypes = [i32, i32]
+        _lib = L
+    return _lib
+
+
+def _check(code: int, where: str):
+    if code != HW_OK:
+        raise HWError(code, where)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+class Pool:
+    """A K/V block pool spanning `num_layers` layers, owned by torch tensors.
+
+    k, v: device tensors [num_layers, num_kv_heads, num_slots, head_dim] in the
+    library's tile layout (see `layout`); block_len / status: device int32.
+    block b owns slots [block_start[b], block_start[b] + block_cap[b]).
+    """
+
+    def __init__(self, num_layers, num_kv_heads, head_dim, block_caps, dtype=torch.bfloat16,
+                 device="cuda", fill=None):
+        caps = [int(c) for c in block_caps]
+        if any(c % HW_TILE_TOKENS for c in caps):
+            raise ValueError("block capacities must be multiples of 32")
+        starts, s = [], 0
+        for c in caps:
+            starts.append(s)
+            s += c
+        self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
+        self.num_slots = max(s, HW_TILE_TOKENS)
+        self.dtype = dtype
+        self.hw_dtype = {torch.bfloat16: HW_BF16, torch.float32: HW_F32}[dtype]
+        shape = (num_layers, num_kv_heads, self.num_slots, head_dim)
+        if fill is None:
+            self.k = torch.zeros(shape, dtype=dtype, device=device)
+            self.v = torch.zeros(shape, dtype=dtype, device=device)
+        else:
+            self.k = torch.full(shape, fill, dtype=dtype, device=device)
+            self.v = torch.full(shape, fill, dtype=dtype, device=device)
+        self.block_len = torch.zeros(len(caps), dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self._start = (ctypes.c_int64 * len(caps))(*starts)
+        self._cap = (ctypes.c_int32 * len(caps))(*caps)
+        self.block_start = starts
+        self.block_cap = caps
+        self.desc = hw_pool(self.hw_dtype, num_layers, num_kv_heads, head_dim, len(caps), 0,
+                            self.num_slots, self.k.data_ptr(), self.v.data_ptr(),
+                            self.block_len.data_ptr(), self.status.data_ptr(),
+                            ctypes.cast(self._start, ctypes.c_void_p),
+                            ctypes.cast(self._cap, ctypes.c_void_p))
+
+    @property
+    def num_blocks(self):
+        return len(self.block_cap)
+
+    # -- layout marshalling (index permutations only) --
+    def store_layer(self, layer, k_logical, v_logical):
+        """Write logical [Hkv, num_slots, D] K/V (pool dtype) into `layer`."""
+        self.k[layer].copy_(layout.pack_keys(k_logical.to(self.k.device, self.dtype)))
+        self.v[layer].copy_(layout.pack_values(v_logical.to(self.v.device, self.dtype)))
+
+    def load_layer(self, layer):
+        """Logical [Hkv, num_slots, D] copies of `layer`'s K/V."""
+        return layout.unpack_keys(self.k[layer]), layout.unpack_values(self.v[layer])
+
+    def set_lengths(self, lens):
+        self.block_len.copy_(torch.as_tensor(lens, dtype=torch.int32))
+
+
+def hw_abi_version() -> int:
+    return int(lib().hw_abi_version())
+
+
+def hw_status_str(code: int) -> str:
+    return lib().hw_status_str(int(code)).decode()
+
+
+def hw_set_tuning(path: int = PATH_AUTO, units_per_head: int = 0):
+    _check(lib().hw_set_tuning(int(path), int(units_per_head)), "hw_set_tuning")
+
+
+def hw_attn_workspace_bytes(pool: Pool, num_workers: int, num_q_heads: int) -> int:
+    return int(lib().hw_attn_workspace_bytes(ctypes.byref(pool.desc), num_workers, num_q_heads))
+
+
+def alloc_workspace(pool: Pool, num_workers: int, num_q_heads: int) -> torch.Tensor:
+    """Zeroed workspace (the per-head sync words must start at zero once)."""
+    n = hw_attn_workspace_bytes(pool, num_workers, num_q_heads)
+    if n == 0:
+        raise HWError(HW_EINVAL, "hw_attn_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=pool.k.device)
+
+
+def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
+                   num_entries: torch.Tensor, rope_theta: float, out: torch.Tensor,
+                   workspace: torch.Tensor, stream=None):
+    """q [W][Hq][D] (pool dtype), tables int32 [W][E][2], num_entries int32 [W], out fp32 [W][Hq][D]."""
+    W, Hq, _ = q.shape
+    code = lib().hw_attn_decode(ctypes.byref(pool.desc), int(layer), _ptr(q), W, Hq, _ptr(tables),
+                                int(tables.shape[1]), _ptr(num_entries), float(rope_theta),
+                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(code, "hw_attn_decode")
+
+
+def hw_block_append(pool: Pool, src_block: int, dst_block: int, rope_theta: float, stream=None):
+    _check(lib().hw_block_append(ctypes.byref(pool.desc), int(src_block), int(dst_block),
+                                 float(rope_theta), _stream(stream)), "hw_block_append")
+
+
+def hw_block_reset(pool: Pool, block: int, stream=None):
+    _check(lib().hw_block_reset(ctypes.byref(pool.desc), int(block), _stream(stream)),
+           "hw_block_reset")
+
+
+def hw_build_combined_tables(pool: Pool, num_workers: int, common_block: int, worker_block,
+                             tables: torch.Tensor, num_entries: torch.Tensor, stream=None):
+    """tables: device int32 [W][W+1][2]; num_entries: device int32 [W]."""
+    wb = (ctypes.c_int32 * num_workers)(*[int(b) for b in worker_block])
+    _check(lib().hw_build_combined_tables(ctypes.byref(pool.desc), int(num_workers),
+                                          int(common_block), ctypes.cast(wb, ctypes.c_void_p),
+                                          _ptr(tables), _ptr(num_entries), _stream(stream)),
+           "hw_build_combined_tables")
+
+
+def hw_pool_status(pool: Pool, clear: bool = False) -> int:
+    flags = ctypes.c_int32(0)
+    _check(lib().hw_pool_status(ctypes.byref(pool.desc), ctypes.byref(flags), int(bool(clear))),
+           "hw_pool_status")
+    return int(flags.value)

@@ -1,0 +1,164 @@
+"""Seeded synthetic workloads shaped like the pages' runs (no method arithmetic here).
+
+Every input is drawn from torch generators seeded per (seed, layer, tensor), so
+a workload can be regenerated on the CPU (for the oracle) or on the GPU (for
+speed) — the same draw is then copied to the other side, never regenerated.
+
+Shapes (QwQ-32B / Qwen3-8B attention shapes; the pages' throughput table uses
+1, 2, 4 workers at 1024 / 8192 / 16384 tokens):
+  tiny      2 workers, 4q/2kv heads, D=64, fp32, theta 1e4; common 256, blocks 64+64
+  qwq_layer 2 workers, 40q/8kv, D=128, bf16, theta 1e6; common 8192, blocks 512+512
+  qwq_step  64 layers, 4 workers, common 16384, worker blocks U[256,1024]
+  sweep     4/2/1 workers, total view 1024/8192/16384 (85% common)
+  qwen3_loop 36 layers, 32q/8kv, 4 workers, common from 32768, appends every 64 steps
+Values: q ~ N(0,1); K, V ~ N(0,1) + a fixed per-(layer, kv head, channel)
+offset ~ N(0, 0.5) for the bf16 shapes (separate offsets for K and V).
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+import torch
+
+TILE = 32
+
+
+def round_up(x: int, m: int = TILE) -> int:
+    return (int(x) + m - 1) // m * m
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    W: int
+    Hq: int
+    Hkv: int
+    D: int
+    theta: float
+    dtype: torch.dtype
+    layers: int
+    lens: list            # [common, worker 0, ..., worker W-1]
+    caps: list            # capacities, multiples of 32
+    offset_sigma: float   # std of the per-channel K/V mean offset (0: none)
+    seed: int
+
+    @property
+    def G(self):
+        return self.Hq // self.Hkv
+
+    @property
+    def rows(self):
+        return self.W * self.G
+
+    @property
+    def common_block(self):
+        return 0
+
+    @property
+    def worker_block(self):
+        return list(range(1, self.W + 1))
+
+    @property
+    def tokens(self):
+        """Unique visible tokens per layer (every worker sees every block)."""
+        return int(sum(self.lens))
+
+    def kv_bytes_per_layer(self):
+        es = 2 if self.dtype == torch.bfloat16 else 4
+        return self.tokens * self.Hkv * self.D * 2 * es
+
+    def algorithmic_bytes_per_layer(self):
+        """Each visible K/V token read once + q read + out (fp32) written."""
+        es = 2 if self.dtype == torch.bfloat16 else 4
+        return self.kv_bytes_per_layer() + self.W * self.Hq * self.D * (es + 4)
+
+
+def tiny(seed: int = 1001) -> Workload:
+    lens = [256, 64, 64]
+    return Workload("tiny_fp32_2w", 2, 4, 2, 64, 1e4, torch.float32, 1, lens,
+                    [round_up(x) for x in lens], 0.0, seed)
+
+
+def qwq_layer(seed: int = 1002) -> Workload:
+    lens = [8192, 512, 512]
+    return Workload("qwq32b_layer_bf16_2w", 2, 40, 8, 128, 1e6, torch.bfloat16, 1, lens,
+                    [round_up(x) for x in lens], 0.5, seed)
+
+
+def qwq_step(seed: int = 1003, layers: int = 64, append_room: int = 1024) -> Workload:
+    rng = np.random.default_rng(seed)
+    workers = [int(x) for x in rng.integers(256, 1025, size=4)]
+    lens = [16384] + workers
+    caps = [round_up(16384 + append_room)] + [1024] * 4
+    return Workload("qwq32b_step_bf16_4w_16k", 4, 40, 8, 128, 1e6, torch.bfloat16, layers, lens,
+                    caps, 0.5, seed)
+
+
+def sweep(C: int, W: int, seed: int = 1004) -> Workload:
+    common = 85 * C // 100
+    rest = C - common
+    per = [rest // W + (1 if i < rest % W else 0) for i in range(W)]
+    lens = [common] + per
+    return Workload(f"sweep_{C}_{W}w", W, 40, 8, 128, 1e6, torch.bfloat16, 1, lens,
+                    [round_up(x) for x in lens], 0.5, seed)
+
+
+def qwen3_loop(seed: int = 1005, layers: int = 36, common0: int = 32768, steps: int = 2048,
+               private_cap: int = 512) -> Workload:
+    rng = np.random.default_rng(seed)
+    lens = [common0] + [int(x) for x in rng.integers(0, 64, size=4)]
+    common_cap = round_up(common0 + steps * 4 + 4 * private_cap)
+    return Workload("qwen3_8b_loop_bf16_4w", 4, 32, 8, 128, 1e6, torch.bfloat16, layers, lens,
+                    [common_cap] + [private_cap] * 4, 0.5, seed)
+
+
+def _gen(seed: int, layer: int, tag: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1_000_003 + layer * 97 + tag) & 0x7FFF_FFFF_FFFF_FFFF)
+    return g
+
+
+def make_q(wl: Workload, layer: int, device="cpu") -> torch.Tensor:
+    """q [W][Hq][D] in the pool dtype, N(0,1)."""
+    g = _gen(wl.seed, layer, 1, device)
+    q = torch.randn(wl.W, wl.Hq, wl.D, generator=g, device=device, dtype=torch.float32)
+    return q.to(wl.dtype)
+
+
+def make_kv(wl: Workload, layer: int, num_slots: int, device="cpu", poison_unused: bool = False,
+            block_start=None):
+    """Logical K, V [Hkv][num_slots][D] in the pool dtype.
+
+    poison_unused: slots outside every block's current length hold NaN (they
+    must never reach a result).
+    """
+    gk = _gen(wl.seed, layer, 2, device)
+    gv = _gen(wl.seed, layer, 3, device)
+    shape = (wl.Hkv, num_slots, wl.D)
+    K = torch.randn(shape, generator=gk, device=device, dtype=torch.float32)
+    V = torch.randn(shape, generator=gv, device=device, dtype=torch.float32)
+    if wl.offset_sigma > 0:
+        go = _gen(wl.seed, layer, 4, device)
+        K += wl.offset_sigma * torch.randn(wl.Hkv, 1, wl.D, generator=go, device=device)
+        V += wl.offset_sigma * torch.randn(wl.Hkv, 1, wl.D, generator=go, device=device)
+    if poison_unused:
+        starts = block_start if block_start is not None else np.cumsum([0] + wl.caps[:-1])
+        used = torch.zeros(num_slots, dtype=torch.bool, device=device)
+        for b, n in enumerate(wl.lens):
+            used[int(starts[b]):int(starts[b]) + int(n)] = True
+        K[:, ~used] = float("nan")
+        V[:, ~used] = float("nan")
+    return K.to(wl.dtype), V.to(wl.dtype)
+
+
+def summary(wl: Workload) -> dict:
+    return {
+        "workload": wl.name, "workers": wl.W, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+        "head_dim": wl.D, "rope_theta": wl.theta, "layers": wl.layers,
+        "block_lens": [int(x) for x in wl.lens], "tokens": wl.tokens,
+        "kv_dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+    }
+
+
+__all__ = ["Workload", "tiny", "qwq_layer", "qwq_step", "sweep", "qwen3_loop", "make_q", "make_kv",
+           "summary", "round_up"]

@@ -1,0 +1,214 @@
+/*
+ * hogwild_attn.h — libhogwild_attn: Hogwild! concurrent-attention decode and
+ * step-completion block append on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (Hogwild! Inference, NeurIPS 2025 notes):
+ *  - Several workers share one KV cache made of blocks.  Worker w's view is a
+ *    list of (block, view_offset) entries; in the combined layout (key design
+ *    2) it is [common cache, the other workers' unfinished steps in worker
+ *    order, w's own step].
+ *  - Every block stores its keys at local positions 0..len-1 (storage
+ *    convention in the method list); the real position of token j of a block
+ *    in w's view is view_offset + j.
+ *  - Attention rotates only the single query token (key design 1):
+ *      rho(q, i_q)[rho(A,i_A) (+) rho(B,i_B) ...]
+ *        = rho(q, i_q - i_A) A (+) rho(q, i_q - i_B) B ...
+ *    i.e. each block is scored with the query rotated by i_q - view_offset,
+ *    and one softmax runs over the concatenation of all blocks' scores
+ *    (omica.com.cn news 1114328, sec. 3.2: scores / sqrt(dim), softmax over
+ *    concat, weighted sum of V).
+ *  - A finished step's KV is rotated and moved into the shared history
+ *    (key design 2, last paragraph).
+ *
+ * Conventions fixed where the pages are silent:
+ *  - RoPE pairs element i with i + D/2 (rotate-half, news 1114328 sec. 2.1),
+ *    angle = position * theta^(-2i/D), theta passed by the caller.
+ *  - i_q[w] = max over w's entries with len > 0 of (view_offset + len) - 1:
+ *    the query's own K/V is already in its block, as in ordinary decode.
+ *  - Softmax scale 1/sqrt(D); no mask inside a view; kv head of q-head h is
+ *    h / (Hq / Hkv).
+ *  - `out` is fp32 whatever the pool type.
+ *
+ * Memory: every pointer marked (device) is device memory on the current HIP
+ * device; (host) is host memory read during the call.  The caller owns every
+ * buffer.  No call allocates, frees or synchronizes, except hw_pool_status().
+ * All device work is enqueued on `stream` (a hipStream_t; NULL = default
+ * stream) and calls return after enqueueing.
+ *
+ * Errors: problems visible on the host are reported by the return code and
+ * then nothing is enqueued.  Problems only visible on the device (lengths
+ * read from device memory, device-resident tables) set bits in the pool's
+ * sticky status word (HW_DEV_*) and the affected work is skipped: decode rows
+ * of an affected worker are written as zeros, an overflowing append moves
+ * nothing.  hw_pool_status() reads and optionally clears that word.
+ */
+#ifndef HOGWILD_ATTN_H
+#define HOGWILD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HW_ABI_VERSION 1
+
+/* Tokens per tile of the pool layout; block starts and capacities are multiples of it. */
+#define HW_TILE_TOKENS 32
+#define HW_MAX_BLOCKS 64   /* blocks per pool                          */
+#define HW_MAX_WORKERS 32  /* workers per decode call                  */
+#define HW_MAX_ROWS 64     /* num_workers * (num_q_heads / num_kv_heads) */
+#define HW_MAX_ENTRIES 64  /* entries per worker table                 */
+
+typedef int32_t hw_status;
+#define HW_OK 0
+#define HW_EINVAL 1        /* null pointer, bad shape, bad id, src == dst      */
+#define HW_ERANGE 2        /* a value outside the supported limits above       */
+#define HW_ECAPACITY 3     /* append cannot fit by the host-known capacities   */
+#define HW_EUNSUPPORTED 4  /* dtype / head_dim combination not built           */
+#define HW_EWORKSPACE 5    /* workspace missing or smaller than required       */
+#define HW_EHIP 6          /* a HIP runtime call failed                        */
+
+/* Device-detected conditions (sticky bits of the pool status word). */
+#define HW_DEV_BAD_ENTRY 1       /* table entry with block id out of range, or a block listed twice */
+#define HW_DEV_BAD_LENGTH 2      /* block_len < 0 or > capacity                                      */
+#define HW_DEV_NO_TOKENS 4       /* a worker sees no token; its rows are written as zeros            */
+#define HW_DEV_APPEND_OVERFLOW 8 /* len_dst + len_src > cap_dst at run time; nothing was moved        */
+
+/* Storage types. */
+#define HW_F32 0
+#define HW_BF16 1
+
+/* One entry of a worker's view: block id and where the block starts in the view. */
+typedef struct {
+  int32_t block_id;
+  int32_t view_offset;
+} hw_entry;
+
+/*
+ * A K/V block pool spanning all layers of a model.
+ *
+ * Storage.  k and v each hold num_layers * num_kv_heads planes of num_slots
+ * slots of head_dim elements of `dtype`; plane (layer l, kv head g) starts at
+ * element (l * num_kv_heads + g) * num_slots * head_dim.  Block b owns slots
+ * [block_start[b], block_start[b] + block_cap[b]) of every plane; its token j
+ * (local position j, 0 <= j < block_len[b]) is slot block_start[b] + j.
+ *
+ * Within a plane, slots are grouped in tiles of 32 (tile T = slot / 32,
+ * t = slot % 32, tile base = T * 32 * head_dim elements) laid out to match the
+ * gfx950 16x16x32 bf16 MFMA operand fragments, so that every wave load is one
+ * contiguous 16-byte vector per lane:
+ *   key   element (slot, d) at tile base + (t / 16) * 16 * D + (d / 8) * 128
+ *                                       + (t % 16) * 8 + d % 8
+ *   value element (slot, d) at tile base + ((t % 16) / 4) * 8 * D + d * 8
+ *                                       + (t / 16) * 4 + t % 4
+ * The same layout is used for fp32 pools.
+ *
+ * block_len is device memory and is changed by hw_block_append /
+ * hw_block_reset; block_start and block_cap are host arrays and fixed for the
+ * pool's lifetime.  status is a device int32 holding the sticky HW_DEV_* bits;
+ * the caller zeroes it once.
+ */
+typedef struct {
+  int32_t dtype;        /* HW_F32 or HW_BF16                               */
+  int32_t num_layers;   /* >= 1                                            */
+  int32_t num_kv_heads; /* >= 1                                            */
+  int32_t head_dim;     /* 64 or 128                                       */
+  int32_t num_blocks;   /* 1 .. HW_MAX_BLOCKS                              */
+  int32_t reserved;     /* must be 0                                       */
+  int64_t num_slots;    /* slots per plane, multiple of 32                 */
+  void* k;              /* (device) key planes                             */
+  void* v;              /* (device) value planes                           */
+  int32_t* block_len;   /* (device) [num_blocks] current lengths           */
+  int32_t* status;      /* (device) sticky HW_DEV_* bits                   */
+  const int64_t* block_start; /* (host) [num_blocks], multiples of 32      */
+  const int32_t* block_cap;   /* (host) [num_blocks], multiples of 32      */
+} hw_pool;
+
+/* Returns HW_ABI_VERSION. */
+int32_t hw_abi_version(void);
+
+/* Static text for a hw_status code. */
+const char* hw_status_str(hw_status status);
+
+/*
+ * Bytes of device workspace hw_attn_decode needs for this pool and call
+ * shape under the current tuning (split partials for the log-sum-exp merge).
+ * Returns 0 if the shape is invalid.  The workspace needs no initialisation.
+ */
+size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t num_q_heads);
+
+/*
+ * One layer of concurrent-attention decode (key design 1; news 1114328 sec. 3.2).
+ *
+ *   q            (device) [num_workers][num_q_heads][head_dim], pool dtype: the
+ *                one current query token of each worker, before RoPE.
+ *   tables       (device) [num_workers][max_entries] views; worker w uses its
+ *                first num_entries[w] entries.  A block not listed is invisible
+ *                to w; a block may be listed at most once per worker.
+ *   num_entries  (device) [num_workers].
+ *   out          (device) [num_workers][num_q_heads][head_dim] fp32.
+ *   workspace    (device) >= hw_attn_workspace_bytes(pool, W, Hq) bytes.
+ *
+ * For each worker w and q-head h (kv head g = h / (Hq/Hkv)):
+ *   out[w][h] = sum over entries (b, off) and j < len_b of
+ *       softmax_j( rho(q[w][h], i_q[w] - off) . K_b[g][j] / sqrt(D) ) V_b[g][j].
+ * Host-checked errors: HW_EINVAL (null pointers, num_q_heads % num_kv_heads,
+ * layer out of range, max_entries < 1), HW_ERANGE (limits above),
+ * HW_EUNSUPPORTED (head_dim), HW_EWORKSPACE, HW_EHIP (launch failure).
+ */
+hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                         int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
+                         const int32_t* num_entries, double rope_theta, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Step completion (key design 2: a finished step's KV is rotated and moved
+ * into the shared history), for every layer and kv head of the pool.
+ * With n = block_len[src] and m = block_len[dst] read on the device: for
+ * j < n, dst token m + j receives the src key re-encoded at local position
+ * m + j (rotated by m with fp64 intermediates, rounded to nearest-even in the
+ * pool type) and the src value unchanged; then block_len[dst] = m + n and
+ * block_len[src] = 0.  src data is left in place.
+ * Host-checked: HW_EINVAL (ids, src == dst), HW_ECAPACITY (cap_src > cap_dst
+ * is allowed; only the run-time lengths decide, see HW_DEV_APPEND_OVERFLOW).
+ */
+hw_status hw_block_append(const hw_pool* pool, int32_t src_block, int32_t dst_block,
+                          double rope_theta, void* stream);
+
+/* Sets block_len[block] = 0 on the device (a worker starts a new step). */
+hw_status hw_block_reset(const hw_pool* pool, int32_t block, void* stream);
+
+/*
+ * Combined layout (key design 2) built on the device from the current
+ * block lengths: for worker w the entries are common_block at offset 0, then
+ * worker_block[v] for v != w in increasing v, then worker_block[w]; each
+ * view_offset is the running sum of the preceding blocks' lengths.
+ *   worker_block (host) [num_workers], distinct, != common_block.
+ *   tables       (device) [num_workers][num_workers + 1] written.
+ *   num_entries  (device) [num_workers] written (= num_workers + 1).
+ */
+hw_status hw_build_combined_tables(const hw_pool* pool, int32_t num_workers, int32_t common_block,
+                                   const int32_t* worker_block, hw_entry* tables,
+                                   int32_t* num_entries, void* stream);
+
+/*
+ * Reads the pool's sticky HW_DEV_* bits into *flags (host).  Synchronizes the
+ * device first.  clear != 0 zeroes the word afterwards.
+ */
+hw_status hw_pool_status(const hw_pool* pool, int32_t* flags, int32_t clear);
+
+/*
+ * Process-wide tuning (not thread-safe against concurrent decode calls).
+ *   path:           0 auto, 1 VALU fp32 kernel, 2 MFMA bf16 kernel (bf16 pools).
+ *   units_per_head: number of split-K work units per kv head; 0 = automatic.
+ * Returns HW_EINVAL for values out of range.
+ */
+hw_status hw_set_tuning(int32_t path, int32_t units_per_head);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HOGWILD_ATTN_H */

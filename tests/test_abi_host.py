@@ -1,0 +1,146 @@
+"""CPU-side checks of libhogwild_attn: it loads, exports every declared call, and
+rejects bad arguments on the host before touching the GPU.  No compute calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_shared_hw_amd import hogwild_attn as hw
+from decode_attention_shared_hw_amd import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hw.LIB_PATH):
+        from decode_attention_shared_hw_amd import build
+        build.build()
+    return hw.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hogwild_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(hw_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert set(names) == set(hw.EXPORTED)
+
+
+def test_abi_version_and_status_text(lib):
+    assert hw.hw_abi_version() == 1
+    assert hw.hw_status_str(hw.HW_OK) == "ok"
+    assert "workspace" in hw.hw_status_str(hw.HW_EWORKSPACE)
+
+
+def test_struct_layout_matches_header(lib):
+    assert ctypes.sizeof(hw.hw_entry) == 8
+    # 6 int32 + int64 + 6 pointers
+    assert ctypes.sizeof(hw.hw_pool) == 6 * 4 + 8 + 6 * 8
+    assert hw.hw_pool.num_slots.offset == 24 and hw.hw_pool.k.offset == 32
+
+
+class FakePool:
+    """A pool descriptor whose device pointers are never dereferenced (host checks only)."""
+
+    def __init__(self, dtype=hw.HW_BF16, D=128, caps=(64, 32, 32), starts=None, Hkv=2, layers=1,
+                 slots=None):
+        starts = starts if starts is not None else list(np.cumsum([0] + list(caps[:-1])))
+        self._s = (ctypes.c_int64 * len(caps))(*starts)
+        self._c = (ctypes.c_int32 * len(caps))(*caps)
+        slots = slots if slots is not None else int(sum(caps))
+        self.desc = hw.hw_pool(dtype, layers, Hkv, D, len(caps), 0, slots, 0x1000, 0x2000,
+                               0x3000, 0x4000, ctypes.cast(self._s, ctypes.c_void_p),
+                               ctypes.cast(self._c, ctypes.c_void_p))
+
+
+def decode_rc(lib, pool, layer=0, W=2, Hq=4, E=3, theta=1e4, ws_bytes=1 << 30, ptr=0x5000):
+    p = ctypes.c_void_p(ptr)
+    return lib.hw_attn_decode(ctypes.byref(pool.desc), layer, p, W, Hq, p, E, p, theta, p, p,
+                              ws_bytes, None)
+
+
+def test_decode_host_validation(lib):
+    ok = FakePool()
+    assert decode_rc(lib, FakePool(D=96)) == hw.HW_EUNSUPPORTED
+    assert decode_rc(lib, FakePool(dtype=7)) == hw.HW_EUNSUPPORTED
+    assert decode_rc(lib, ok, Hq=3) == hw.HW_EINVAL              # Hq % Hkv
+    assert decode_rc(lib, ok, layer=1) == hw.HW_EINVAL           # layer out of range
+    assert decode_rc(lib, ok, W=0) == hw.HW_ERANGE
+    assert decode_rc(lib, ok, W=33) == hw.HW_ERANGE
+    assert decode_rc(lib, ok, W=32, Hq=8) == hw.HW_ERANGE        # rows 128 > 64
+    assert decode_rc(lib, ok, E=0) == hw.HW_ERANGE
+    assert decode_rc(lib, ok, theta=-1.0) == hw.HW_EINVAL
+    assert decode_rc(lib, ok, theta=float("nan")) == hw.HW_EINVAL
+    assert decode_rc(lib, ok, ws_bytes=16) == hw.HW_EWORKSPACE
+    assert decode_rc(lib, ok, ptr=0) == hw.HW_EINVAL             # null q/tables/out
+    assert decode_rc(lib, FakePool(caps=(64, 33, 32))) == hw.HW_EINVAL       # cap % 32
+    assert decode_rc(lib, FakePool(caps=(64, 32), starts=[0, 32])) == hw.HW_EINVAL  # overlap
+    assert decode_rc(lib, FakePool(caps=(64,), slots=32)) == hw.HW_EINVAL    # beyond slots
+    assert decode_rc(lib, FakePool(caps=tuple([32] * 65))) == hw.HW_ERANGE   # too many blocks
+
+
+def test_workspace_bytes(lib):
+    pool = FakePool()
+    n = lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4)
+    # sync words + (m, l) + accumulators for Hkv=2 heads, rows 4, D=128, 256 units per head
+    assert n >= 2 * 256 * 4 * 128 * 4
+    assert lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 3) == 0
+    hw.hw_set_tuning(hw.PATH_AUTO, 8)
+    try:
+        assert lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4) < n
+    finally:
+        hw.hw_set_tuning(hw.PATH_AUTO, 0)
+
+
+def test_tuning_validation(lib):
+    assert lib.hw_set_tuning(3, 0) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, -1) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, 257) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, 0) == hw.HW_OK
+
+
+def test_append_reset_tables_host_validation(lib):
+    pool = FakePool()
+    P = ctypes.byref(pool.desc)
+    assert lib.hw_block_append(P, 1, 1, 1e4, None) == hw.HW_EINVAL
+    assert lib.hw_block_append(P, 1, 3, 1e4, None) == hw.HW_EINVAL
+    assert lib.hw_block_append(P, -1, 0, 1e4, None) == hw.HW_EINVAL
+    assert lib.hw_block_append(P, 1, 0, 0.0, None) == hw.HW_EINVAL
+    assert lib.hw_block_reset(P, 5, None) == hw.HW_EINVAL
+    wb = (ctypes.c_int32 * 2)(1, 1)
+    p = ctypes.c_void_p(0x5000)
+    assert lib.hw_build_combined_tables(P, 2, 0, ctypes.cast(wb, ctypes.c_void_p), p, p,
+                                        None) == hw.HW_EINVAL
+    wb = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.hw_build_combined_tables(P, 2, 0, ctypes.cast(wb, ctypes.c_void_p), p, p,
+                                        None) == hw.HW_EINVAL
+    assert lib.hw_build_combined_tables(P, 0, 0, ctypes.cast(wb, ctypes.c_void_p), p, p,
+                                        None) == hw.HW_ERANGE
+    assert lib.hw_pool_status(None, None, 0) == hw.HW_EINVAL
+
+
+def test_layout_positions_follow_the_documented_formula():
+    for D in (64, 128):
+        S = 64
+        x = torch.arange(S * D, dtype=torch.float64).reshape(S, D)   # value = logical index
+        pk = layout.pack_keys(x).reshape(-1)
+        pv = layout.pack_values(x).reshape(-1)
+        for slot in (0, 1, 15, 16, 17, 31, 32, 47, 63):
+            for d in (0, 1, 7, 8, 63, D - 1):
+                T, t = slot // 32, slot % 32
+                ko = T * 32 * D + (t // 16) * 16 * D + (d // 8) * 128 + (t % 16) * 8 + d % 8
+                vo = T * 32 * D + ((t % 16) // 4) * 8 * D + d * 8 + (t // 16) * 4 + t % 4
+                assert pk[ko] == slot * D + d
+                assert pv[vo] == slot * D + d
+        assert torch.equal(layout.unpack_keys(layout.pack_keys(x)), x)
+        assert torch.equal(layout.unpack_values(layout.pack_values(x)), x)

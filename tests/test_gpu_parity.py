@@ -1,0 +1,328 @@
+"""GPU parity: libhogwild_attn (through its C ABI) against the CPU oracle.
+
+Attention outputs: bf16 inputs within 5e-3 max-abs and 1e-2 relative L2 of the
+fp64 oracle; fp32 inputs within 1e-5 (normwise).  Tables, lengths and append
+indexing: bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_shared_hw_amd import hogwild_attn as hw
+from decode_attention_shared_hw_amd import workloads
+from hw_harness import Setup, assert_close, errors
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [hw.PATH_VALU, hw.PATH_MFMA]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _tuning(request):
+    _say(f"[case] {request.node.name}")
+    yield
+    hw.hw_set_tuning(hw.PATH_AUTO, 0)
+
+
+def _custom(W, Hq, Hkv, D, lens, dtype=torch.bfloat16, theta=1e6, caps=None, sigma=0.5, seed=7):
+    caps = caps or [workloads.round_up(max(x, 1)) for x in lens]
+    return workloads.Workload(f"custom_W{W}_G{Hq // Hkv}_D{D}", W, Hq, Hkv, D, theta, dtype, 1,
+                              list(lens), list(caps), sigma, seed)
+
+
+# ---------------------------------------------------------------- tables (a1)
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
+def test_device_tables_match_oracle(W):
+    rng = np.random.default_rng(W)
+    for trial in range(5):
+        lens = [int(x) for x in rng.integers(0, 300, size=W + 1)]
+        wl = _custom(W, 8 * W, 8, 64, lens)
+        pool = hw.Pool(1, 1, 64, wl.caps, dtype=torch.bfloat16)
+        pool.set_lengths(lens)
+        t = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
+        ne = torch.zeros(W, dtype=torch.int32, device="cuda")
+        hw.hw_build_combined_tables(pool, W, 0, list(range(1, W + 1)), t, ne)
+        tb, to, one = oracle.build_combined_tables(0, list(range(1, W + 1)), lens)
+        t = t.cpu().numpy()
+        assert (t[..., 0] == tb).all() and (t[..., 1] == to).all()
+        assert (ne.cpu().numpy() == one).all()
+
+
+# --------------------------------------------------------- decode, configs
+def test_tiny_fp32_matches_oracle_definition_form():
+    s = Setup(workloads.tiny())
+    ref, rc = s.oracle_decode(form=oracle.FORM_DEFINITION)
+    assert rc == 0
+    got = s.decode()
+    assert_close(got, ref, torch.float32, "tiny fp32")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_qwq_layer_bf16_matches_oracle(path):
+    hw.hw_set_tuning(path, 0)
+    s = Setup(workloads.qwq_layer())
+    ref, rc = s.oracle_decode()
+    assert rc == 0
+    got = s.decode()
+    ma, rl = assert_close(got, ref, torch.bfloat16, f"qwq layer path {path}")
+    _say(f"  path {path}: max_abs {ma:.2e} rel_l2 {rl:.2e}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", [
+    # (W, Hq, Hkv, D, lens)  ragged tails, empty blocks, one-token blocks, GQA 1..8
+    (1, 8, 8, 128, [37, 0]),
+    (1, 1, 1, 64, [1, 0]),
+    (1, 2, 1, 128, [0, 1]),
+    (2, 4, 2, 64, [256, 64, 64]),
+    (2, 16, 2, 128, [70, 0, 33]),
+    (3, 6, 2, 64, [1, 1, 1, 1]),
+    (4, 40, 8, 128, [1000, 257, 31, 0, 64]),
+    (8, 8, 2, 64, [300] + [5, 17, 0, 33, 64, 1, 2, 40]),
+    (4, 32, 8, 128, [2048, 100, 200, 300, 400]),
+    (16, 16, 4, 64, [129] + [3] * 16),
+])
+def test_ragged_shapes_match_oracle(path, case):
+    W, Hq, Hkv, D, lens = case
+    hw.hw_set_tuning(path, 0)
+    wl = _custom(W, Hq, Hkv, D, lens)
+    if path == hw.PATH_MFMA and wl.rows > 32:
+        pytest.skip("MFMA path holds at most 32 rows")
+    s = Setup(wl, poison_unused=True)
+    ref, rc = s.oracle_decode()
+    assert rc == 0
+    got = s.decode()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, torch.bfloat16, f"{case} path {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_fp32_ragged_matches_oracle(path):
+    if path == hw.PATH_MFMA:
+        hw.hw_set_tuning(path, 0)
+        wl = _custom(2, 4, 2, 64, [40, 3, 9], dtype=torch.float32, theta=1e4, sigma=0.0)
+        s = Setup(wl)
+        q = s.q[0].cuda()
+        out = torch.zeros(2, 4, 64, device="cuda")
+        with pytest.raises(hw.HWError) as e:
+            hw.hw_attn_decode(s.pool, 0, q, s.tables, s.num_entries, wl.theta, out, s.ws)
+        assert e.value.code == hw.HW_EUNSUPPORTED
+        return
+    wl = _custom(3, 6, 3, 128, [200, 31, 0, 65], dtype=torch.float32, theta=1e4, sigma=0.0)
+    s = Setup(wl, poison_unused=True)
+    ref, rc = s.oracle_decode(form=oracle.FORM_DEFINITION)
+    assert rc == 0
+    assert_close(s.decode(), ref, torch.float32, "fp32 ragged")
+
+
+# ------------------------------------------------------------- invariants
+@pytest.mark.parametrize("path", PATHS)
+def test_single_visible_token_returns_value_exactly(path):
+    hw.hw_set_tuning(path, 0)
+    wl = _custom(2, 4, 2, 128, [1, 0, 0], seed=3)
+    s = Setup(wl, poison_unused=True)
+    got = s.decode()
+    V = s.V[0].float().numpy()
+    for w in range(2):
+        for h in range(4):
+            assert (got[w, h] == V[h // 2, 0]).all()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_unit_count_does_not_change_the_result(path):
+    wl = _custom(4, 40, 8, 128, [3000, 100, 31, 250, 7])
+    s = Setup(wl)
+    outs = []
+    for units in (1, 3, 16, 64):
+        hw.hw_set_tuning(path, units)
+        s.ws = hw.alloc_workspace(s.pool, wl.W, wl.Hq)
+        outs.append(s.decode())
+    ref, _ = s.oracle_decode()
+    for o in outs:
+        assert_close(o, ref, torch.bfloat16, f"units path {path}")
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() < 2e-3
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_deterministic_across_runs(path):
+    hw.hw_set_tuning(path, 0)
+    s = Setup(workloads.qwq_layer())
+    a = s.decode()
+    b = s.decode()
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_batched_workers_equal_single_worker_calls(path):
+    hw.hw_set_tuning(path, 0)
+    wl = _custom(4, 16, 4, 128, [500, 40, 90, 3, 77])
+    s = Setup(wl)
+    full = s.decode()
+    tb = s.tables.cpu()
+    ne = s.num_entries.cpu()
+    for w in range(wl.W):
+        one = s.decode(q=s.q[0][w:w + 1], tables=tb[w:w + 1].contiguous().cuda(),
+                       num_entries=ne[w:w + 1].contiguous().cuda())
+        assert np.abs(one[0] - full[w]).max() < 1e-6
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_partial_visibility_and_entry_order(path):
+    hw.hw_set_tuning(path, 0)
+    wl = _custom(3, 6, 2, 64, [120, 50, 60, 70])
+    s = Setup(wl)
+    # worker 0: only common and its own block; worker 1: reversed order of entries;
+    # worker 2: common only, shifted offsets
+    tables = np.zeros((3, 4, 2), np.int32)
+    ne = np.array([2, 4, 1], np.int32)
+    tables[0, :2] = [(0, 0), (1, 120)]
+    tables[1, :4] = [(2, 240), (3, 170), (1, 120), (0, 0)]
+    tables[2, :1] = [(0, 1000)]
+    got = s.decode(tables=torch.from_numpy(tables).cuda(), num_entries=torch.from_numpy(ne).cuda())
+    ref, rc = s.oracle_decode(tables=(tables[..., 0].copy(), tables[..., 1].copy(), ne))
+    assert rc == 0
+    assert_close(got, ref, torch.bfloat16, "partial visibility")
+
+
+# ------------------------------------------------------- device error paths
+def test_bad_table_entry_sets_status_and_zeroes_that_worker():
+    wl = _custom(2, 4, 2, 64, [64, 32, 32])
+    s = Setup(wl)
+    hw.hw_pool_status(s.pool, clear=True)
+    tables = s.tables.clone()
+    tables[1, 1, 0] = 99  # block id out of range for worker 1
+    got = s.decode(tables=tables)
+    flags = hw.hw_pool_status(s.pool, clear=True)
+    assert flags & hw.HW_DEV_BAD_ENTRY
+    assert (got[1] == 0).all()
+    ref, _ = s.oracle_decode()
+    assert_close(got[0], ref[0], torch.bfloat16, "healthy worker")
+
+
+def test_length_beyond_capacity_sets_status():
+    wl = _custom(1, 2, 2, 64, [64, 32])
+    s = Setup(wl)
+    hw.hw_pool_status(s.pool, clear=True)
+    s.pool.set_lengths([64, 33])  # capacity of block 1 is 32
+    s.decode()
+    assert hw.hw_pool_status(s.pool, clear=True) & hw.HW_DEV_BAD_LENGTH
+
+
+def test_worker_without_tokens_gets_zeros_and_status():
+    wl = _custom(2, 4, 2, 64, [0, 0, 0])
+    s = Setup(wl)
+    hw.hw_pool_status(s.pool, clear=True)
+    got = s.decode()
+    assert (got == 0).all()
+    assert hw.hw_pool_status(s.pool, clear=True) & hw.HW_DEV_NO_TOKENS
+
+
+# ---------------------------------------------------------------- append (a5)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_append_matches_oracle_bit_exact(dtype):
+    theta = 1e6 if dtype == torch.bfloat16 else 1e4
+    lens = [1000, 333, 17, 64]
+    wl = workloads.Workload("append", 3, 6, 2, 128, theta, dtype, 2, lens,
+                            [2048, 352, 32, 64], 0.5, 11)
+    s = Setup(wl, n_layers=2)
+    src, dst = 1, 0
+    K0 = np.stack([k.double().numpy() for k in s.K])
+    V0 = np.stack([v.double().numpy() for v in s.V])
+    Ko, Vo = K0.copy(), V0.copy()
+    lo = np.array(lens, np.int32)
+    rc = oracle.block_append(Ko, Vo, s.pool.block_start, s.pool.block_cap, lo, src, dst, theta,
+                             oracle.HWO_BF16 if dtype == torch.bfloat16 else oracle.HWO_F32)
+    assert rc == 0
+    hw.hw_block_append(s.pool, src, dst, theta)
+    torch.cuda.synchronize()
+    assert s.pool.block_len.cpu().tolist() == lo.tolist()
+    for layer in range(2):
+        Kg, Vg = s.pool.load_layer(layer)
+        Kg = Kg.cpu().double().numpy()
+        Vg = Vg.cpu().double().numpy()
+        assert np.array_equal(Vg, Vo[layer])
+        if dtype == torch.bfloat16:
+            assert np.array_equal(Kg, Ko[layer])
+        else:
+            diff = Kg != Ko[layer]
+            if diff.any():  # at most one ulp of fp32, and rarely
+                ulp = np.spacing(np.abs(Ko[layer][diff]).astype(np.float32)).astype(np.float64)
+                assert (np.abs(Kg[diff] - Ko[layer][diff]) <= ulp).all()
+                assert diff.sum() <= 4
+
+
+def test_append_then_review_attention_is_unchanged():
+    """src right after common in worker 0's view: attention before == after the append."""
+    wl = _custom(2, 8, 2, 128, [700, 45, 300], caps=[1024, 64, 320])
+    s = Setup(wl)
+    before = s.decode()
+    hw.hw_block_append(s.pool, 2, 0, wl.theta)  # worker 1's block follows common for worker 0
+    hw.hw_build_combined_tables(s.pool, wl.W, 0, wl.worker_block, s.tables, s.num_entries)
+    after = s.decode()
+    assert s.pool.block_len.cpu().tolist() == [1000, 45, 0]
+    assert np.abs(after[0] - before[0]).max() < 5e-3
+
+
+def test_append_overflow_moves_nothing():
+    wl = _custom(1, 2, 2, 64, [30, 20], caps=[32, 32])
+    s = Setup(wl)
+    hw.hw_pool_status(s.pool, clear=True)
+    k0, v0 = s.pool.k.clone(), s.pool.v.clone()
+    hw.hw_block_append(s.pool, 1, 0, wl.theta)
+    assert hw.hw_pool_status(s.pool, clear=True) & hw.HW_DEV_APPEND_OVERFLOW
+    assert s.pool.block_len.cpu().tolist() == [30, 20]
+    assert torch.equal(s.pool.k, k0) and torch.equal(s.pool.v, v0)
+
+
+def test_reset_block():
+    wl = _custom(1, 2, 2, 64, [30, 20], caps=[32, 32])
+    s = Setup(wl)
+    hw.hw_block_reset(s.pool, 1)
+    assert s.pool.block_len.cpu().tolist() == [30, 0]
+
+
+# ------------------------------------------- full-size step (sampled outputs)
+def test_qwq_step_full_size_sampled():
+    """64-layer pool of the 16K / 4-worker step, outputs sampled against the oracle."""
+    wl = workloads.qwq_step()
+    pool = hw.Pool(wl.layers, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
+    pool.set_lengths(wl.lens)
+    sample_layers = [0, 31, 63]
+    host = {}
+    for layer in range(wl.layers):
+        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+        pool.store_layer(layer, K, V)
+        if layer in sample_layers:
+            host[layer] = (K.cpu(), V.cpu(), workloads.make_q(wl, layer, device="cuda").cpu())
+        del K, V
+    tables = torch.zeros(wl.W, wl.W + 1, 2, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(wl.W, dtype=torch.int32, device="cuda")
+    hw.hw_build_combined_tables(pool, wl.W, 0, wl.worker_block, tables, ne)
+    ws = hw.alloc_workspace(pool, wl.W, wl.Hq)
+    tb, to, one = oracle.build_combined_tables(0, wl.worker_block, wl.lens)
+    rng = np.random.default_rng(0)
+    for layer in sample_layers:
+        K, V, q = host[layer]
+        out = torch.empty(wl.W, wl.Hq, wl.D, device="cuda")
+        hw.hw_attn_decode(pool, layer, q.cuda(), tables, ne, wl.theta, out, ws)
+        got = out.cpu().numpy()
+        for _ in range(4):
+            w, h = int(rng.integers(wl.W)), int(rng.integers(wl.Hq))
+            g = h // wl.G
+            ref, rc = oracle.attn_one(oracle.FORM_METHOD, q[w, h].double().numpy(),
+                                      K[g].double().numpy(), V[g].double().numpy(), tb[w], to[w],
+                                      np.asarray(wl.lens, np.int32),
+                                      np.asarray(pool.block_start, np.int64), wl.theta)
+            assert rc == 0
+            ma, rl = errors(got[w, h], ref)
+            assert ma <= 5e-3 and rl <= 1e-2, (layer, w, h, ma, rl)
+    assert hw.hw_pool_status(pool) == 0
