@@ -11,8 +11,8 @@
 namespace hw {
 namespace {
 
-constexpr int kMaxUnitsPerHead = 256;
-constexpr int kTargetWorkgroups = 512;  // 2 resident workgroups on each of 256 CUs
+constexpr int kMaxUnitsPerHead = kMaxUnits;
+constexpr int kTargetWorkgroups = 256;  // one workgroup on each of MI355X's 256 CUs
 
 int g_path = 0;            // 0 auto, 1 VALU, 2 MFMA
 int g_units_per_head = 0;  // 0 automatic
@@ -54,6 +54,9 @@ hw_status check_pool(const hw_pool* p) {
   if (p->num_layers < 1 || p->num_kv_heads < 1 || p->reserved != 0) return HW_EINVAL;
   if (p->num_blocks < 1 || p->num_blocks > HW_MAX_BLOCKS) return HW_ERANGE;
   if (p->num_slots <= 0 || p->num_slots % HW_TILE_TOKENS != 0) return HW_EINVAL;
+  // one (layer, kv head) plane is addressed with 32-bit byte offsets
+  if (p->num_slots * p->head_dim * (p->dtype == HW_F32 ? 4 : 2) >= (int64_t(1) << 31))
+    return HW_ERANGE;
   if (!p->k || !p->v || !p->block_len || !p->status || !p->block_start || !p->block_cap)
     return HW_EINVAL;
   for (int b = 0; b < p->num_blocks; ++b) {
@@ -85,15 +88,15 @@ int units_per_head_setting(int num_kv_heads) {
 }
 
 struct WsLayout {
-  size_t sync_off, ml_off, acc_off, total;
+  size_t ml_off, acc_off, total;
 };
 
+// [Hkv][units][rows] (m, l) pairs, then [Hkv][units][rows][D] accumulators.
 WsLayout ws_layout(int hkv, int units, int rows, int D) {
   WsLayout w;
-  w.sync_off = 0;
-  w.ml_off = 256 * ((2 * static_cast<size_t>(hkv) * 4 + 255) / 256);
+  w.ml_off = 0;
   const size_t ml = static_cast<size_t>(hkv) * units * rows * sizeof(float2);
-  w.acc_off = w.ml_off + 256 * ((ml + 255) / 256);
+  w.acc_off = 256 * ((ml + 255) / 256);
   const size_t acc = static_cast<size_t>(hkv) * units * rows * D * sizeof(float);
   w.total = w.acc_off + acc;
   return w;
@@ -165,15 +168,10 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
   DeviceInfo* di = nullptr;
   st = device_info(&di);
   if (st != HW_OK) return st;
-  const int occ = di->occ[path][pool->dtype][pool->head_dim == 128][rows > 16];
-  const int64_t capacity = static_cast<int64_t>(occ) * di->cus;
-  if (capacity < pool->num_kv_heads) return HW_ERANGE;
-  // units per head: the setting, bounded by residency (the per-head barrier
-  // needs every workgroup resident) and by the tiles the blocks can hold
+  // units per head: the setting, bounded by the tiles the blocks can hold
   int64_t max_tiles = 0;
   for (int b = 0; b < pool->num_blocks; ++b) max_tiles += pool->block_cap[b] / HW_TILE_TOKENS;
   int64_t P = P_ws;
-  if (P > capacity / pool->num_kv_heads) P = capacity / pool->num_kv_heads;
   if (P > max_tiles) P = max_tiles;
   if (P < 1) P = 1;
 
@@ -192,10 +190,10 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
   a.out = out;
   a.status = pool->status;
   char* ws = static_cast<char*>(workspace);
-  a.ws_sync = reinterpret_cast<uint32_t*>(ws + wl.sync_off);
   a.ws_ml = reinterpret_cast<float2*>(ws + wl.ml_off);
   a.ws_acc = reinterpret_cast<float*>(ws + wl.acc_off);
   a.plane_elems = plane;
+  a.plane_bytes = static_cast<int32_t>(plane * static_cast<int64_t>(esz));
   a.W = num_workers;
   a.Hq = num_q_heads;
   a.Hkv = pool->num_kv_heads;
@@ -210,14 +208,15 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
   a.xcd_map = (grid % 8 == 0) ? 1 : 0;
   a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
   for (int b = 0; b < pool->num_blocks; ++b) {
-    a.block_start[b] = pool->block_start[b];
-    a.block_cap[b] = pool->block_cap[b];
+    a.tab.block_start[b] = pool->block_start[b];
+    a.tab.block_cap[b] = pool->block_cap[b];
   }
   for (int i = 0; i < pool->head_dim / 2; ++i)
-    a.inv_freq[i] = pow(rope_theta, -2.0 * i / static_cast<double>(pool->head_dim));
-  const hipError_t e = path == 2
-                           ? launch_decode_mfma(a, static_cast<int>(grid), static_cast<hipStream_t>(stream))
-                           : launch_decode_valu(a, static_cast<int>(grid), static_cast<hipStream_t>(stream));
+    a.tab.inv_freq[i] = pow(rope_theta, -2.0 * i / static_cast<double>(pool->head_dim));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = path == 2 ? launch_decode_mfma(a, static_cast<int>(grid), hs)
+                           : launch_decode_valu(a, static_cast<int>(grid), hs);
+  if (e == hipSuccess) e = launch_merge(a, hs);
   return e == hipSuccess ? HW_OK : HW_EHIP;
 }
 

@@ -1,24 +1,31 @@
-// hw_decode.hip — fused concurrent-attention decode kernels for gfx950.
+// hw_decode.hip — concurrent-attention decode kernels for gfx950.
 //
-// One launch per layer.  Work unit = (kv head g, unit u): a contiguous range
-// of 32-token tiles in the concatenation of the visible blocks of head g.
-// Each workgroup
-//   1. decodes the worker tables and device block lengths into a plan
-//      (visibility, view offsets, i_q, tile prefix)           [prologue]
+// One decode call = two launches on the caller's stream:
+//
+//  split kernel, one workgroup per work unit (kv head g, unit u); a unit owns
+//  a contiguous range of 32-token tiles in the concatenation of the blocks
+//  that some worker sees.  Each workgroup
+//   1. decodes the worker tables and the device block lengths into a plan
+//      (visibility, view offsets, i_q, tile prefix)                  [prologue]
 //   2. for every block its range touches, rotates the stacked W*G query rows
-//      of head g by i_q - view_offset (Hogwild! notes, key design 1: only the
-//      single query token is rotated, never the cache)         [a2]
+//      of head g by i_q - view_offset: only the single current query token is
+//      rotated, never the cache (Hogwild! notes, key design 1)        [a2]
 //   3. streams its K/V tiles once for all rows with an online softmax in the
-//      exp2 domain (Flash-Decoding split-K; news 1114328 sec. 3.2)  [a3]
-//   4. writes its partial (m, l, acc) and meets the other units of head g at
-//      a per-head barrier; then every unit merges its own slice of the head's
-//      outputs by log-sum-exp weights in fixed unit order (deterministic)  [a4]
+//      exp2 domain (split-K / Flash-Decoding; news 1114328 sec. 3.2)   [a3]
+//   4. writes its partial (m, l, acc) with plain stores.
+//  merge kernel, one workgroup per (kv head, row): log-sum-exp merge of the
+//  units' partials in fixed unit order (deterministic) and the output row [a4].
 //
-// Two main loops share the prologue and the epilogue:
-//   decode_valu<T>   fp32 VALU arithmetic over LDS tiles; fp32 and bf16 pools.
-//   decode_mfma<D,NT> bf16 MFMA 16x16x32: S^T = K Q~^T and O^T = V^T P^T, with
-//                    tiles loaded straight into operand fragments (the pool
-//                    layout matches them), rows = W*G <= 32.
+// The kernel boundary orders the partials' stores before their loads, so no
+// workgroup ever waits on another and no cache maintenance is needed inside
+// a kernel.
+//
+// Two split kernels share the prologue:
+//   decode_valu<T>    fp32 VALU arithmetic over LDS-staged tiles (fp32 and
+//                     bf16 pools, rows <= 64).
+//   decode_mfma<D,NT> bf16 MFMA 16x16x32: S^T = K Q~^T and O^T = V^T P^T with
+//                     tiles loaded straight into operand fragments (the pool
+//                     layout matches them), rows = W*G <= 16*NT <= 32.
 #include <math.h>
 
 #include "hw_internal.h"
@@ -44,7 +51,7 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t 
 }
 
 // cos/sin of delta * w with the angle formed and reduced mod 2*pi in fp64,
-// so that positions of ~1e5 keep ~1e-7 rad of accuracy.
+// so that positions of ~1e5 keep ~1e-7 rad of accuracy (fp32 pools).
 __device__ __forceinline__ void rope_cos_sin(int64_t delta, double w, float* c, float* s) {
   const double a = static_cast<double>(delta) * w;
   const double k = rint(a * 0.15915494309189535);      // 1 / (2 pi)
@@ -53,86 +60,157 @@ __device__ __forceinline__ void rope_cos_sin(int64_t delta, double w, float* c, 
   sincosf(static_cast<float>(r), s, c);
 }
 
+// Same angle, evaluated with the hardware v_sin/v_cos (argument in
+// revolutions): the angle is reduced in fp64 to [-1/2, 1/2] revolution, so the
+// result carries ~1e-6 absolute error, far below the bf16 rounding applied to
+// the rotated query on the MFMA path.  Pure ALU: no table loads.
+__device__ __forceinline__ void rope_cos_sin_hw(int64_t delta, double w_rev, float* c, float* s) {
+  const double rev = static_cast<double>(delta) * w_rev;
+  const float fr = static_cast<float>(rev - rint(rev));
+  *s = __builtin_amdgcn_sinf(fr);
+  *c = __builtin_amdgcn_cosf(fr);
+}
+
 // ----------------------------------------------------------------- prologue
 struct Plan {
   int32_t len[HW_MAX_BLOCKS];
   uint32_t vis[HW_MAX_BLOCKS];        // bit w set: worker w sees block b
   int32_t tile0[HW_MAX_BLOCKS + 1];   // tiles of visible blocks, prefix sums
-  int64_t iq[HW_MAX_WORKERS];         // query position per worker, -1: none
+  long long iq[HW_MAX_WORKERS];       // query position per worker, -1: none
   int32_t off[HW_MAX_WORKERS * HW_MAX_BLOCKS];
+  int64_t start[HW_MAX_BLOCKS];       // first slot of each block
+  double invf[kMaxHalf];              // theta^(-2i/D)
+  double invf_rev[kMaxHalf];          // theta^(-2i/D) / (2 pi)
+  uint32_t bad_workers;
   int32_t flags;
   int32_t head, unit, lo, hi;
 };
 
-__device__ void build_plan(const DecodeArgs& a, Plan& p) {
+// Every global load of the prologue is issued before its first barrier, so
+// the plan costs one memory round trip.  Each thread keeps up to kEntryRegs
+// table entries in registers between the load and the visibility pass.
+// issue(): the kernel's own loads, issued with the plan's; commit(): their
+// LDS stores, run before the first barrier.
+constexpr int kEntryRegs = (HW_MAX_WORKERS * HW_MAX_ENTRIES + kThreads - 1) / kThreads;
+static_assert(kTablesVec <= kThreads, "per-call arrays exceed one vector per thread");
+
+__device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, int* unit) {
+  int lin = blockIdx.x;
+  if (a.xcd_map) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  *head = lin / a.P;
+  *unit = lin - *head * a.P;
+}
+
+template <typename Issue, typename Commit>
+__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
   const int tid = threadIdx.x;
+  const int WE = a.W * a.E;
+  // ---- loads (independent, all in flight together)
+  const int len_raw = tid < a.NB ? a.block_len[tid] : 0;
+  u32x4 tabv = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kTablesVec) tabv = reinterpret_cast<const u32x4*>(&a.tab)[tid];
+  hw_entry ent[kEntryRegs];
+  int ent_ne[kEntryRegs];
+#pragma unroll
+  for (int k = 0; k < kEntryRegs; ++k) {
+    const int i = tid + k * kThreads;
+    ent[k].block_id = -1;
+    ent[k].view_offset = 0;
+    ent_ne[k] = 0;
+    if (i < WE) {
+      ent[k] = a.tables[i];
+      ent_ne[k] = a.num_entries[i / a.E];
+    }
+  }
+  issue();
+  // ---- phase A: zeroed state, copied per-call arrays
+  __shared__ DecodeTables tab;
   if (tid == 0) {
     p.flags = 0;
-    int lin = blockIdx.x;
-    const int grid = gridDim.x;
-    if (a.xcd_map) lin = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
-    p.head = lin / a.P;
-    p.unit = lin % a.P;
+    p.bad_workers = 0u;
+    plan_head_unit(a, &p.head, &p.unit);
   }
-  for (int i = tid; i < a.NB; i += kThreads) {
-    int len = a.block_len[i];
-    if (len < 0 || len > a.block_cap[i]) {
+  if (tid < kTablesVec) reinterpret_cast<u32x4*>(&tab)[tid] = tabv;
+  if (tid < a.NB) p.vis[tid] = 0u;
+  if (tid < a.W) p.iq[tid] = -1;
+  for (int i = tid; i < a.W * a.NB; i += kThreads) p.off[i] = 0;
+  commit();
+  __syncthreads();
+  // ---- phase B: lengths, visibility and view offsets from the tables
+  if (tid < a.NB) {
+    int len = len_raw;
+    if (len < 0 || len > tab.block_cap[tid]) {
       atomicOr(&p.flags, HW_DEV_BAD_LENGTH);
       len = 0;
     }
-    p.len[i] = len;
-    p.vis[i] = 0u;
+    p.len[tid] = len;
+    p.start[tid] = tab.block_start[tid];
   }
-  for (int i = tid; i < a.W * a.NB; i += kThreads) p.off[i] = 0;
-  __syncthreads();
-  __shared__ uint32_t bad_workers;
-  if (tid == 0) bad_workers = 0u;
-  __syncthreads();
-  for (int i = tid; i < a.W * a.E; i += kThreads) {
-    const int w = i / a.E;
-    const int e = i - w * a.E;
-    const int ne = a.num_entries[w];
+  if (tid < a.D / 2) {
+    p.invf[tid] = tab.inv_freq[tid];
+    p.invf_rev[tid] = tab.inv_freq[tid] * 0.15915494309189535;
+  }
+#pragma unroll
+  for (int k = 0; k < kEntryRegs; ++k) {
+    const int i = tid + k * kThreads;
+    if (i >= WE) continue;
+    const int w = i / a.E, e = i - w * a.E;
+    const int ne = ent_ne[k];
     if (ne < 0 || ne > a.E) {
-      atomicOr(&bad_workers, 1u << w);
+      atomicOr(&p.bad_workers, 1u << w);
       continue;
     }
     if (e >= ne) continue;
-    const hw_entry en = a.tables[i];
-    if (en.block_id < 0 || en.block_id >= a.NB) {
-      atomicOr(&bad_workers, 1u << w);
+    const int b = ent[k].block_id;
+    if (b < 0 || b >= a.NB) {
+      atomicOr(&p.bad_workers, 1u << w);
       continue;
     }
-    const uint32_t old = atomicOr(&p.vis[en.block_id], 1u << w);
-    if (old & (1u << w)) atomicOr(&bad_workers, 1u << w);
-    p.off[w * a.NB + en.block_id] = en.view_offset;
+    const uint32_t old = atomicOr(&p.vis[b], 1u << w);
+    if (old & (1u << w)) atomicOr(&p.bad_workers, 1u << w);
+    p.off[w * a.NB + b] = ent[k].view_offset;
   }
   __syncthreads();
-  if (bad_workers) {
+  if (p.bad_workers) {
     // a worker with a malformed table sees nothing: its rows come out as zeros
-    for (int i = tid; i < a.NB; i += kThreads) p.vis[i] &= ~bad_workers;
+    if (tid < a.NB) p.vis[tid] &= ~p.bad_workers;
     if (tid == 0) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid < a.W) {
-    int64_t iq = -1;
-    for (int b = 0; b < a.NB; ++b) {
-      if (((p.vis[b] >> tid) & 1u) && p.len[b] > 0) {
-        const int64_t last = static_cast<int64_t>(p.off[tid * a.NB + b]) + p.len[b] - 1;
-        iq = last > iq ? last : iq;
+  // ---- phase C: query positions (entry-parallel max) and the tile split
+  // (one wave scans the blocks)
+#pragma unroll
+  for (int k = 0; k < kEntryRegs; ++k) {
+    const int i = tid + k * kThreads;
+    if (i >= WE) continue;
+    const int w = i / a.E, e = i - w * a.E;
+    if (e >= ent_ne[k] || ((p.bad_workers >> w) & 1u)) continue;
+    const int b = ent[k].block_id;
+    if (p.len[b] > 0)
+      atomicMax(&p.iq[w], static_cast<long long>(ent[k].view_offset) + p.len[b] - 1);
+  }
+  if (tid >= 64 && tid < 128) {
+    const int lane = tid - 64;
+    int nt = 0;
+    for (int b0 = 0; b0 < a.NB; b0 += 64) {
+      const int b = b0 + lane;
+      int v = 0;
+      if (b < a.NB && p.vis[b] != 0u && p.len[b] > 0) v = (p.len[b] + kTile - 1) / kTile;
+      int incl = v;
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const int y = __shfl_up(incl, s);
+        if (lane >= s) incl += y;
       }
+      if (b < a.NB) p.tile0[b] = nt + incl - v;
+      nt += __shfl(incl, 63);
     }
-    p.iq[tid] = iq;
-  }
-  if (tid == 64) {
-    int acc = 0;
-    for (int b = 0; b < a.NB; ++b) {
-      p.tile0[b] = acc;
-      if (p.vis[b] != 0u && p.len[b] > 0) acc += (p.len[b] + kTile - 1) / kTile;
+    if (lane == 0) {
+      p.tile0[a.NB] = nt;
+      const int64_t n = nt;
+      p.lo = static_cast<int>(n * p.unit / a.P);
+      p.hi = static_cast<int>(n * (p.unit + 1) / a.P);
     }
-    p.tile0[a.NB] = acc;
-    const int64_t n = acc;
-    p.lo = static_cast<int>(n * p.unit / a.P);
-    p.hi = static_cast<int>(n * (p.unit + 1) / a.P);
   }
   __syncthreads();
 }
@@ -143,87 +221,9 @@ __device__ __forceinline__ int block_of_tile(const Plan& p, int nb, int j, int b
   return b;
 }
 
-// ----------------------------------------------------------------- epilogue
-// Per-head barrier + merge of this unit's slice of the head's R*D outputs.
-// Requires every workgroup of the launch to be resident (grid sized by the
-// host from occupancy); the wait is bounded and reports kDevSyncTimeout.
-__device__ void head_barrier_and_merge(const DecodeArgs& a, Plan& p, float* wgt) {
-  const int tid = threadIdx.x;
-  const int g = p.head, u = p.unit;
-  __shared__ int timed_out;
-  __syncthreads();  // every partial store of this workgroup has been issued
-  if (tid == 0) {
-    __threadfence();
-    uint32_t* arrive = a.ws_sync + g;
-    atomicAdd(arrive, 1u);
-    uint32_t n = 0;
-    int spins = 0;
-    while ((n = __hip_atomic_load(arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)) <
-               static_cast<uint32_t>(a.P) &&
-           spins < (1 << 22)) {
-      __builtin_amdgcn_s_sleep(2);
-      ++spins;
-    }
-    timed_out = n < static_cast<uint32_t>(a.P);
-    __threadfence();
-  }
-  __syncthreads();
-  const int RD = a.R * a.D;
-  const int o_lo = static_cast<int>(static_cast<int64_t>(RD) * u / a.P);
-  const int o_hi = static_cast<int>(static_cast<int64_t>(RD) * (u + 1) / a.P);
-  if (!timed_out && o_hi > o_lo) {
-    const int r_lo = o_lo / a.D;
-    const int r_hi = (o_hi - 1) / a.D;  // inclusive
-    const int nr = r_hi - r_lo + 1;
-    const float2* ml = a.ws_ml + static_cast<int64_t>(g) * a.P * a.R;
-    // per-row max and normalizer over the units, in unit order
-    for (int rr = tid; rr < nr; rr += kThreads) {
-      const int r = r_lo + rr;
-      float M = -INFINITY;
-      for (int k = 0; k < a.P; ++k) M = fmaxf(M, ml[k * a.R + r].x);
-      float L = 0.f;
-      if (M != -INFINITY)
-        for (int k = 0; k < a.P; ++k) {
-          const float2 v = ml[k * a.R + r];
-          L += v.y * __builtin_amdgcn_exp2f(v.x - M);
-        }
-      wgt[a.P * nr + 2 * rr] = M;
-      wgt[a.P * nr + 2 * rr + 1] = L > 0.f ? 1.f / L : 0.f;
-      if (!(L > 0.f)) atomicOr(a.status, HW_DEV_NO_TOKENS);
-    }
-    __syncthreads();
-    for (int i = tid; i < a.P * nr; i += kThreads) {
-      const int k = i / nr, rr = i - k * nr;
-      const float M = wgt[a.P * nr + 2 * rr];
-      const float invL = wgt[a.P * nr + 2 * rr + 1];
-      const float mk = ml[k * a.R + r_lo + rr].x;
-      wgt[i] = (invL > 0.f && mk != -INFINITY) ? __builtin_amdgcn_exp2f(mk - M) * invL : 0.f;
-    }
-    __syncthreads();
-    const float* acc = a.ws_acc + static_cast<int64_t>(g) * a.P * RD;
-    for (int o = o_lo + tid; o < o_hi; o += kThreads) {
-      const int r = o / a.D;
-      const int d = o - r * a.D;
-      const int rr = r - r_lo;
-      float s = 0.f;
-      for (int k = 0; k < a.P; ++k) s += acc[static_cast<int64_t>(k) * RD + o] * wgt[k * nr + rr];
-      const int w = r / a.G;
-      const int h = g * a.G + (r - w * a.G);
-      a.out[(static_cast<int64_t>(w) * a.Hq + h) * a.D + d] = s;
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    if (timed_out) atomicOr(a.status, kDevSyncTimeout);
-    if (p.flags) atomicOr(a.status, p.flags);
-    uint32_t* depart = a.ws_sync + a.Hkv + g;
-    const uint32_t old = atomicAdd(depart, 1u);
-    if (old == static_cast<uint32_t>(a.P) - 1u) {
-      // last one out: every unit of this head has passed the barrier
-      __hip_atomic_store(a.ws_sync + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+// Per-unit partial: (m, l) per row and the unnormalised accumulator.
+__device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan& p) {
+  return static_cast<int64_t>(p.head) * a.P + p.unit;
 }
 
 // ------------------------------------------------------------- VALU kernel
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
   __shared__ float vs[kTile * 128];
   __shared__ float ps[HW_MAX_ROWS * (kTile + 1)];
   __shared__ float m_s[HW_MAX_ROWS], l_s[HW_MAX_ROWS], al_s[HW_MAX_ROWS];
-  build_plan(a, plan);
+  build_plan(a, plan, [] {}, [] {});
   const int tid = threadIdx.x;
   const int g = plan.head;
   const int D = a.D, R = a.R, half = D / 2;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
         const int w = r / a.G, h = g * a.G + (r - w * a.G);
         const bool vis = (plan.vis[b] >> w) & 1u;
         float c = 0.f, s = 0.f;
-        if (vis) rope_cos_sin(plan.iq[w] - plan.off[w * a.NB + b], a.inv_freq[i], &c, &s);
+        if (vis) rope_cos_sin(plan.iq[w] - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
         const int64_t qo = (static_cast<int64_t>(w) * a.Hq + h) * D;
         const float x0 = load_elem(qg, qo + i), x1 = load_elem(qg, qo + i + half);
         qr[r * D + i] = vis ? (x0 * c - x1 * s) * a.qscale : 0.f;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
     }
     const int tl = j - plan.tile0[b];
     const int valid = min(kTile, plan.len[b] - tl * kTile);
-    const int64_t base = (a.block_start[b] + static_cast<int64_t>(tl) * kTile) * D;
+    const int64_t base = (plan.start[b] + static_cast<int64_t>(tl) * kTile) * D;
     __syncthreads();
     for (int x = tid; x < kTile * D; x += kThreads) {
       // key tile element x of the pool layout -> (token, dim)
@@ -323,26 +323,27 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       if (idx < R * D) {
         const int r = idx / D, d = idx - r * D;
         float s = acc[k] * al_s[r];
+#pragma unroll 4
         for (int t = 0; t < kTile; ++t) s += ps[r * (kTile + 1) + t] * vs[t * D + d];
         acc[k] = s;
       }
     }
   }
   __syncthreads();
-  const int64_t pu = static_cast<int64_t>(g) * a.P + plan.unit;
+  const int64_t pu = partial_index(a, plan);
   for (int r = tid; r < R; r += kThreads) a.ws_ml[pu * R + r] = make_float2(m_s[r], l_s[r]);
 #pragma unroll
   for (int k = 0; k < kValuMaxAcc; ++k) {
     const int idx = tid + k * kThreads;
     if (idx < R * D) a.ws_acc[pu * R * D + idx] = acc[k];
   }
-  head_barrier_and_merge(a, plan, ps);
+  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
 }
 
 // ------------------------------------------------------------- MFMA kernel
 // bf16 pools, rows R = W*G <= 16*NT.  Each wave owns every 4th tile of the
-// workgroup's range and keeps its own (m, l, O^T) for all rows; waves are
-// merged in LDS at the end.
+// workgroup's range and keeps its own (m, l, O^T) for all rows; the four
+// waves are combined in LDS at the end.
 //
 // Fragments (v_mfma_f32_16x16x32_bf16, lane l: i = l%16, q4 = l/16):
 //   S^T[tok][row] = K[tok][:] . Q~[row][:]
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
 //     A (V^T): dim 16m+i, tokens {4*q4+v, 16+4*q4+v} (one 16-B load)
 //     B (P^T): row 16t+i, the same 8 tokens = this lane's S^T outputs
 //     D:       dims 16m + 4*q4 + v, row 16t+i
+
 struct TileRef {
   int b;          // block
   int valid;      // tokens of the tile inside the block's length
@@ -360,52 +362,66 @@ struct TileRef {
 };
 
 template <int D>
-__device__ __forceinline__ TileRef tile_ref(const Plan& p, const DecodeArgs& a, int j, int& bcur) {
-  bcur = block_of_tile(p, a.NB, j, bcur);
+__device__ __forceinline__ TileRef tile_ref(const Plan& p, int nb, int j, int& bcur) {
+  bcur = block_of_tile(p, nb, j, bcur);
   const int tl = j - p.tile0[bcur];
   TileRef r;
   r.b = bcur;
   r.valid = min(kTile, p.len[bcur] - tl * kTile);
-  r.base = (a.block_start[bcur] + static_cast<int64_t>(tl) * kTile) * D;
+  r.base = (p.start[bcur] + static_cast<int64_t>(tl) * kTile) * D;
   return r;
 }
 
-// (a3) one 16-byte load per lane per fragment; every load of a wave is one
-// contiguous 1 KB (keys) or four contiguous 256 B runs (values).
+// Raw buffer resource over one kv-head plane (gfx9 descriptor word 3).
+// Out-of-range offsets read as zero, so a bad offset can never fault.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+
+// (a3) one 16-byte buffer load per lane per fragment: every key load of a
+// wave is one contiguous 1 KB, every value load four contiguous 256 B runs.
+// koff / voff: this lane's byte offsets inside a tile; tile: the tile's byte
+// offset in the plane (wave-uniform, kept in an SGPR).
 template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* kp, const uint16_t* vp, int64_t base,
-                                          int li, int q4, bf16x8 (&kf)[2][D / 32],
-                                          bf16x8 (&vf)[D / 16]) {
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                          uint32_t tile, uint32_t koff, uint32_t voff,
+                                          bf16x8 (&kf)[2][D / 32], bf16x8 (&vf)[D / 16]) {
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      kf[h2][s] = *reinterpret_cast<const bf16x8*>(kp + base + h2 * 16 * D + (4 * s + q4) * 128 +
-                                                   li * 8);
+      kf[h2][s] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                      krs, koff + (h2 * 16 * D + 4 * s * 128) * 2, tile, 0));
 #pragma unroll
   for (int m = 0; m < D / 16; ++m)
-    vf[m] = *reinterpret_cast<const bf16x8*>(vp + base + q4 * 8 * D + (16 * m + li) * 8);
+    vf[m] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + 16 * m * 8 * 2, tile, 0));
 }
 
 // Scores, online softmax and P.V for one tile held in registers.
+// qf: this lane's rotated-query B fragments, [NT][KS] x 64 lanes in LDS.
 template <int D, int NT>
 __device__ __forceinline__ void compute_tile(bf16x8 (&kf)[2][D / 32], bf16x8 (&vf)[D / 16],
-                                             const bf16x8 (&qf)[NT][D / 32],
+                                             const bf16x8* qf, int lane,
                                              const bool (&rowvis)[NT], int valid, int q4,
                                              f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
                                              float (&l_run)[NT]) {
   constexpr int KS = D / 32, MT = D / 16;
   f32x4 sc[2][NT];
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
+  for (int t = 0; t < NT; ++t) {
+    f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h2][s], qf[t][s], c, 0, 0, 0);
-      sc[h2][t] = c;
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 qv = qf[(t * KS + s) * 64 + lane];
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][s], qv, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][s], qv, c1, 0, 0, 0);
     }
+    sc[0][t] = c0;
+    sc[1][t] = c1;
+  }
   bf16x8 pf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -469,24 +485,55 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
   constexpr int RP = 16 * NT; // padded rows
   constexpr int HALF = D / 2;
   constexpr int ACC_STRIDE = D + 4;
+  constexpr int kWaveState = RP * ACC_STRIDE + 2 * RP;  // one wave's (O^T, m, l)
+  constexpr int kQfFloats = kWaves * NT * KS * 64 * 4;  // rotated-query fragments
+  constexpr int kUnionFloats =
+      kWaves * kWaveState > kQfFloats ? kWaves * kWaveState : kQfFloats;
   __shared__ Plan plan;
-  // per-wave rotation tables (main loop) / per-wave O^T (wave merge)
-  constexpr int kCsFloats = 2 * HW_MAX_WORKERS * HALF;
-  constexpr int kMergeFloats = RP * ACC_STRIDE + 2 * RP;
-  constexpr int kWaveFloats = kCsFloats > kMergeFloats ? kCsFloats : kMergeFloats;
-  __shared__ __attribute__((aligned(16))) float smem[kWaves * kWaveFloats];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
+  // main loop: each wave's rotated-query fragments; afterwards: the four
+  // waves' softmax states
+  __shared__ __attribute__((aligned(16))) float ubuf[kUnionFloats];
 
-  build_plan(a, plan);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;
-  const int g = plan.head;
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+  // this head's query rows, loaded with the plan's loads and staged in LDS so
+  // the main loop issues no vector memory operations other than the K/V stream
+  constexpr int kQVec = RP * D / 8;
+  constexpr int kQRegs = (kQVec + kThreads - 1) / kThreads;
+  u32x4 qv[kQRegs];
+  {
+    int h0, u0;
+    plan_head_unit(a, &h0, &u0);
+    auto issue = [&] {
+#pragma unroll
+      for (int k = 0; k < kQRegs; ++k) {
+        const int x = tid + k * kThreads;
+        const int r = (8 * x) / D, d = (8 * x) - r * D;
+        qv[k] = u32x4{0u, 0u, 0u, 0u};
+        if (x < kQVec && r < a.R) {
+          const int w = r / a.G, h = h0 * a.G + (r - w * a.G);
+          qv[k] =
+              *reinterpret_cast<const u32x4*>(qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d);
+        }
+      }
+    };
+    auto commit = [&] {
+#pragma unroll
+      for (int k = 0; k < kQRegs; ++k) {
+        const int x = tid + k * kThreads;
+        if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
+      }
+    };
+    build_plan(a, plan, issue, commit);
+  }
+  const int g = plan.head;
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + g * a.plane_elems;
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) + g * a.plane_elems;
-  float2* cs = reinterpret_cast<float2*>(smem + wave * kWaveFloats);
 
-  bf16x8 qf[NT][KS];
+  bf16x8* qf = reinterpret_cast<bf16x8*>(ubuf) + wave * NT * KS * 64;
   bool rowvis[NT];
   f32x4 acc[MT][NT];
   float m_run[NT], l_run[NT];
@@ -496,135 +543,182 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
     l_run[t] = 0.f;
     rowvis[t] = false;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[t][s] = bf16x8{};
-#pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // (a2) rotate the stacked query rows of head g for block b into B fragments
+  // (a2) rotate this lane's slice of the stacked query rows of head g for
+  // block b: rows 16t+li, dims 8*(4s+q4)..+8 and their rotate-half partners.
   auto build_qf = [&](int b) {
-    for (int x = lane; x < a.W * HALF; x += 64) {
-      const int w = x / HALF, i = x - w * HALF;
-      float c = 0.f, s = 0.f;
-      if ((plan.vis[b] >> w) & 1u)
-        rope_cos_sin(plan.iq[w] - plan.off[w * a.NB + b], a.inv_freq[i], &c, &s);
-      cs[x] = make_float2(c, s);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + li;
       const int w = r / a.G;
       rowvis[t] = r < a.R && ((plan.vis[b] >> w) & 1u);
-      const int h = g * a.G + (r - w * a.G);
-      const int64_t qo = (static_cast<int64_t>(w) * a.Hq + h) * D;
+      const int64_t delta = rowvis[t] ? plan.iq[w] - plan.off[w * a.NB + b] : 0;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int d0 = 8 * (4 * s + q4);
-        const int p0 = d0 < HALF ? d0 + HALF : d0 - HALF;
-        u32x4 xv = u32x4{0u, 0u, 0u, 0u}, yv = u32x4{0u, 0u, 0u, 0u};
-        if (rowvis[t]) {
-          xv = *reinterpret_cast<const u32x4*>(qg + qo + d0);
-          yv = *reinterpret_cast<const u32x4*>(qg + qo + p0);
-        }
-        bf16x8 f;
+      for (int s = 0; s < KS / 2; ++s) {
+        const int d0 = 8 * (4 * s + q4);  // < HALF; its partner block is d0 + HALF
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(qs + r * D + d0);
+        const u32x4 yv = *reinterpret_cast<const u32x4*>(qs + r * D + d0 + HALF);
+        bf16x8 lo, hi;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t xw = xv[e >> 1], yw = yv[e >> 1];
           const float x = __uint_as_float((e & 1) ? (xw & 0xffff0000u) : (xw << 16));
           const float y = __uint_as_float((e & 1) ? (yw & 0xffff0000u) : (yw << 16));
-          const int fi = (d0 + e) & (HALF - 1);
-          const float2 csv = rowvis[t] ? cs[w * HALF + fi] : make_float2(0.f, 0.f);
-          const float val = d0 < HALF ? x * csv.x - y * csv.y : x * csv.x + y * csv.y;
-          f[e] = static_cast<__bf16>(val * a.qscale);
+          float c = 0.f, sn = 0.f;
+          if (rowvis[t]) rope_cos_sin_hw(delta, plan.invf_rev[d0 + e], &c, &sn);
+          lo[e] = static_cast<__bf16>((x * c - y * sn) * a.qscale);
+          hi[e] = static_cast<__bf16>((y * c + x * sn) * a.qscale);
         }
-        qf[t][s] = f;
+        qf[(t * KS + s) * 64 + lane] = lo;
+        qf[(t * KS + s + KS / 2) * 64 + lane] = hi;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
   };
 
-  // Tiles lo+wave, lo+wave+4, ...; two register sets so the next tile's loads
-  // are in flight while the current one is computed.
-  bf16x8 kA[2][KS], kB[2][KS], vA[MT], vB[MT];
+  // One tile in flight per wave.
+  const __amdgpu_buffer_rsrc_t krs = plane_rsrc(kp, a.plane_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(vp, a.plane_bytes);
+  const uint32_t koff = (q4 * 128 + li * 8) * 2;
+  const uint32_t voff = (q4 * 8 * D + li * 8) * 2;
   int bcur = 0, qb = -1;
-  int j = plan.lo + wave;
-  if (j < plan.hi) {
-    TileRef ra = tile_ref<D>(plan, a, j, bcur);
-    load_tile<D>(kp, vp, ra.base, li, q4, kA, vA);
-    while (true) {
-      const int jb = j + kWaves;
-      const bool hb = jb < plan.hi;
-      TileRef rb{};
-      if (hb) {
-        rb = tile_ref<D>(plan, a, jb, bcur);
-        load_tile<D>(kp, vp, rb.base, li, q4, kB, vB);
-      }
-      if (ra.b != qb) {
-        build_qf(ra.b);
-        qb = ra.b;
-      }
-      compute_tile<D, NT>(kA, vA, qf, rowvis, ra.valid, q4, acc, m_run, l_run);
-      if (!hb) break;
-      const int jc = jb + kWaves;
-      const bool hc = jc < plan.hi;
-      TileRef rc{};
-      if (hc) {
-        rc = tile_ref<D>(plan, a, jc, bcur);
-        load_tile<D>(kp, vp, rc.base, li, q4, kA, vA);
-      }
-      if (rb.b != qb) {
-        build_qf(rb.b);
-        qb = rb.b;
-      }
-      compute_tile<D, NT>(kB, vB, qf, rowvis, rb.valid, q4, acc, m_run, l_run);
-      if (!hc) break;
-      ra = rc;
-      j = jc;
+  for (int j = plan.lo + wave; j < plan.hi; j += kWaves) {
+    const TileRef rt = tile_ref<D>(plan, a.NB, j, bcur);
+    if (rt.b != qb) {
+      build_qf(rt.b);
+      qb = rt.b;
     }
+    const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
+    bf16x8 kf[2][KS], vf[MT];
+    load_tile<D>(krs, vrs, tile, koff, voff, kf, vf);
+    // keep all 16 loads ahead of the arithmetic
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<D, NT>(kf, vf, qf, lane, rowvis, rt.valid, q4, acc, m_run, l_run);
   }
 
-  // wave merge in LDS, then this unit's partial
-  __syncthreads();
-  float* wm = smem + wave * kWaveFloats;  // [RP][ACC_STRIDE] then m[RP], l[RP]
+  // full row sums (the four lanes of a row hold partial sums)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float lsum = l_run[t];
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    const int r = 16 * t + li;
-    if (q4 == 0) {
-      wm[RP * ACC_STRIDE + r] = m_run[t];
-      wm[RP * ACC_STRIDE + RP + r] = lsum;
-    }
+    l_run[t] += __shfl_xor(l_run[t], 16);
+    l_run[t] += __shfl_xor(l_run[t], 32);
+  }
+  // the four waves deposit their states, then every thread combines its
+  // share of the unit's R*D outputs
+  __syncthreads();
+  {
+    float* buf = ubuf + wave * kWaveState;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-      *reinterpret_cast<f32x4*>(wm + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
+    for (int t = 0; t < NT; ++t) {
+      const int r = 16 * t + li;
+      if (q4 == 0) {
+        buf[RP * ACC_STRIDE + r] = m_run[t];
+        buf[RP * ACC_STRIDE + RP + r] = l_run[t];
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        *reinterpret_cast<f32x4*>(buf + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
+    }
   }
   __syncthreads();
-  const int64_t pu = static_cast<int64_t>(g) * a.P + plan.unit;
-  for (int x = tid; x < a.R * D; x += kThreads) {
-    const int r = x / D, d = x - r * D;
+  const int64_t pu = partial_index(a, plan);
+  for (int x = tid; x < a.R * (D / 4); x += kThreads) {
+    const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
+    float mw[kWaves];
     float M = -INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, smem[wv * kWaveFloats + RP * ACC_STRIDE + r]);
-    float L = 0.f, O = 0.f;
+    for (int wv = 0; wv < kWaves; ++wv) {
+      mw[wv] = ubuf[wv * kWaveState + RP * ACC_STRIDE + r];
+      M = fmaxf(M, mw[wv]);
+    }
+    float L = 0.f;
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
       for (int wv = 0; wv < kWaves; ++wv) {
-        const float* src = smem + wv * kWaveFloats;
-        const float mw = src[RP * ACC_STRIDE + r];
-        const float sc2 = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        L += src[RP * ACC_STRIDE + RP + r] * sc2;
-        O += src[r * ACC_STRIDE + d] * sc2;
+        const float* src = ubuf + wv * kWaveState;
+        const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
+        L += src[RP * ACC_STRIDE + RP + r] * sc;
+        O += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d4) * sc;
       }
     }
-    a.ws_acc[pu * a.R * D + x] = O;
-    if (d == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
+    *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d4) = O;
+    if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
   }
-  head_barrier_and_merge(a, plan, smem);
+  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
+}
+
+// ----------------------------------------------------------- merge kernel
+// (a4) One workgroup per (kv head g, row r): out = sum_u acc_u 2^(m_u - M) / L
+// with M = max_u m_u and L = sum_u l_u 2^(m_u - M), units in fixed order.
+constexpr int kMergeThreads = 128;
+constexpr int kMergeChunk = 32;  // accumulator loads in flight per thread
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x / a.R;
+  const int r = blockIdx.x - g * a.R;
+  const int P = a.P, D = a.D;
+  __shared__ float wk[kMaxUnits];
+  __shared__ float red[kMergeThreads / 64][2];
+  const float2* ml = a.ws_ml + static_cast<int64_t>(g) * P * a.R + r;
+  const float* accp = a.ws_acc + (static_cast<int64_t>(g) * P * a.R + r) * D + tid;
+  const int64_t ustride = static_cast<int64_t>(a.R) * D;
+  // issue this thread's (m, l) loads and its first accumulator loads together
+  float2 mlv[kMaxUnits / kMergeThreads];
+#pragma unroll
+  for (int k = 0; k < kMaxUnits / kMergeThreads; ++k) {
+    const int u = tid + k * kMergeThreads;
+    mlv[k] = u < P ? ml[static_cast<int64_t>(u) * a.R] : make_float2(-INFINITY, 0.f);
+  }
+  float av[kMergeChunk];
+#pragma unroll
+  for (int k = 0; k < kMergeChunk; ++k) av[k] = (tid < D && k < P) ? accp[k * ustride] : 0.f;
+  // M: block max over the units
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxUnits / kMergeThreads; ++k) M = fmaxf(M, mlv[k].x);
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
+  if ((tid & 63) == 0) red[tid >> 6][0] = M;
+  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int wv = 1; wv < kMergeThreads / 64; ++wv) M = fmaxf(M, red[wv][0]);
+  // unit weights 2^(m_u - M) and L
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxUnits / kMergeThreads; ++k) {
+    const int u = tid + k * kMergeThreads;
+    const float w = (M == -INFINITY || mlv[k].x == -INFINITY)
+                        ? 0.f
+                        : __builtin_amdgcn_exp2f(mlv[k].x - M);
+    if (u < P) wk[u] = w;
+    L += mlv[k].y * w;
+  }
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) L += __shfl_xor(L, s);
+  if ((tid & 63) == 0) red[tid >> 6][1] = L;
+  __syncthreads();
+  L = 0.f;
+#pragma unroll
+  for (int wv = 0; wv < kMergeThreads / 64; ++wv) L += red[wv][1];
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeChunk; ++k)
+      if (k < P) s += av[k] * wk[k];
+    for (int k0 = kMergeChunk; k0 < P; k0 += kMergeChunk) {
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) av[k] = k0 + k < P ? accp[(k0 + k) * ustride] : 0.f;
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k)
+        if (k0 + k < P) s += av[k] * wk[k0 + k];
+    }
+    const int w = r / a.G, h = g * a.G + (r - w * a.G);
+    a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = L > 0.f ? s / L : 0.f;
+  }
+  if (tid == 0 && !(L > 0.f)) atomicOr(a.status, HW_DEV_NO_TOKENS);
 }
 
 template <typename K>
@@ -660,6 +754,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
+  if (a.P > kMaxUnits || a.D > kMergeThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.R), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -12,10 +12,7 @@ constexpr int kTile = HW_TILE_TOKENS;  // tokens per pool tile
 constexpr int kThreads = 256;          // threads per decode workgroup (4 waves)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxHalf = 64;           // head_dim / 2 upper bound
-
-// Extra sticky bit (internal): a workgroup waited too long at the per-head
-// barrier; the workspace sync words must be zeroed again.
-constexpr int32_t kDevSyncTimeout = 16;
+constexpr int kMaxUnits = 256;         // split-K work units per kv head
 
 // Element offset of key (slot, d) inside one (layer, kv head) plane.  Tiles of
 // 32 slots; inside a tile: [half t/16][chunk d/8][token t%16][d%8].
@@ -33,8 +30,18 @@ __host__ __device__ inline int64_t value_offset(int64_t slot, int d, int D) {
   return tile * 32 * D + ((t & 15) >> 2) * 8 * D + d * 8 + ((t >> 4) << 2) + (t & 3);
 }
 
+// Per-call arrays of the decode kernels, copied into LDS at kernel start with
+// one 16-byte vector load per thread (dynamic indexing of kernel arguments
+// would otherwise cost one serialized memory round trip per array).
+struct alignas(16) DecodeTables {
+  int64_t block_start[HW_MAX_BLOCKS];
+  int32_t block_cap[HW_MAX_BLOCKS];
+  double inv_freq[kMaxHalf];  // theta^(-2i/D), i < D/2
+};
+constexpr int kTablesVec = static_cast<int>(sizeof(DecodeTables) / 16);
+
 // Kernel arguments of the fused decode kernels (passed by value).
-struct DecodeArgs {
+struct alignas(16) DecodeArgs {
   const void* q;            // [W][Hq][D] pool dtype
   const void* k;            // plane of (layer, kv head 0)
   const void* v;
@@ -45,20 +52,19 @@ struct DecodeArgs {
   int32_t* status;
   float2* ws_ml;            // [Hkv][P][R] (m, l) partials
   float* ws_acc;            // [Hkv][P][R][D] partial accumulators
-  uint32_t* ws_sync;        // [2][Hkv] arrival / departure counters
   int64_t plane_elems;      // num_slots * D
+  int32_t plane_bytes;      // plane_elems * element size (< 2^31)
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
   int32_t dtype;            // HW_F32 / HW_BF16
   int32_t xcd_map;          // 1: map consecutive work units to one XCD
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
-  int64_t block_start[HW_MAX_BLOCKS];
-  int32_t block_cap[HW_MAX_BLOCKS];
-  double inv_freq[kMaxHalf];  // theta^(-2i/D), i < D/2
+  DecodeTables tab;
 };
 
 // Launchers (hw_decode.hip).
 hipError_t launch_decode_valu(const DecodeArgs& a, int grid, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 int decode_blocks_per_cu(int path, int dtype, int D, int rows);
 
 // Launchers (hw_cache.hip).

@@ -19,7 +19,6 @@ LIB_PATH = os.path.join(_PKG, "libhogwild_attn.so")
 
 HW_OK, HW_EINVAL, HW_ERANGE, HW_ECAPACITY, HW_EUNSUPPORTED, HW_EWORKSPACE, HW_EHIP = range(7)
 HW_DEV_BAD_ENTRY, HW_DEV_BAD_LENGTH, HW_DEV_NO_TOKENS, HW_DEV_APPEND_OVERFLOW = 1, 2, 4, 8
-HW_DEV_SYNC_TIMEOUT = 16
 HW_F32, HW_BF16 = 0, 1
 HW_TILE_TOKENS = 32
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
@@ -186,11 +185,11 @@ def hw_attn_workspace_bytes(pool: Pool, num_workers: int, num_q_heads: int) -> i
 
 
 def alloc_workspace(pool: Pool, num_workers: int, num_q_heads: int) -> torch.Tensor:
-    """Zeroed workspace (the per-head sync words must start at zero once)."""
+    """Device workspace for hw_attn_decode (needs no initialisation)."""
     n = hw_attn_workspace_bytes(pool, num_workers, num_q_heads)
     if n == 0:
         raise HWError(HW_EINVAL, "hw_attn_workspace_bytes")
-    return torch.zeros(n, dtype=torch.uint8, device=pool.k.device)
+    return torch.empty(n, dtype=torch.uint8, device=pool.k.device)
 
 
 def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,

@@ -92,8 +92,9 @@ def test_decode_host_validation(lib):
 def test_workspace_bytes(lib):
     pool = FakePool()
     n = lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4)
-    # sync words + (m, l) + accumulators for Hkv=2 heads, rows 4, D=128, 256 units per head
-    assert n >= 2 * 256 * 4 * 128 * 4
+    # (m, l) + accumulators for Hkv=2 heads, rows 4, D=128, 128 units per head by default
+    units = 256 // 2
+    assert n >= 2 * units * 4 * (128 + 2) * 4
     assert lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 3) == 0
     hw.hw_set_tuning(hw.PATH_AUTO, 8)
     try:
