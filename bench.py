@@ -30,6 +30,36 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_qwq32b_step_hbm_traffic.md")
+
+
+def kernel_source_sha256() -> str:
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "decode_attention_shared_hw_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel sources changed since the counters were taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_sha256") != kernel_source_sha256():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -45,6 +75,8 @@ def parse():
     ap.add_argument("--cpu-pairs", type=int, default=96,
                     help="(worker, q-head) pairs of one layer timed on the CPU oracle")
     ap.add_argument("--kernel-timing-steps", type=int, default=10)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -186,6 +218,16 @@ def main():
             app_us.append(evs["app"][0].elapsed_time(evs["app"][1]) * 1e3)
     torch.cuda.synchronize()
     flags = hw.hw_pool_status(pool)
+    if args.calibrate_copy > 0:
+        # one plain copy of a known size: HBM counters of this dispatch scale
+        # the decode kernel's counters (bytes read = bytes written = MIB MiB)
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_per_step = gpu_ms / args.steps
     step_s = ms_per_step / 1e3
@@ -211,8 +253,9 @@ def main():
                    if use_graph else "tables + 64 x decode + 1 block append (eager)"},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "decode_mfma<128,2>" if path != hw.PATH_VALU else "decode_valu<bf16>",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+            "kernel": ("decode call = split kernel decode_mfma<128,2> + merge_kernel"
+                       if path != hw.PATH_VALU else "decode call = decode_valu<bf16> + merge_kernel"),
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": dec_avg,
             "p10_us": float(np.percentile(dec_us, 10)),
