@@ -91,7 +91,8 @@ struct Plan {
 // table entries in registers between the load and the visibility pass.
 // issue(): the kernel's own loads, issued with the plan's; commit(): their
 // LDS stores, run before the first barrier.
-constexpr int kEntryRegs = (HW_MAX_WORKERS * HW_MAX_ENTRIES + kThreads - 1) / kThreads;
+template <int NTHR>
+constexpr int entry_regs() { return (HW_MAX_WORKERS * HW_MAX_ENTRIES + NTHR - 1) / NTHR; }
 static_assert(kTablesVec <= kThreads, "per-call arrays exceed one vector per thread");
 
 __device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, int* unit) {
@@ -101,8 +102,9 @@ __device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, i
   *unit = lin - *head * a.P;
 }
 
-template <typename Issue, typename Commit>
+template <int NTHR, typename Issue, typename Commit>
 __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
+  constexpr int kEntryRegs = entry_regs<NTHR>();
   const int tid = threadIdx.x;
   const int WE = a.W * a.E;
   // ---- loads (independent, all in flight together)
@@ -113,7 +115,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   int ent_ne[kEntryRegs];
 #pragma unroll
   for (int k = 0; k < kEntryRegs; ++k) {
-    const int i = tid + k * kThreads;
+    const int i = tid + k * NTHR;
     ent[k].block_id = -1;
     ent[k].view_offset = 0;
     ent_ne[k] = 0;
@@ -133,7 +135,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   if (tid < kTablesVec) reinterpret_cast<u32x4*>(&tab)[tid] = tabv;
   if (tid < a.NB) p.vis[tid] = 0u;
   if (tid < a.W) p.iq[tid] = -1;
-  for (int i = tid; i < a.W * a.NB; i += kThreads) p.off[i] = 0;
+  for (int i = tid; i < a.W * a.NB; i += NTHR) p.off[i] = 0;
   commit();
   __syncthreads();
   // ---- phase B: lengths, visibility and view offsets from the tables
@@ -152,7 +154,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   }
 #pragma unroll
   for (int k = 0; k < kEntryRegs; ++k) {
-    const int i = tid + k * kThreads;
+    const int i = tid + k * NTHR;
     if (i >= WE) continue;
     const int w = i / a.E, e = i - w * a.E;
     const int ne = ent_ne[k];
@@ -181,7 +183,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   // (one wave scans the blocks)
 #pragma unroll
   for (int k = 0; k < kEntryRegs; ++k) {
-    const int i = tid + k * kThreads;
+    const int i = tid + k * NTHR;
     if (i >= WE) continue;
     const int w = i / a.E, e = i - w * a.E;
     if (e >= ent_ne[k] || ((p.bad_workers >> w) & 1u)) continue;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
   __shared__ float vs[kTile * 128];
   __shared__ float ps[HW_MAX_ROWS * (kTile + 1)];
   __shared__ float m_s[HW_MAX_ROWS], l_s[HW_MAX_ROWS], al_s[HW_MAX_ROWS];
-  build_plan(a, plan, [] {}, [] {});
+  build_plan<kThreads>(a, plan, [] {}, [] {});
   const int tid = threadIdx.x;
   const int g = plan.head;
   const int D = a.D, R = a.R, half = D / 2;
@@ -372,8 +374,10 @@ __device__ __forceinline__ TileRef tile_ref(const Plan& p, int nb, int j, int& b
   return r;
 }
 
-// Raw buffer resource over one kv-head plane (gfx9 descriptor word 3).
-// Out-of-range offsets read as zero, so a bad offset can never fault.
+// Raw buffer resource over one kv-head plane (gfx9 descriptor word 3).  The
+// lane offsets are range-checked against the plane; the tile offset (an SGPR
+// operand) is in range by construction: a tile lies inside its block's
+// capacity, whose slots the host checked against the plane.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* p, int32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes,
                                            0x00020000);
@@ -384,44 +388,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* p, int3
 // koff / voff: this lane's byte offsets inside a tile; tile: the tile's byte
 // offset in the plane (wave-uniform, kept in an SGPR).
 template <int D>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                          uint32_t tile, uint32_t koff, uint32_t voff,
-                                          bf16x8 (&kf)[2][D / 32], bf16x8 (&vf)[D / 16]) {
+__device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t tile,
+                                          uint32_t koff, u32x4 (&kf)[2][D / 32]) {
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      kf[h2][s] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                      krs, koff + (h2 * 16 * D + 4 * s * 128) * 2, tile, 0));
-#pragma unroll
-  for (int m = 0; m < D / 16; ++m)
-    vf[m] = __builtin_bit_cast(
-        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + 16 * m * 8 * 2, tile, 0));
+      kf[h2][s] = __builtin_amdgcn_raw_buffer_load_b128(
+          krs, koff + (h2 * 16 * D + 4 * s * 128) * 2, tile, 0);
 }
 
-// Scores, online softmax and P.V for one tile held in registers.
+template <int D>
+__device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t tile,
+                                            uint32_t voff, u32x4 (&vf)[D / 16]) {
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m)
+    vf[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + 16 * m * 8 * 2, tile, 0);
+}
+
+// S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
 // qf: this lane's rotated-query B fragments, [NT][KS] x 64 lanes in LDS.
 template <int D, int NT>
-__device__ __forceinline__ void compute_tile(bf16x8 (&kf)[2][D / 32], bf16x8 (&vf)[D / 16],
-                                             const bf16x8* qf, int lane,
-                                             const bool (&rowvis)[NT], int valid, int q4,
-                                             f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
-                                             float (&l_run)[NT]) {
-  constexpr int KS = D / 32, MT = D / 16;
-  f32x4 sc[2][NT];
+__device__ __forceinline__ void tile_scores(const u32x4 (&kf)[2][D / 32], const bf16x8* qf,
+                                            int lane, f32x4 (&sc)[2][NT]) {
+  constexpr int KS = D / 32;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8 qv = qf[(t * KS + s) * 64 + lane];
-      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][s], qv, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][s], qv, c1, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[0][s]), qv, c0,
+                                                   0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[1][s]), qv, c1,
+                                                   0, 0, 0);
     }
     sc[0][t] = c0;
     sc[1][t] = c1;
   }
+}
+
+// Online softmax of one tile's scores and the P.V update of the running
+// (m, l, O^T); tokens at or past `valid` are dropped, their values zeroed.
+template <int D, int NT>
+__device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT], u32x4 (&vf)[D / 16],
+                                            const bool (&rowvis)[NT], int valid, int q4,
+                                            f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
+                                            float (&l_run)[NT]) {
+  constexpr int MT = D / 16;
   bf16x8 pf[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -465,30 +479,30 @@ __device__ __forceinline__ void compute_tile(bf16x8 (&kf)[2][D / 32], bf16x8 (&v
       keep[e2] = (t0 < valid ? 0x0000ffffu : 0u) | (t1 < valid ? 0xffff0000u : 0u);
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      u32x4 bits = __builtin_bit_cast(u32x4, vf[m]);
-      bits &= keep;
-      vf[m] = __builtin_bit_cast(bf16x8, bits);
-    }
+    for (int m = 0; m < MT; ++m) vf[m] &= keep;
   }
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[m], pf[t], acc[m][t], 0, 0, 0);
+      acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[m]), pf[t],
+                                                          acc[m][t], 0, 0, 0);
 }
 
 template <int D, int NT>
-__global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
+  constexpr int NTHR = kMfmaThreads;
+  constexpr int NWAVE = kMfmaWaves;
+  constexpr int NSTATE = NWAVE / 2;  // wave states held in LDS at once
   constexpr int KS = D / 32;  // k-steps of the QK product
   constexpr int MT = D / 16;  // 16-dim tiles of the output
   constexpr int RP = 16 * NT; // padded rows
   constexpr int HALF = D / 2;
   constexpr int ACC_STRIDE = D + 4;
   constexpr int kWaveState = RP * ACC_STRIDE + 2 * RP;  // one wave's (O^T, m, l)
-  constexpr int kQfFloats = kWaves * NT * KS * 64 * 4;  // rotated-query fragments
+  constexpr int kQfFloats = NWAVE * NT * KS * 64 * 4;   // rotated-query fragments
   constexpr int kUnionFloats =
-      kWaves * kWaveState > kQfFloats ? kWaves * kWaveState : kQfFloats;
+      NSTATE * kWaveState > kQfFloats ? NSTATE * kWaveState : kQfFloats;
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
   // main loop: each wave's rotated-query fragments; afterwards: the four
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
   // this head's query rows, loaded with the plan's loads and staged in LDS so
   // the main loop issues no vector memory operations other than the K/V stream
   constexpr int kQVec = RP * D / 8;
-  constexpr int kQRegs = (kQVec + kThreads - 1) / kThreads;
+  constexpr int kQRegs = (kQVec + NTHR - 1) / NTHR;
   u32x4 qv[kQRegs];
   {
     int h0, u0;
@@ -510,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
     auto issue = [&] {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * kThreads;
+        const int x = tid + k * NTHR;
         const int r = (8 * x) / D, d = (8 * x) - r * D;
         qv[k] = u32x4{0u, 0u, 0u, 0u};
         if (x < kQVec && r < a.R) {
@@ -523,11 +537,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
     auto commit = [&] {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * kThreads;
+        const int x = tid + k * NTHR;
         if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
       }
     };
-    build_plan(a, plan, issue, commit);
+    build_plan<NTHR>(a, plan, issue, commit);
   }
   const int g = plan.head;
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + g * a.plane_elems;
@@ -577,24 +591,49 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
     }
   };
 
-  // One tile in flight per wave.
+  // Software pipeline over this wave's tiles j, j + NWAVE, ...: the next
+  // tile's keys are loaded into the key registers as soon as the current
+  // scores are formed, its values into the value registers right after the
+  // P.V products, so every wave keeps a tile in flight while it computes.
   const __amdgpu_buffer_rsrc_t krs = plane_rsrc(kp, a.plane_bytes);
   const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(vp, a.plane_bytes);
   const uint32_t koff = (q4 * 128 + li * 8) * 2;
   const uint32_t voff = (q4 * 8 * D + li * 8) * 2;
-  int bcur = 0, qb = -1;
-  for (int j = plan.lo + wave; j < plan.hi; j += kWaves) {
-    const TileRef rt = tile_ref<D>(plan, a.NB, j, bcur);
-    if (rt.b != qb) {
-      build_qf(rt.b);
-      qb = rt.b;
+  int j = plan.lo + wave;
+  if (j < plan.hi) {
+    int bcur = 0, qb = -1;
+    TileRef rt = tile_ref<D>(plan, a.NB, j, bcur);
+    u32x4 kf[2][KS], vf[MT];
+    {
+      const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
+      load_keys<D>(krs, tile, koff, kf);
+      load_values<D>(vrs, tile, voff, vf);
     }
-    const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
-    bf16x8 kf[2][KS], vf[MT];
-    load_tile<D>(krs, vrs, tile, koff, voff, kf, vf);
-    // keep all 16 loads ahead of the arithmetic
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile<D, NT>(kf, vf, qf, lane, rowvis, rt.valid, q4, acc, m_run, l_run);
+    for (;;) {
+      if (rt.b != qb) {
+        build_qf(rt.b);
+        qb = rt.b;
+      }
+      f32x4 sc[2][NT];
+      const int jn = j + NWAVE;
+      if (jn >= plan.hi) {
+        tile_scores<D, NT>(kf, qf, lane, sc);
+        tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
+        break;
+      }
+      const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
+      const uint32_t tn = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * 2));
+      tile_scores<D, NT>(kf, qf, lane, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_keys<D>(krs, tn, koff, kf);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
+      __builtin_amdgcn_sched_barrier(0);
+      load_values<D>(vrs, tn, voff, vf);
+      __builtin_amdgcn_sched_barrier(0);
+      j = jn;
+      rt = rn;
+    }
   }
 
   // full row sums (the four lanes of a row hold partial sums)
@@ -603,11 +642,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
     l_run[t] += __shfl_xor(l_run[t], 16);
     l_run[t] += __shfl_xor(l_run[t], 32);
   }
-  // the four waves deposit their states, then every thread combines its
-  // share of the unit's R*D outputs
-  __syncthreads();
-  {
-    float* buf = ubuf + wave * kWaveState;
+  // Combine the waves' softmax states in LDS, half of them at a time: the
+  // upper waves deposit, each lower wave folds in its partner (same fragment
+  // positions, so lane-local), the lower waves deposit, and every thread
+  // combines its share of the unit's R*D outputs over those.
+  auto deposit = [&](float* buf) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + li;
@@ -619,15 +658,38 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
       for (int m = 0; m < MT; ++m)
         *reinterpret_cast<f32x4*>(buf + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
     }
+  };
+  __syncthreads();  // every wave is done with its query fragments
+  if (wave >= NSTATE) deposit(ubuf + (wave - NSTATE) * kWaveState);
+  __syncthreads();
+  if (wave < NSTATE) {
+    const float* src = ubuf + wave * kWaveState;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = 16 * t + li;
+      const float m2 = src[RP * ACC_STRIDE + r];
+      const float l2 = src[RP * ACC_STRIDE + RP + r];
+      const float M = fmaxf(m_run[t], m2);
+      const float s1 = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - M);
+      const float s2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+      l_run[t] = l_run[t] * s1 + l2 * s2;
+      m_run[t] = M;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m][t] = acc[m][t] * s1 +
+                    *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + 16 * m + 4 * q4) * s2;
+    }
   }
   __syncthreads();
+  if (wave < NSTATE) deposit(ubuf + wave * kWaveState);
+  __syncthreads();
   const int64_t pu = partial_index(a, plan);
-  for (int x = tid; x < a.R * (D / 4); x += kThreads) {
+  for (int x = tid; x < a.R * (D / 4); x += NTHR) {
     const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
-    float mw[kWaves];
+    float mw[NSTATE];
     float M = -INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
+    for (int wv = 0; wv < NSTATE; ++wv) {
       mw[wv] = ubuf[wv * kWaveState + RP * ACC_STRIDE + r];
       M = fmaxf(M, mw[wv]);
     }
@@ -635,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeArgs a) {
     f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) {
+      for (int wv = 0; wv < NSTATE; ++wv) {
         const float* src = ubuf + wv * kWaveState;
         const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
         L += src[RP * ACC_STRIDE + RP + r] * sc;
@@ -722,9 +784,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
 }
 
 template <typename K>
-int occupancy(K kernel) {
+int occupancy(K kernel, int threads) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) return 0;
   return n;
 }
 
@@ -743,14 +805,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
   if (a.dtype != HW_BF16 || a.R > 32) return hipErrorInvalidValue;
   if (a.D == 128) {
     if (a.R <= 16)
-      hipLaunchKernelGGL((decode_mfma<128, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<128, 1>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_mfma<128, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<128, 2>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
   } else if (a.D == 64) {
     if (a.R <= 16)
-      hipLaunchKernelGGL((decode_mfma<64, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<64, 1>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_mfma<64, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<64, 2>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -766,10 +828,13 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
 // Resident workgroups per CU of the kernel a launch would use (0 on error).
 int decode_blocks_per_cu(int path, int dtype, int D, int rows) {
   if (path == 2) {
-    if (D == 128) return rows <= 16 ? occupancy(decode_mfma<128, 1>) : occupancy(decode_mfma<128, 2>);
-    return rows <= 16 ? occupancy(decode_mfma<64, 1>) : occupancy(decode_mfma<64, 2>);
+    const int t = kMfmaThreads;
+    if (D == 128)
+      return rows <= 16 ? occupancy(decode_mfma<128, 1>, t) : occupancy(decode_mfma<128, 2>, t);
+    return rows <= 16 ? occupancy(decode_mfma<64, 1>, t) : occupancy(decode_mfma<64, 2>, t);
   }
-  return dtype == HW_F32 ? occupancy(decode_valu<float>) : occupancy(decode_valu<uint16_t>);
+  return dtype == HW_F32 ? occupancy(decode_valu<float>, kThreads)
+                         : occupancy(decode_valu<uint16_t>, kThreads);
 }
 
 }  // namespace hw

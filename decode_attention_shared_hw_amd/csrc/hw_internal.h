@@ -11,6 +11,8 @@ namespace hw {
 constexpr int kTile = HW_TILE_TOKENS;  // tokens per pool tile
 constexpr int kThreads = 256;          // threads per decode workgroup (4 waves)
 constexpr int kWaves = kThreads / 64;
+constexpr int kMfmaThreads = 512;      // threads per MFMA decode workgroup (8 waves)
+constexpr int kMfmaWaves = kMfmaThreads / 64;
 constexpr int kMaxHalf = 64;           // head_dim / 2 upper bound
 constexpr int kMaxUnits = 256;         // split-K work units per kv head
 
