@@ -73,6 +73,16 @@ hw_status check_pool(const hw_pool* p) {
   return HW_OK;
 }
 
+// frac(w / (2 pi)) as a 64-bit binary fraction (rounded): the per-dimension
+// rotation step in revolutions, for exact integer angle reduction on the GPU.
+uint64_t rope_fraction(double w) {
+  const double f = w * 0.15915494309189535;  // 1 / (2 pi)
+  const double fr = f - floor(f);
+  const double scaled = ldexp(fr, 64);
+  if (!(scaled < 18446744073709551616.0)) return 0;  // rounds up to a whole turn
+  return static_cast<uint64_t>(scaled);
+}
+
 int select_path(const hw_pool* p, int rows) {
   if (g_path == 1) return 1;
   if (g_path == 2) return 2;
@@ -211,8 +221,11 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
     a.tab.block_start[b] = pool->block_start[b];
     a.tab.block_cap[b] = pool->block_cap[b];
   }
-  for (int i = 0; i < pool->head_dim / 2; ++i)
-    a.tab.inv_freq[i] = pow(rope_theta, -2.0 * i / static_cast<double>(pool->head_dim));
+  for (int i = 0; i < pool->head_dim / 2; ++i) {
+    const double w = pow(rope_theta, -2.0 * i / static_cast<double>(pool->head_dim));
+    a.tab.inv_freq[i] = w;
+    a.tab.rope_frac[i] = rope_fraction(w);
+  }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = path == 2 ? launch_decode_mfma(a, static_cast<int>(grid), hs)
                            : launch_decode_valu(a, static_cast<int>(grid), hs);

@@ -60,13 +60,16 @@ __device__ __forceinline__ void rope_cos_sin(int64_t delta, double w, float* c, 
   sincosf(static_cast<float>(r), s, c);
 }
 
-// Same angle, evaluated with the hardware v_sin/v_cos (argument in
-// revolutions): the angle is reduced in fp64 to [-1/2, 1/2] revolution, so the
-// result carries ~1e-6 absolute error, far below the bf16 rounding applied to
-// the rotated query on the MFMA path.  Pure ALU: no table loads.
-__device__ __forceinline__ void rope_cos_sin_hw(int64_t delta, double w_rev, float* c, float* s) {
-  const double rev = static_cast<double>(delta) * w_rev;
-  const float fr = static_cast<float>(rev - rint(rev));
+// Same angle in revolutions, reduced exactly: frac is theta^(-2i/D)/(2 pi)
+// mod 1 as a 64-bit binary fraction, so delta * frac mod 2^64 (integer
+// wrap-around) is the angle's fractional revolution; its top 32 bits, as a
+// signed value, give the angle in [-1/2, 1/2) revolution.  The hardware
+// v_sin/v_cos take revolutions; the result carries ~1e-6 absolute error, far
+// below the bf16 rounding applied to the rotated query on the MFMA path.
+__device__ __forceinline__ void rope_cos_sin_fx(int64_t delta, uint64_t frac, float* c,
+                                                float* s) {
+  const uint64_t ph = static_cast<uint64_t>(delta) * frac;
+  const float fr = static_cast<float>(static_cast<int32_t>(ph >> 32)) * 0x1p-32f;
   *s = __builtin_amdgcn_sinf(fr);
   *c = __builtin_amdgcn_cosf(fr);
 }
@@ -80,7 +83,7 @@ struct Plan {
   int32_t off[HW_MAX_WORKERS * HW_MAX_BLOCKS];
   int64_t start[HW_MAX_BLOCKS];       // first slot of each block
   double invf[kMaxHalf];              // theta^(-2i/D)
-  double invf_rev[kMaxHalf];          // theta^(-2i/D) / (2 pi)
+  uint64_t rope_frac[kMaxHalf];       // theta^(-2i/D) / (2 pi) mod 1, 64-bit fixed point
   uint32_t bad_workers;
   int32_t flags;
   int32_t head, unit, lo, hi;
@@ -150,7 +153,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   }
   if (tid < a.D / 2) {
     p.invf[tid] = tab.inv_freq[tid];
-    p.invf_rev[tid] = tab.inv_freq[tid] * 0.15915494309189535;
+    p.rope_frac[tid] = tab.rope_frac[tid];
   }
 #pragma unroll
   for (int k = 0; k < kEntryRegs; ++k) {
@@ -500,13 +503,13 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int HALF = D / 2;
   constexpr int ACC_STRIDE = D + 4;
   constexpr int kWaveState = RP * ACC_STRIDE + 2 * RP;  // one wave's (O^T, m, l)
-  constexpr int kQfFloats = NWAVE * NT * KS * 64 * 4;   // rotated-query fragments
+  constexpr int kQfFloats = kQfBlocks * NT * KS * 64 * 4;  // rotated-query fragments
   constexpr int kUnionFloats =
       NSTATE * kWaveState > kQfFloats ? NSTATE * kWaveState : kQfFloats;
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
-  // main loop: each wave's rotated-query fragments; afterwards: the four
-  // waves' softmax states
+  // main loop: the rotated-query fragments of up to kQfBlocks blocks;
+  // afterwards: the waves' softmax states
   __shared__ __attribute__((aligned(16))) float ubuf[kUnionFloats];
 
   const int tid = threadIdx.x;
@@ -547,7 +550,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + g * a.plane_elems;
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) + g * a.plane_elems;
 
-  bf16x8* qf = reinterpret_cast<bf16x8*>(ubuf) + wave * NT * KS * 64;
   bool rowvis[NT];
   f32x4 acc[MT][NT];
   float m_run[NT], l_run[NT];
@@ -560,79 +562,111 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     for (int m = 0; m < MT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // (a2) rotate this lane's slice of the stacked query rows of head g for
-  // block b: rows 16t+li, dims 8*(4s+q4)..+8 and their rotate-half partners.
-  auto build_qf = [&](int b) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int r = 16 * t + li;
+  // (a2) rotated queries of blocks gb..ge-1, shared by all waves: for each
+  // block the stacked rows of head g rotated by i_q - view_offset of their
+  // worker, scaled, rounded to bf16 and laid out as MFMA B fragments
+  // (row 16t+li, dims 8*(4s+q4)..+8 at qfs[((blk*NT + t)*KS + s)*64 + lane]).
+  // Rows past R or of workers that do not see the block are zero.
+  bf16x8* qfs = reinterpret_cast<bf16x8*>(ubuf);
+  auto rotate_blocks = [&](int gb, int ge) {
+    const int items = (ge - gb) * NT * (KS / 2) * 64;
+    for (int x = tid; x < items; x += NTHR) {
+      const int ln = x & 63;
+      const int y = x >> 6;
+      const int sh = y % (KS / 2);
+      const int t = (y / (KS / 2)) % NT;
+      const int bi = y / ((KS / 2) * NT);
+      const int b = gb + bi;
+      const int r = 16 * t + (ln & 15);
       const int w = r / a.G;
-      rowvis[t] = r < a.R && ((plan.vis[b] >> w) & 1u);
-      const int64_t delta = rowvis[t] ? plan.iq[w] - plan.off[w * a.NB + b] : 0;
+      const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
+      const int wc = vis ? w : 0;
+      const int64_t delta = plan.iq[wc] - plan.off[wc * a.NB + b];
+      const float sc = vis ? a.qscale : 0.f;
+      const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner block is d0 + HALF
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(qs + r * D + d0);
+      const u32x4 yv = *reinterpret_cast<const u32x4*>(qs + r * D + d0 + HALF);
+      bf16x8 lo, hi;
 #pragma unroll
-      for (int s = 0; s < KS / 2; ++s) {
-        const int d0 = 8 * (4 * s + q4);  // < HALF; its partner block is d0 + HALF
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(qs + r * D + d0);
-        const u32x4 yv = *reinterpret_cast<const u32x4*>(qs + r * D + d0 + HALF);
-        bf16x8 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t xw = xv[e >> 1], yw = yv[e >> 1];
-          const float x = __uint_as_float((e & 1) ? (xw & 0xffff0000u) : (xw << 16));
-          const float y = __uint_as_float((e & 1) ? (yw & 0xffff0000u) : (yw << 16));
-          float c = 0.f, sn = 0.f;
-          if (rowvis[t]) rope_cos_sin_hw(delta, plan.invf_rev[d0 + e], &c, &sn);
-          lo[e] = static_cast<__bf16>((x * c - y * sn) * a.qscale);
-          hi[e] = static_cast<__bf16>((y * c + x * sn) * a.qscale);
-        }
-        qf[(t * KS + s) * 64 + lane] = lo;
-        qf[(t * KS + s + KS / 2) * 64 + lane] = hi;
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t xw = xv[e >> 1], yw = yv[e >> 1];
+        const float x0 = __uint_as_float((e & 1) ? (xw & 0xffff0000u) : (xw << 16));
+        const float y0 = __uint_as_float((e & 1) ? (yw & 0xffff0000u) : (yw << 16));
+        float c, sn;
+        rope_cos_sin_fx(delta, plan.rope_frac[d0 + e], &c, &sn);
+        lo[e] = static_cast<__bf16>((x0 * c - y0 * sn) * sc);
+        hi[e] = static_cast<__bf16>((y0 * c + x0 * sn) * sc);
       }
+      qfs[((bi * NT + t) * KS + sh) * 64 + ln] = lo;
+      qfs[((bi * NT + t) * KS + sh + KS / 2) * 64 + ln] = hi;
     }
   };
 
-  // Software pipeline over this wave's tiles j, j + NWAVE, ...: the next
-  // tile's keys are loaded into the key registers as soon as the current
-  // scores are formed, its values into the value registers right after the
-  // P.V products, so every wave keeps a tile in flight while it computes.
+  // Blocks with tiles in [lo, hi) form the index range [b_first, b_last];
+  // they are rotated kQfBlocks at a time.  Within a group, a software
+  // pipeline runs over this wave's tiles j, j + NWAVE, ...: the next tile's
+  // keys are loaded into the key registers as soon as the current scores are
+  // formed, its values into the value registers right after the P.V products,
+  // so every wave keeps a tile in flight while it computes.  The group's
+  // first tile is requested before the rotation.
   const __amdgpu_buffer_rsrc_t krs = plane_rsrc(kp, a.plane_bytes);
   const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(vp, a.plane_bytes);
   const uint32_t koff = (q4 * 128 + li * 8) * 2;
   const uint32_t voff = (q4 * 8 * D + li * 8) * 2;
-  int j = plan.lo + wave;
-  if (j < plan.hi) {
-    int bcur = 0, qb = -1;
-    TileRef rt = tile_ref<D>(plan, a.NB, j, bcur);
-    u32x4 kf[2][KS], vf[MT];
-    {
-      const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
-      load_keys<D>(krs, tile, koff, kf);
-      load_values<D>(vrs, tile, voff, vf);
-    }
-    for (;;) {
-      if (rt.b != qb) {
-        build_qf(rt.b);
-        qb = rt.b;
+  if (plan.lo < plan.hi) {
+    const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
+    const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
+    for (int gb = b_first; gb <= b_last; gb += kQfBlocks) {
+      const int ge = min(gb + kQfBlocks, b_last + 1);
+      const int t_lo = max(plan.lo, plan.tile0[gb]);
+      const int t_hi = min(plan.hi, plan.tile0[ge]);
+      int j = t_lo + wave;
+      int bcur = gb;
+      TileRef rt = {0, 0, 0};
+      u32x4 kf[2][KS], vf[MT];
+      if (j < t_hi) {
+        rt = tile_ref<D>(plan, a.NB, j, bcur);
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
+        load_keys<D>(krs, tile, koff, kf);
+        load_values<D>(vrs, tile, voff, vf);
       }
-      f32x4 sc[2][NT];
-      const int jn = j + NWAVE;
-      if (jn >= plan.hi) {
-        tile_scores<D, NT>(kf, qf, lane, sc);
-        tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
-        break;
+      if (gb != b_first) __syncthreads();  // the previous group's fragments are consumed
+      rotate_blocks(gb, ge);
+      __syncthreads();
+      if (j < t_hi) {
+        int qb = -1;
+        const bf16x8* qf = qfs;
+        for (;;) {
+          if (rt.b != qb) {
+            qb = rt.b;
+            qf = qfs + (qb - gb) * NT * KS * 64;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const int r = 16 * t + li;
+              rowvis[t] = r < a.R && ((plan.vis[qb] >> (r / a.G)) & 1u);
+            }
+          }
+          f32x4 sc[2][NT];
+          const int jn = j + NWAVE;
+          if (jn >= t_hi) {
+            tile_scores<D, NT>(kf, qf, lane, sc);
+            tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
+            break;
+          }
+          const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
+          const uint32_t tn = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * 2));
+          tile_scores<D, NT>(kf, qf, lane, sc);
+          __builtin_amdgcn_sched_barrier(0);
+          load_keys<D>(krs, tn, koff, kf);
+          __builtin_amdgcn_sched_barrier(0);
+          tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
+          __builtin_amdgcn_sched_barrier(0);
+          load_values<D>(vrs, tn, voff, vf);
+          __builtin_amdgcn_sched_barrier(0);
+          j = jn;
+          rt = rn;
+        }
       }
-      const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
-      const uint32_t tn = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * 2));
-      tile_scores<D, NT>(kf, qf, lane, sc);
-      __builtin_amdgcn_sched_barrier(0);
-      load_keys<D>(krs, tn, koff, kf);
-      __builtin_amdgcn_sched_barrier(0);
-      tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
-      __builtin_amdgcn_sched_barrier(0);
-      load_values<D>(vrs, tn, voff, vf);
-      __builtin_amdgcn_sched_barrier(0);
-      j = jn;
-      rt = rn;
     }
   }
 
@@ -646,10 +680,12 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // upper waves deposit, each lower wave folds in its partner (same fragment
   // positions, so lane-local), the lower waves deposit, and every thread
   // combines its share of the unit's R*D outputs over those.
+  // Only rows below R carry data (padding rows are skipped).
   auto deposit = [&](float* buf) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + li;
+      if (r >= a.R) continue;
       if (q4 == 0) {
         buf[RP * ACC_STRIDE + r] = m_run[t];
         buf[RP * ACC_STRIDE + RP + r] = l_run[t];
@@ -659,7 +695,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         *reinterpret_cast<f32x4*>(buf + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
     }
   };
-  __syncthreads();  // every wave is done with its query fragments
+  __syncthreads();  // every wave is done with the query fragments
   if (wave >= NSTATE) deposit(ubuf + (wave - NSTATE) * kWaveState);
   __syncthreads();
   if (wave < NSTATE) {
@@ -667,6 +703,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + li;
+      if (r >= a.R) continue;
       const float m2 = src[RP * ACC_STRIDE + r];
       const float l2 = src[RP * ACC_STRIDE + RP + r];
       const float M = fmaxf(m_run[t], m2);

@@ -13,6 +13,7 @@ constexpr int kThreads = 256;          // threads per decode workgroup (4 waves)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMfmaThreads = 512;      // threads per MFMA decode workgroup (8 waves)
 constexpr int kMfmaWaves = kMfmaThreads / 64;
+constexpr int kQfBlocks = 8;           // blocks whose rotated queries are held in LDS at once
 constexpr int kMaxHalf = 64;           // head_dim / 2 upper bound
 constexpr int kMaxUnits = 256;         // split-K work units per kv head
 
@@ -39,6 +40,7 @@ struct alignas(16) DecodeTables {
   int64_t block_start[HW_MAX_BLOCKS];
   int32_t block_cap[HW_MAX_BLOCKS];
   double inv_freq[kMaxHalf];  // theta^(-2i/D), i < D/2
+  uint64_t rope_frac[kMaxHalf];  // frac(theta^(-2i/D) / (2 pi)) * 2^64, i < D/2
 };
 constexpr int kTablesVec = static_cast<int>(sizeof(DecodeTables) / 16);
 

@@ -137,6 +137,22 @@ def test_single_visible_token_returns_value_exactly(path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("units", [1, 2])
+def test_unit_spanning_many_blocks(path, units):
+    # one or two work units cover 8-17 visible blocks (16 workers, 32 rows):
+    # the rotated queries are built for several groups of blocks in turn
+    # inside one workgroup
+    wl = _custom(16, 2, 1, 128, [40] + [3] * 12 + [0, 33, 1, 64])
+    hw.hw_set_tuning(path, units)
+    s = Setup(wl, poison_unused=True)
+    ref, rc = s.oracle_decode()
+    assert rc == 0
+    got = s.decode()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, torch.bfloat16, f"many blocks units {units} path {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_unit_count_does_not_change_the_result(path):
     wl = _custom(4, 40, 8, 128, [3000, 100, 31, 250, 7])
     s = Setup(wl)
