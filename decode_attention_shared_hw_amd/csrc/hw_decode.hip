@@ -89,6 +89,20 @@ struct Plan {
   int32_t head, unit, lo, hi;
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16, then the last lane of row 0
+// (row 2) is added to row 1 (row 3), and the last lane of row 1 to rows 2
+// and 3.  Lanes shifted in from outside a row read 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
 // Every global load of the prologue is issued before its first barrier, so
 // the plan costs one memory round trip.  Each thread keeps up to kEntryRegs
 // table entries in registers between the load and the visibility pass.
@@ -195,22 +209,14 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
       atomicMax(&p.iq[w], static_cast<long long>(ent[k].view_offset) + p.len[b] - 1);
   }
   if (tid >= 64 && tid < 128) {
-    const int lane = tid - 64;
-    int nt = 0;
-    for (int b0 = 0; b0 < a.NB; b0 += 64) {
-      const int b = b0 + lane;
-      int v = 0;
-      if (b < a.NB && p.vis[b] != 0u && p.len[b] > 0) v = (p.len[b] + kTile - 1) / kTile;
-      int incl = v;
-#pragma unroll
-      for (int s = 1; s < 64; s <<= 1) {
-        const int y = __shfl_up(incl, s);
-        if (lane >= s) incl += y;
-      }
-      if (b < a.NB) p.tile0[b] = nt + incl - v;
-      nt += __shfl(incl, 63);
-    }
-    if (lane == 0) {
+    // one wave scans the blocks (NB <= 64, one per lane)
+    const int b = tid - 64;
+    int v = 0;
+    if (b < a.NB && p.vis[b] != 0u && p.len[b] > 0) v = (p.len[b] + kTile - 1) / kTile;
+    const int incl = wave_inclusive_scan(v);
+    if (b < a.NB) p.tile0[b] = incl - v;
+    const int nt = __builtin_amdgcn_readlane(incl, 63);
+    if (b == 0) {
       p.tile0[a.NB] = nt;
       const int64_t n = nt;
       p.lo = static_cast<int>(n * p.unit / a.P);
@@ -748,75 +754,56 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
 }
 
 // ----------------------------------------------------------- merge kernel
-// (a4) One workgroup per (kv head g, row r): out = sum_u acc_u 2^(m_u - M) / L
-// with M = max_u m_u and L = sum_u l_u 2^(m_u - M), units in fixed order.
-constexpr int kMergeThreads = 128;
-constexpr int kMergeChunk = 32;  // accumulator loads in flight per thread
+// (a4) One workgroup per (kv head g, row r), one thread per output dim:
+// out = sum_u acc_u 2^(m_u - M) / L with M = max_u m_u and
+// L = sum_u l_u 2^(m_u - M), units in fixed order.  Units are taken
+// kMergeChunk at a time: lane k of every wave loads unit u0+k's (m, l) and
+// forms its weight, which the lanes read back with readlane while summing
+// their accumulators, so the kernel has neither LDS nor barriers; the
+// running (M, L, sum) is rescaled when a later chunk raises M.
+constexpr int kMergeChunk = 32;  // units whose loads are in flight together
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
-  const int tid = threadIdx.x;
+// Lane k's value of x (the builtin moves 32-bit integers: pass the bits).
+__device__ __forceinline__ float readlane_f32(float x, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
+}
+
+__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
+  const int tid = threadIdx.x;  // output dim
+  const int lane = tid & 63;
   const int g = blockIdx.x / a.R;
   const int r = blockIdx.x - g * a.R;
   const int P = a.P, D = a.D;
-  __shared__ float wk[kMaxUnits];
-  __shared__ float red[kMergeThreads / 64][2];
   const float2* ml = a.ws_ml + static_cast<int64_t>(g) * P * a.R + r;
   const float* accp = a.ws_acc + (static_cast<int64_t>(g) * P * a.R + r) * D + tid;
   const int64_t ustride = static_cast<int64_t>(a.R) * D;
-  // issue this thread's (m, l) loads and its first accumulator loads together
-  float2 mlv[kMaxUnits / kMergeThreads];
+  float M = -INFINITY, L = 0.f, s = 0.f;
+  for (int u0 = 0; u0 < P; u0 += kMergeChunk) {
+    const int uk = u0 + (lane & (kMergeChunk - 1));
+    const float2 mv = ml[static_cast<int64_t>(min(uk, P - 1)) * a.R];
+    float av[kMergeChunk];
 #pragma unroll
-  for (int k = 0; k < kMaxUnits / kMergeThreads; ++k) {
-    const int u = tid + k * kMergeThreads;
-    mlv[k] = u < P ? ml[static_cast<int64_t>(u) * a.R] : make_float2(-INFINITY, 0.f);
-  }
-  float av[kMergeChunk];
+    for (int k = 0; k < kMergeChunk; ++k) av[k] = accp[min(u0 + k, P - 1) * ustride];
+    const float mk = uk < P ? mv.x : -INFINITY;
+    float Mc = M;
 #pragma unroll
-  for (int k = 0; k < kMergeChunk; ++k) av[k] = (tid < D && k < P) ? accp[k * ustride] : 0.f;
-  // M: block max over the units
-  float M = -INFINITY;
+    for (int k = 0; k < kMergeChunk; ++k) Mc = fmaxf(Mc, readlane_f32(mk, k));
+    // while no unit has tokens every weight is 0 and (L, sum) stay 0
+    const float Mu = Mc == -INFINITY ? 0.f : Mc;
+    const float wk = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - Mu);
+    const float lk = uk < P ? mv.y * wk : 0.f;
+    const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mu);
+    L *= sc;
+    s *= sc;
 #pragma unroll
-  for (int k = 0; k < kMaxUnits / kMergeThreads; ++k) M = fmaxf(M, mlv[k].x);
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) M = fmaxf(M, __shfl_xor(M, s));
-  if ((tid & 63) == 0) red[tid >> 6][0] = M;
-  __syncthreads();
-  M = red[0][0];
-#pragma unroll
-  for (int wv = 1; wv < kMergeThreads / 64; ++wv) M = fmaxf(M, red[wv][0]);
-  // unit weights 2^(m_u - M) and L
-  float L = 0.f;
-#pragma unroll
-  for (int k = 0; k < kMaxUnits / kMergeThreads; ++k) {
-    const int u = tid + k * kMergeThreads;
-    const float w = (M == -INFINITY || mlv[k].x == -INFINITY)
-                        ? 0.f
-                        : __builtin_amdgcn_exp2f(mlv[k].x - M);
-    if (u < P) wk[u] = w;
-    L += mlv[k].y * w;
-  }
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) L += __shfl_xor(L, s);
-  if ((tid & 63) == 0) red[tid >> 6][1] = L;
-  __syncthreads();
-  L = 0.f;
-#pragma unroll
-  for (int wv = 0; wv < kMergeThreads / 64; ++wv) L += red[wv][1];
-  if (tid < D) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k)
-      if (k < P) s += av[k] * wk[k];
-    for (int k0 = kMergeChunk; k0 < P; k0 += kMergeChunk) {
-#pragma unroll
-      for (int k = 0; k < kMergeChunk; ++k) av[k] = k0 + k < P ? accp[(k0 + k) * ustride] : 0.f;
-#pragma unroll
-      for (int k = 0; k < kMergeChunk; ++k)
-        if (k0 + k < P) s += av[k] * wk[k0 + k];
+    for (int k = 0; k < kMergeChunk; ++k) {
+      L += readlane_f32(lk, k);
+      s += av[k] * readlane_f32(wk, k);
     }
-    const int w = r / a.G, h = g * a.G + (r - w * a.G);
-    a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = L > 0.f ? s / L : 0.f;
+    M = Mc;
   }
+  const int w = r / a.G, h = g * a.G + (r - w * a.G);
+  a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = L > 0.f ? s / L : 0.f;
   if (tid == 0 && !(L > 0.f)) atomicOr(a.status, HW_DEV_NO_TOKENS);
 }
 
@@ -857,8 +844,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-  if (a.P > kMaxUnits || a.D > kMergeThreads) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.R), dim3(kMergeThreads), 0, s, a);
+  if (a.P > kMaxUnits || a.D > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.R), dim3(a.D), 0, s, a);
   return hipGetLastError();
 }
 
