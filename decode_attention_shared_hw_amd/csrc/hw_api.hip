@@ -98,17 +98,20 @@ int units_per_head_setting(int num_kv_heads) {
 }
 
 struct WsLayout {
-  size_t ml_off, acc_off, total;
+  size_t ml_off, acc_off, hint_off, total;
 };
 
-// [Hkv][units][rows] (m, l) pairs, then [Hkv][units][rows][D] accumulators.
+// [Hkv][units][rows] (m, l) pairs, then [Hkv][units][rows][D] accumulators,
+// then [Hkv][units][kMfmaWaves] first-tile hints.
 WsLayout ws_layout(int hkv, int units, int rows, int D) {
   WsLayout w;
   w.ml_off = 0;
   const size_t ml = static_cast<size_t>(hkv) * units * rows * sizeof(float2);
   w.acc_off = 256 * ((ml + 255) / 256);
   const size_t acc = static_cast<size_t>(hkv) * units * rows * D * sizeof(float);
-  w.total = w.acc_off + acc;
+  w.hint_off = 256 * ((w.acc_off + acc + 255) / 256);
+  const size_t hint = static_cast<size_t>(hkv) * units * kMfmaWaves * sizeof(uint32_t);
+  w.total = w.hint_off + hint;
   return w;
 }
 
@@ -202,6 +205,7 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
   char* ws = static_cast<char*>(workspace);
   a.ws_ml = reinterpret_cast<float2*>(ws + wl.ml_off);
   a.ws_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+  a.ws_hint = reinterpret_cast<uint32_t*>(ws + wl.hint_off);
   a.plane_elems = plane;
   a.plane_bytes = static_cast<int32_t>(plane * static_cast<int64_t>(esz));
   a.W = num_workers;

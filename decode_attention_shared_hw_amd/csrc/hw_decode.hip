@@ -415,6 +415,26 @@ __device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t
     vf[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + 16 * m * 8 * 2, tile, 0);
 }
 
+// The same loads with the tile offset in the range-checked lane offset: a
+// tile offset past the plane reads zeros, so any value may be passed (used
+// for the speculative first tile, whose offset comes from the last call).
+template <int D>
+__device__ __forceinline__ void load_tile_checked(__amdgpu_buffer_rsrc_t krs,
+                                                  __amdgpu_buffer_rsrc_t vrs, uint32_t tile,
+                                                  uint32_t koff, uint32_t voff,
+                                                  u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16]) {
+  const uint32_t kb = koff + tile, vb = voff + tile;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      kf[h2][s] = __builtin_amdgcn_raw_buffer_load_b128(
+          krs, kb + (h2 * 16 * D + 4 * s * 128) * 2, 0, 0);
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m)
+    vf[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vb + 16 * m * 8 * 2, 0, 0);
+}
+
 // S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
 // qf: this lane's rotated-query B fragments, [NT][KS] x 64 lanes in LDS.
 template <int D, int NT>
@@ -527,9 +547,24 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int kQVec = RP * D / 8;
   constexpr int kQRegs = (kQVec + NTHR - 1) / NTHR;
   u32x4 qv[kQRegs];
+  // Speculative first tile: within a decode step every layer's call has the
+  // same plan, so each wave's first tile of the last call (hint) is requested
+  // before the plan is built, and kept if the plan confirms it.
+  int h0, u0;
+  plan_head_unit(a, &h0, &u0);
+  const uint32_t koff = (q4 * 128 + li * 8) * 2;
+  const uint32_t voff = (q4 * 8 * D + li * 8) * 2;
+  const __amdgpu_buffer_rsrc_t krs = plane_rsrc(
+      static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(h0) * a.plane_elems, a.plane_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(
+      static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(h0) * a.plane_elems, a.plane_bytes);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t* hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
+  const uint32_t spec = *hint;  // uniform: a scalar load
+  u32x4 kf[2][KS], vf[MT];
   {
-    int h0, u0;
-    plan_head_unit(a, &h0, &u0);
+    // the plan's and the query's loads go first: loads complete in issue
+    // order, so the plan can consume them while the tile is still in flight
     auto issue = [&] {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
@@ -542,6 +577,9 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
               *reinterpret_cast<const u32x4*>(qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile_checked<D>(krs, vrs, spec, koff, voff, kf, vf);
+      __builtin_amdgcn_sched_barrier(0);
     };
     auto commit = [&] {
 #pragma unroll
@@ -552,10 +590,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     };
     build_plan<NTHR>(a, plan, issue, commit);
   }
-  const int g = plan.head;
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + g * a.plane_elems;
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + g * a.plane_elems;
-
   bool rowvis[NT];
   f32x4 acc[MT][NT];
   float m_run[NT], l_run[NT];
@@ -615,10 +649,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // formed, its values into the value registers right after the P.V products,
   // so every wave keeps a tile in flight while it computes.  The group's
   // first tile is requested before the rotation.
-  const __amdgpu_buffer_rsrc_t krs = plane_rsrc(kp, a.plane_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(vp, a.plane_bytes);
-  const uint32_t koff = (q4 * 128 + li * 8) * 2;
-  const uint32_t voff = (q4 * 8 * D + li * 8) * 2;
+  uint32_t first = 0xffffffffu;  // this wave's first tile (byte offset), none: all ones
   if (plan.lo < plan.hi) {
     const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
     const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
@@ -629,12 +660,14 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       int j = t_lo + wave;
       int bcur = gb;
       TileRef rt = {0, 0, 0};
-      u32x4 kf[2][KS], vf[MT];
       if (j < t_hi) {
         rt = tile_ref<D>(plan, a.NB, j, bcur);
         const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
-        load_keys<D>(krs, tile, koff, kf);
-        load_values<D>(vrs, tile, voff, vf);
+        if (gb == b_first) first = tile;
+        if (gb != b_first || tile != spec) {
+          load_keys<D>(krs, tile, koff, kf);
+          load_values<D>(vrs, tile, voff, vf);
+        }
       }
       if (gb != b_first) __syncthreads();  // the previous group's fragments are consumed
       rotate_blocks(gb, ge);
@@ -675,6 +708,8 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       }
     }
   }
+
+  if (lane == 0) *hint = first;
 
   // full row sums (the four lanes of a row hold partial sums)
 #pragma unroll

@@ -56,6 +56,7 @@ struct alignas(16) DecodeArgs {
   int32_t* status;
   float2* ws_ml;            // [Hkv][P][R] (m, l) partials
   float* ws_acc;            // [Hkv][P][R][D] partial accumulators
+  uint32_t* ws_hint;        // [Hkv][P][kMfmaWaves] first tile (byte offset) of the last call
   int64_t plane_elems;      // num_slots * D
   int32_t plane_bytes;      // plane_elems * element size (< 2^31)
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
