@@ -28,6 +28,8 @@
 //                     layout matches them), rows = W*G <= 16*NT <= 32.
 #include <math.h>
 
+#include <type_traits>
+
 #include "hw_internal.h"
 
 namespace hw {
@@ -383,6 +385,9 @@ __device__ __forceinline__ TileRef tile_ref(const Plan& p, int nb, int j, int& b
   return r;
 }
 
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+constexpr int kOneLevelRows = 24;  // rows up to which all waves' states fit in LDS together
+
 // Raw buffer resource over one kv-head plane (gfx9 descriptor word 3).  The
 // lane offsets are range-checked against the plane; the tile offset (an SGPR
 // operand) is in range by construction: a tile lies inside its block's
@@ -528,10 +533,13 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int RP = 16 * NT; // padded rows
   constexpr int HALF = D / 2;
   constexpr int ACC_STRIDE = D + 4;
-  constexpr int kWaveState = RP * ACC_STRIDE + 2 * RP;  // one wave's (O^T, m, l)
+  // one wave's (O^T, m, l) with room for RC1 rows (all waves at once) or RP
+  // rows (half of the waves at a time)
+  constexpr int RC1 = RP < kOneLevelRows ? RP : kOneLevelRows;
+  constexpr int kState1 = RC1 * ACC_STRIDE + 2 * RC1;
+  constexpr int kState2 = RP * ACC_STRIDE + 2 * RP;
   constexpr int kQfFloats = kQfBlocks * NT * KS * 64 * 4;  // rotated-query fragments
-  constexpr int kUnionFloats =
-      NSTATE * kWaveState > kQfFloats ? NSTATE * kWaveState : kQfFloats;
+  constexpr int kUnionFloats = cmax(cmax(NWAVE * kState1, NSTATE * kState2), kQfFloats);
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
   // main loop: the rotated-query fragments of up to kQfBlocks blocks;
@@ -717,73 +725,84 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     l_run[t] += __shfl_xor(l_run[t], 16);
     l_run[t] += __shfl_xor(l_run[t], 32);
   }
-  // Combine the waves' softmax states in LDS, half of them at a time: the
-  // upper waves deposit, each lower wave folds in its partner (same fragment
-  // positions, so lane-local), the lower waves deposit, and every thread
-  // combines its share of the unit's R*D outputs over those.
-  // Only rows below R carry data (padding rows are skipped).
-  auto deposit = [&](float* buf) {
+  // Combine the waves' softmax states (O^T rows below R, m, l) in LDS.  When
+  // every wave's state fits (R <= RC1 rows), all waves deposit at once;
+  // otherwise half of them at a time: the upper waves deposit, each lower
+  // wave folds in its partner (same fragment positions, so lane-local), and
+  // the lower waves deposit.  Then every thread combines its share of the
+  // unit's R*D outputs over the deposited states and stores the partial.
+  auto deposit = [&](float* buf, int rc) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + li;
       if (r >= a.R) continue;
       if (q4 == 0) {
-        buf[RP * ACC_STRIDE + r] = m_run[t];
-        buf[RP * ACC_STRIDE + RP + r] = l_run[t];
+        buf[rc * ACC_STRIDE + r] = m_run[t];
+        buf[rc * ACC_STRIDE + rc + r] = l_run[t];
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         *reinterpret_cast<f32x4*>(buf + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
     }
   };
-  __syncthreads();  // every wave is done with the query fragments
-  if (wave >= NSTATE) deposit(ubuf + (wave - NSTATE) * kWaveState);
-  __syncthreads();
-  if (wave < NSTATE) {
-    const float* src = ubuf + wave * kWaveState;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int r = 16 * t + li;
-      if (r >= a.R) continue;
-      const float m2 = src[RP * ACC_STRIDE + r];
-      const float l2 = src[RP * ACC_STRIDE + RP + r];
-      const float M = fmaxf(m_run[t], m2);
-      const float s1 = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - M);
-      const float s2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-      l_run[t] = l_run[t] * s1 + l2 * s2;
-      m_run[t] = M;
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[m][t] = acc[m][t] * s1 +
-                    *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + 16 * m + 4 * q4) * s2;
-    }
-  }
-  __syncthreads();
-  if (wave < NSTATE) deposit(ubuf + wave * kWaveState);
-  __syncthreads();
   const int64_t pu = partial_index(a, plan);
-  for (int x = tid; x < a.R * (D / 4); x += NTHR) {
-    const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
-    float mw[NSTATE];
-    float M = -INFINITY;
+  auto combine_store = [&](auto nstate_c, int state, int rc) {
+    constexpr int NS = decltype(nstate_c)::value;
+    for (int x = tid; x < a.R * (D / 4); x += NTHR) {
+      const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
+      float mw[NS];
+      float M = -INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < NSTATE; ++wv) {
-      mw[wv] = ubuf[wv * kWaveState + RP * ACC_STRIDE + r];
-      M = fmaxf(M, mw[wv]);
+      for (int wv = 0; wv < NS; ++wv) {
+        mw[wv] = ubuf[wv * state + rc * ACC_STRIDE + r];
+        M = fmaxf(M, mw[wv]);
+      }
+      float L = 0.f;
+      f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int wv = 0; wv < NS; ++wv) {
+          const float* src = ubuf + wv * state;
+          const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
+          L += src[rc * ACC_STRIDE + rc + r] * sc;
+          O += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d4) * sc;
+        }
+      }
+      *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d4) = O;
+      if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
     }
-    float L = 0.f;
-    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
+  };
+  __syncthreads();  // every wave is done with the query fragments
+  if (a.R <= RC1) {
+    deposit(ubuf + wave * kState1, RC1);
+    __syncthreads();
+    combine_store(std::integral_constant<int, NWAVE>{}, kState1, RC1);
+  } else {
+    if (wave >= NSTATE) deposit(ubuf + (wave - NSTATE) * kState2, RP);
+    __syncthreads();
+    if (wave < NSTATE) {
+      const float* src = ubuf + wave * kState2;
 #pragma unroll
-      for (int wv = 0; wv < NSTATE; ++wv) {
-        const float* src = ubuf + wv * kWaveState;
-        const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
-        L += src[RP * ACC_STRIDE + RP + r] * sc;
-        O += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d4) * sc;
+      for (int t = 0; t < NT; ++t) {
+        const int r = 16 * t + li;
+        if (r >= a.R) continue;
+        const float m2 = src[RP * ACC_STRIDE + r];
+        const float l2 = src[RP * ACC_STRIDE + RP + r];
+        const float M = fmaxf(m_run[t], m2);
+        const float s1 = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - M);
+        const float s2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+        l_run[t] = l_run[t] * s1 + l2 * s2;
+        m_run[t] = M;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[m][t] = acc[m][t] * s1 +
+                      *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + 16 * m + 4 * q4) * s2;
       }
     }
-    *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d4) = O;
-    if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
+    __syncthreads();
+    if (wave < NSTATE) deposit(ubuf + wave * kState2, RP);
+    __syncthreads();
+    combine_store(std::integral_constant<int, NSTATE>{}, kState2, RP);
   }
   if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
 }
