@@ -50,6 +50,8 @@ struct AppendArgs {
   int32_t src, dst;
   int32_t D, dtype;
   int32_t tiles_per_plane;  // dst tiles a run of up to cap_src tokens can touch
+  int32_t xcd_map;          // 1: consecutive tiles of a plane on one XCD
+  int64_t planes;           // layers * kv heads
   double inv_freq[kMaxHalf];
 };
 
@@ -73,68 +75,138 @@ __device__ uint16_t f64_to_bf16_bits(double x) {
   return static_cast<uint16_t>(__float_as_uint(static_cast<float>(y)) >> 16);
 }
 
+__device__ __forceinline__ double to_f64(float x) { return x; }
+__device__ __forceinline__ double to_f64(uint16_t b) {
+  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
+}
 template <typename T>
-__device__ __forceinline__ double load_f64(const T* p, int64_t i);
+__device__ __forceinline__ T round_to(double x);
 template <>
-__device__ __forceinline__ double load_f64<float>(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float round_to<float>(double x) { return static_cast<float>(x); }
 template <>
-__device__ __forceinline__ double load_f64<uint16_t>(const uint16_t* p, int64_t i) {
-  return static_cast<double>(__uint_as_float(static_cast<uint32_t>(p[i]) << 16));
-}
-__device__ __forceinline__ void store_rounded(float* p, int64_t i, double x) {
-  p[i] = static_cast<float>(x);
-}
-__device__ __forceinline__ void store_rounded(uint16_t* p, int64_t i, double x) {
-  p[i] = f64_to_bf16_bits(x);
-}
+__device__ __forceinline__ uint16_t round_to<uint16_t>(double x) { return f64_to_bf16_bits(x); }
 
 // One workgroup per (layer*kv head plane, destination tile).  A src key at
 // local position j moves to dst position len_dst + j: rotating it by len_dst
 // re-encodes it there (rho(rho(x, j), n) = rho(x, j + n)).
+//
+// Data move in 16-byte chunks (kChunk elements).  In the key layout a chunk
+// holds consecutive dims of one token, so a lane loads a chunk and its
+// rotate-half partner chunk (dims + D/2) of one src token, rotates the pairs
+// in fp64 and stores both rounded.  In the value layout a chunk holds one dim
+// of several tokens, and the shift by len_dst mixes tokens of two src tiles:
+// the run's src values are staged in LDS (token-major), then every dst chunk
+// the run touches is rebuilt, keeping the tokens outside the run, and stored
+// whole.
 template <typename T>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma clang fp contract(off)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kChunk = 16 / static_cast<int>(sizeof(T));
   const int tid = threadIdx.x;
-  const int64_t plane = blockIdx.x / a.tiles_per_plane;
-  const int k = blockIdx.x - static_cast<int>(plane * a.tiles_per_plane);
+  // consecutive dst tiles of one plane on one XCD (they share src tiles)
+  int lin = blockIdx.x;
+  if (a.xcd_map) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t plane = lin / a.tiles_per_plane;
+  const int k = lin - static_cast<int>(plane * a.tiles_per_plane);
+  if (plane >= a.planes) return;
   const int32_t ls = a.block_len[a.src];
   const int32_t ld = a.block_len[a.dst];
   if (ls <= 0 || ld < 0 || ls > a.cap_src || static_cast<int64_t>(ld) + ls > a.cap_dst) return;
   const int64_t first = a.start_dst + ld;  // first destination slot
   const int64_t last = first + ls;
-  const int64_t t0 = ((first >> 5) + k) << 5;
+  const int64_t t0 = ((first >> 5) + k) << 5;  // this dst tile's first slot
   const int64_t s_begin = first > t0 ? first : t0;
   const int64_t s_end = last < t0 + 32 ? last : t0 + 32;
   if (s_begin >= s_end) return;
   const int D = a.D, half = D / 2;
+  const int n = static_cast<int>(s_end - s_begin);
+  const int64_t ss0 = a.start_src + (s_begin - first);  // src slot of the first token
   __shared__ double cs[2 * kMaxHalf];
+  __shared__ T vstage[32 * 128];  // run values, [token - s_begin][dim]
   if (tid < half) {
     double s, c;
     sincos(static_cast<double>(ld) * a.inv_freq[tid], &s, &c);
     cs[2 * tid] = c;
     cs[2 * tid + 1] = s;
   }
-  __syncthreads();
   T* kp = static_cast<T*>(a.k) + plane * a.plane_elems;
   T* vp = static_cast<T*>(a.v) + plane * a.plane_elems;
-  const int n = static_cast<int>(s_end - s_begin);
-  for (int x = tid; x < n * half; x += 256) {
-    const int64_t sd = s_begin + x / half;
-    const int i = x % half;
-    const int64_t ss = a.start_src + (sd - first);
-    const double x0 = load_f64(kp, key_offset(ss, i, D));
-    const double x1 = load_f64(kp, key_offset(ss, i + half, D));
-    const double c = cs[2 * i], s = cs[2 * i + 1];
-    const double y0 = x0 * c - x1 * s;
-    const double y1 = x1 * c + x0 * s;
-    store_rounded(kp, key_offset(sd, i, D), y0);
-    store_rounded(kp, key_offset(sd, i + half, D), y1);
+  // ---- values, phase 1: src chunks of the (at most two) src tiles the run
+  // reads, scattered into LDS
+  const int64_t st_lo = ss0 >> 5, st_hi = (ss0 + n - 1) >> 5;
+  const int cpt = 32 * D / kChunk;  // chunks per tile
+  for (int x = tid; x < static_cast<int>(st_hi - st_lo + 1) * cpt; x += 256) {
+    const int64_t st = st_lo + x / cpt;
+    const int off = (x % cpt) * kChunk;  // element offset inside the tile
+    const int g = off / (8 * D), d = (off % (8 * D)) / 8, r0 = off % 8;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(vp + st * 32 * D + off);
+    const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int r8 = r0 + i;
+      const int64_t slot = st * 32 + (r8 >> 2) * 16 + 4 * g + (r8 & 3);
+      const int64_t j = slot - ss0;
+      if (j >= 0 && j < n) vstage[j * D + d] = e[i];
+    }
   }
-  for (int x = tid; x < n * D; x += 256) {
-    const int64_t sd = s_begin + x / D;
-    const int d = x % D;
-    const int64_t ss = a.start_src + (sd - first);
-    vp[value_offset(sd, d, D)] = vp[value_offset(ss, d, D)];
+  __syncthreads();
+  // ---- keys: chunk pairs (token, dims c*kChunk.. and + D/2)
+  const int cph = half / kChunk;  // chunks per half
+  for (int x = tid; x < n * cph; x += 256) {
+    const int j = x / cph;
+    const int d0 = (x % cph) * kChunk;
+    const u32x4 r0 = *reinterpret_cast<const u32x4*>(kp + key_offset(ss0 + j, d0, D));
+    const u32x4 r1 = *reinterpret_cast<const u32x4*>(kp + key_offset(ss0 + j, d0 + half, D));
+    const T* e0 = reinterpret_cast<const T*>(&r0);
+    const T* e1 = reinterpret_cast<const T*>(&r1);
+    u32x4 w0, w1;
+    T* o0 = reinterpret_cast<T*>(&w0);
+    T* o1 = reinterpret_cast<T*>(&w1);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const double x0 = to_f64(e0[i]), x1 = to_f64(e1[i]);
+      const double c = cs[2 * (d0 + i)], s = cs[2 * (d0 + i) + 1];
+      o0[i] = round_to<T>(x0 * c - x1 * s);
+      o1[i] = round_to<T>(x1 * c + x0 * s);
+    }
+    *reinterpret_cast<u32x4*>(kp + key_offset(s_begin + j, d0, D)) = w0;
+    *reinterpret_cast<u32x4*>(kp + key_offset(s_begin + j, d0 + half, D)) = w1;
+  }
+  // ---- values, phase 2: every chunk of the dst tile holding a run token
+  const int tb = static_cast<int>(s_begin - t0), te = static_cast<int>(s_end - t0);
+  for (int x = tid; x < cpt; x += 256) {
+    const int off = x * kChunk;
+    const int g = off / (8 * D), d = (off % (8 * D)) / 8, r0 = off % 8;
+    int tmin = 64, tmax = -1;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int r8 = r0 + i;
+      const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
+      if (t >= tb && t < te) {
+        tmin = min(tmin, t);
+        tmax = max(tmax, t);
+      }
+    }
+    if (tmax < 0) continue;  // no run token in this chunk
+    T* dst = vp + t0 * D + off;
+    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    bool whole = true;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int r8 = r0 + i;
+      const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
+      whole = whole && t >= tb && t < te;
+    }
+    if (!whole) raw = *reinterpret_cast<const u32x4*>(dst);  // keep tokens outside the run
+    T* e = reinterpret_cast<T*>(&raw);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int r8 = r0 + i;
+      const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
+      if (t >= tb && t < te) e[i] = vstage[(t - tb) * D + d];
+    }
+    *reinterpret_cast<u32x4*>(dst) = raw;
   }
 }
 
@@ -196,7 +268,12 @@ hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double t
   for (int i = 0; i < pool.head_dim / 2; ++i)
     a.inv_freq[i] = pow(theta, -2.0 * i / static_cast<double>(pool.head_dim));
   const int64_t planes = static_cast<int64_t>(pool.num_layers) * pool.num_kv_heads;
-  const int64_t grid = planes * a.tiles_per_plane;
+  a.planes = planes;
+  int64_t grid = planes * a.tiles_per_plane;
+  if (grid >= 8) {
+    grid = (grid + 7) / 8 * 8;  // whole rounds of the 8 XCDs; the excess exits at once
+    a.xcd_map = 1;
+  }
   if (a.cap_src > 0 && grid > 0) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (pool.dtype == HW_F32)
