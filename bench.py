@@ -77,7 +77,145 @@ def parse():
     ap.add_argument("--kernel-timing-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--config", choices=["step", "sweep", "loop"], default="step",
+                    help="step: the headline 64-layer step (default); sweep: context x workers "
+                         "grid, per-layer time on both paths; loop: 36-layer generation loop "
+                         "with appends")
+    ap.add_argument("--loop-steps", type=int, default=2048)
     return ap.parse_args()
+
+
+def _graph_layers_us(hw, torch, pool, wl, q, reps=20):
+    """Per-layer time of one decode call over every layer of `pool`, in graph replay."""
+    W, L = wl.W, pool.num_layers
+    out = torch.zeros(L, W, wl.Hq, wl.D, device="cuda")
+    tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(W, dtype=torch.int32, device="cuda")
+    hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne)
+    ws = hw.alloc_workspace(pool, W, wl.Hq)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for layer in range(L):
+            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+        st.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for layer in range(L):
+                hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+        g.replay()
+        st.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        st.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * L)
+
+
+def run_sweep(args):
+    """Context x workers grid (40 q / 8 kv heads, D 128, bf16): per-layer time of
+    one decode call.  The K/V bytes do not depend on W, so with the reads shared
+    by all workers the time stays flat in W.  Each point cycles through enough
+    layers (distinct K/V) that the 256 MB Infinity Cache cannot hold them."""
+    import torch
+
+    from decode_attention_shared_hw_amd import hogwild_attn as hw
+    from decode_attention_shared_hw_amd import workloads
+
+    points = []
+    for path_name, path in (("mfma", hw.PATH_MFMA), ("valu", hw.PATH_VALU)):
+        hw.hw_set_tuning(path, args.units)
+        for C in (1024, 8192, 16384):
+            for W in (1, 2, 4):
+                wl = workloads.sweep(C, W)
+                L = min(256, max(8, -(-2 * 256 * 2**20 // wl.kv_bytes_per_layer())))
+                wl.layers = L
+                pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
+                pool.set_lengths(wl.lens)
+                for layer in range(L):
+                    K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+                    pool.store_layer(layer, K, V)
+                    del K, V
+                q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
+                us = _graph_layers_us(hw, torch, pool, wl, q)
+                b = wl.algorithmic_bytes_per_layer()
+                points.append({"path": path_name, "context": C, "workers": W, "layers_cycled": L,
+                               "us_per_layer": us, "worker_tokens_per_s_per_layer": W / (us * 1e-6),
+                               "algorithmic_bytes": b, "achieved_gbs": b / (us * 1e-6) / 1e9,
+                               "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                               "status": hw.hw_pool_status(pool)})
+                print(f"# {path_name} C={C} W={W}: {us:.2f} us/layer", file=sys.stderr, flush=True)
+                del pool, q
+                torch.cuda.empty_cache()
+    hw.hw_set_tuning(hw.PATH_AUTO, 0)
+    print(json.dumps({"config": "sweep", "unit": "us per layer (graph replay)",
+                      "data": "synthetic, seeded", "points": points}), flush=True)
+
+
+def run_loop(args):
+    """Generation loop (Qwen3-8B heads: 36 layers, 32 q / 8 kv heads, D 128, bf16,
+    4 workers, common cache from 32768 tokens).  Each step the private blocks
+    grow by one token (a length bump over pre-filled random capacity: the K/V
+    written by the model for the new token is not part of this path), the
+    tables are rebuilt on the device and all 36 layers decode; every 64 steps
+    one worker's block is appended into the common block and reset (shuffled
+    round robin).  Eager launches, timed end to end with HIP events."""
+    import numpy as np
+    import torch
+
+    from decode_attention_shared_hw_amd import hogwild_attn as hw
+    from decode_attention_shared_hw_amd import workloads
+
+    steps = args.loop_steps
+    wl = workloads.qwen3_loop(steps=steps)
+    sched = workloads.loop_appends(wl, steps)
+    L, W = wl.layers, wl.W
+    pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
+    pool.set_lengths(wl.lens)
+    for layer in range(L):
+        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+        pool.store_layer(layer, K, V)
+        del K, V
+    q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
+    out = torch.zeros(L, W, wl.Hq, wl.D, device="cuda")
+    tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(W, dtype=torch.int32, device="cuda")
+    ws = hw.alloc_workspace(pool, W, wl.Hq)
+    st = torch.cuda.Stream()
+    lens = np.array(wl.lens, np.int64)
+    dec_bytes = 0
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for step in range(steps):
+            pool.block_len[1:] += 1  # harness: the new token of every worker
+            lens[1:] += 1
+            hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
+            for layer in range(L):
+                hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+            dec_bytes += L * (int(lens.sum()) * wl.Hkv * wl.D * 2 * 2 + W * wl.Hq * wl.D * 6)
+            if step in sched:
+                b = wl.worker_block[sched[step]]
+                hw.hw_block_append(pool, b, wl.common_block, wl.theta, st)
+                hw.hw_block_reset(pool, b, st)
+                lens[0] += lens[b]
+                lens[b] = 0
+        e1.record(st)
+        st.synchronize()
+    ms = e0.elapsed_time(e1)
+    step_us = ms * 1e3 / steps
+    res = {"config": "loop", "workload": wl.name, "steps": steps, "layers": L, "workers": W,
+           "appends": len(sched), "common_tokens": [int(wl.lens[0]), int(lens[0])],
+           "us_per_step": step_us, "us_per_layer": step_us / L,
+           "worker_tokens_per_s_per_layer": W * L / (step_us * 1e-6),
+           "decode_achieved_gbs": dec_bytes / (ms * 1e-3) / 1e9,
+           "status": hw.hw_pool_status(pool),
+           "final_lengths": pool.block_len.cpu().tolist(), "expected_lengths": lens.tolist()}
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(wl, pool_block_start, K, V, q, pairs):
@@ -129,6 +267,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     hw.lib()  # fail loudly if the library is missing
+    if args.config == "sweep":
+        return run_sweep(args)
+    if args.config == "loop":
+        return run_loop(args)
     path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
     hw.hw_set_tuning(path, args.units)
 
@@ -253,7 +395,8 @@ def main():
                    if use_graph else "tables + 64 x decode + 1 block append (eager)"},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic() if path != hw.PATH_VALU else None,
             "kernel": ("decode call = split kernel decode_mfma<128,2> + merge_kernel"
                        if path != hw.PATH_VALU else "decode call = decode_valu<bf16> + merge_kernel"),
             "bytes_per_launch": bytes_per_launch,

@@ -112,6 +112,26 @@ def qwen3_loop(seed: int = 1005, layers: int = 36, common0: int = 32768, steps: 
                     [common_cap] + [private_cap] * 4, 0.5, seed)
 
 
+def loop_appends(wl: Workload, steps: int, every: int = 64) -> dict:
+    """Generation-loop schedule: {step: worker} for the steps after which one
+    worker's block is appended into the common block and reset.
+
+    Every `every` steps exactly one worker is picked, by a shuffled round
+    robin: a fresh seeded permutation of the W workers for every W * every
+    steps, so the gap between two appends of one worker is 1 to 2W - 1
+    windows and a private block never holds more than (2W - 1) * every plus
+    its initial length of tokens.
+    """
+    rng = np.random.default_rng(wl.seed + 7)
+    out = {}
+    order = []
+    for k, s in enumerate(range(every - 1, steps, every)):
+        if not order:
+            order = [int(x) for x in rng.permutation(wl.W)]
+        out[s] = order.pop(0)
+    return out
+
+
 def _gen(seed: int, layer: int, tag: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed((seed * 1_000_003 + layer * 97 + tag) & 0x7FFF_FFFF_FFFF_FFFF)
@@ -160,5 +180,5 @@ def summary(wl: Workload) -> dict:
     }
 
 
-__all__ = ["Workload", "tiny", "qwq_layer", "qwq_step", "sweep", "qwen3_loop", "make_q", "make_kv",
-           "summary", "round_up"]
+__all__ = ["Workload", "tiny", "qwq_layer", "qwq_step", "sweep", "qwen3_loop", "loop_appends",
+           "make_q", "make_kv", "summary", "round_up"]

@@ -342,3 +342,58 @@ def test_qwq_step_full_size_sampled():
             ma, rl = errors(got[w, h], ref)
             assert ma <= 5e-3 and rl <= 1e-2, (layer, w, h, ma, rl)
     assert hw.hw_pool_status(pool) == 0
+
+
+# ------------------------------------------------- generation loop (config 5)
+def test_generation_loop_matches_oracle():
+    """A shortened config-5 loop (Qwen3-8B heads, 4 workers): every step the
+    private blocks grow by one token (length bump over pre-filled capacity),
+    the tables are rebuilt on the device and every layer decodes; every 64
+    steps one worker's block is appended into the common block and reset.
+    The oracle replays the same appends on its own fp64 copy of the pool;
+    attention is checked at several steps and the whole pool bit-exactly at
+    the end."""
+    steps, L = 256, 2
+    wl = workloads.qwen3_loop(layers=L, common0=2048, steps=steps)
+    sched = workloads.loop_appends(wl, steps)
+    s = Setup(wl, n_layers=L)
+    Kh = np.stack([k.double().numpy() for k in s.K])
+    Vh = np.stack([v.double().numpy() for v in s.V])
+    lens = np.array(wl.lens, np.int32)
+    starts = np.asarray(s.pool.block_start, np.int64)
+    out = torch.zeros(L, wl.W, wl.Hq, wl.D, device="cuda")
+    checks = {0, 63, 64, 130, 255}
+    worst = 0.0
+    for step in range(steps):
+        lens[1:] += 1
+        s.pool.block_len[1:] += 1
+        hw.hw_build_combined_tables(s.pool, wl.W, wl.common_block, wl.worker_block, s.tables,
+                                    s.num_entries)
+        for layer in range(L):
+            hw.hw_attn_decode(s.pool, layer, s.q[layer].cuda(), s.tables, s.num_entries, wl.theta,
+                              out[layer], s.ws)
+        if step in checks:
+            got = out.cpu().numpy()
+            tb, to, ne = oracle.build_combined_tables(wl.common_block, wl.worker_block, lens)
+            for layer in range(L):
+                ref, rc = oracle.attn_decode(oracle.FORM_METHOD, s.q[layer].double().numpy(),
+                                             Kh[layer], Vh[layer], tb, to, ne, lens, starts,
+                                             wl.theta)
+                assert rc == 0
+                ma, _ = assert_close(got[layer], ref, torch.bfloat16, f"loop step {step} layer {layer}")
+                worst = max(worst, ma)
+        if step in sched:
+            b = wl.worker_block[sched[step]]
+            hw.hw_block_append(s.pool, b, wl.common_block, wl.theta)
+            hw.hw_block_reset(s.pool, b)
+            rc = oracle.block_append(Kh, Vh, starts, s.pool.block_cap, lens, b, wl.common_block,
+                                     wl.theta, oracle.HWO_BF16)
+            assert rc == 0
+    torch.cuda.synchronize()
+    assert s.pool.block_len.cpu().tolist() == lens.tolist()
+    assert hw.hw_pool_status(s.pool) == 0
+    for layer in range(L):
+        Kg, Vg = s.pool.load_layer(layer)
+        assert np.array_equal(Kg.cpu().double().numpy(), Kh[layer])
+        assert np.array_equal(Vg.cpu().double().numpy(), Vh[layer])
+    _say(f"  loop: {len(sched)} appends, common {lens[0]} tokens, worst max_abs {worst:.2e}")
