@@ -239,120 +239,6 @@ __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan
   return static_cast<int64_t>(p.head) * a.P + p.unit;
 }
 
-// ------------------------------------------------------------- VALU kernel
-// Generic path: any dtype, rows <= HW_MAX_ROWS, D in {64, 128}.  Tiles are
-// staged in LDS in logical [token][dim] order; scores, softmax and P.V run
-// in fp32 on the vector ALUs.
-constexpr int kValuMaxAcc = HW_MAX_ROWS * 128 / kThreads;  // 32
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
-  __shared__ Plan plan;
-  __shared__ float qr[HW_MAX_ROWS * 128];
-  __shared__ float ks[kTile * 129];
-  __shared__ float vs[kTile * 128];
-  __shared__ float ps[HW_MAX_ROWS * (kTile + 1)];
-  __shared__ float m_s[HW_MAX_ROWS], l_s[HW_MAX_ROWS], al_s[HW_MAX_ROWS];
-  build_plan<kThreads>(a, plan, [] {}, [] {});
-  const int tid = threadIdx.x;
-  const int g = plan.head;
-  const int D = a.D, R = a.R, half = D / 2;
-  const T* qg = static_cast<const T*>(a.q);
-  const T* kp = static_cast<const T*>(a.k) + g * a.plane_elems;
-  const T* vp = static_cast<const T*>(a.v) + g * a.plane_elems;
-  for (int r = tid; r < R; r += kThreads) {
-    m_s[r] = -INFINITY;
-    l_s[r] = 0.f;
-  }
-  float acc[kValuMaxAcc];
-#pragma unroll
-  for (int k = 0; k < kValuMaxAcc; ++k) acc[k] = 0.f;
-  int b = 0, cur_b = -1;
-  for (int j = plan.lo; j < plan.hi; ++j) {
-    b = block_of_tile(plan, a.NB, j, b);
-    if (b != cur_b) {
-      __syncthreads();
-      // rotate every row of head g for this block: q~ = rho(q, i_q - off)
-      for (int x = tid; x < R * half; x += kThreads) {
-        const int r = x / half, i = x - r * half;
-        const int w = r / a.G, h = g * a.G + (r - w * a.G);
-        const bool vis = (plan.vis[b] >> w) & 1u;
-        float c = 0.f, s = 0.f;
-        if (vis) rope_cos_sin(plan.iq[w] - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
-        const int64_t qo = (static_cast<int64_t>(w) * a.Hq + h) * D;
-        const float x0 = load_elem(qg, qo + i), x1 = load_elem(qg, qo + i + half);
-        qr[r * D + i] = vis ? (x0 * c - x1 * s) * a.qscale : 0.f;
-        qr[r * D + i + half] = vis ? (x1 * c + x0 * s) * a.qscale : 0.f;
-      }
-      cur_b = b;
-    }
-    const int tl = j - plan.tile0[b];
-    const int valid = min(kTile, plan.len[b] - tl * kTile);
-    const int64_t base = (plan.start[b] + static_cast<int64_t>(tl) * kTile) * D;
-    __syncthreads();
-    for (int x = tid; x < kTile * D; x += kThreads) {
-      // key tile element x of the pool layout -> (token, dim)
-      const int hk = x / (16 * D), rk = x - hk * 16 * D;
-      const int tk = hk * 16 + ((rk & 127) >> 3), dk = (rk >> 7) * 8 + (rk & 7);
-      ks[tk * 129 + dk] = load_elem(kp, base + x);
-      // value tile element x -> (token, dim)
-      const int gv = x / (8 * D), rv = x - gv * 8 * D;
-      const int sv = rv & 7, dv = rv >> 3;
-      const int tv = (sv >> 2) * 16 + gv * 4 + (sv & 3);
-      vs[tv * D + dv] = tv < valid ? load_elem(vp, base + x) : 0.f;
-    }
-    __syncthreads();
-    for (int x = tid; x < R * kTile; x += kThreads) {
-      const int r = x / kTile, t = x - r * kTile;
-      const int w = r / a.G;
-      float s = -INFINITY;
-      if (t < valid && ((plan.vis[b] >> w) & 1u)) {
-        s = 0.f;
-        for (int d = 0; d < D; ++d) s += qr[r * D + d] * ks[t * 129 + d];
-      }
-      ps[r * (kTile + 1) + t] = s;
-    }
-    __syncthreads();
-    for (int r = tid; r < R; r += kThreads) {
-      float mt = -INFINITY;
-      for (int t = 0; t < kTile; ++t) mt = fmaxf(mt, ps[r * (kTile + 1) + t]);
-      const float mn = fmaxf(m_s[r], mt);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float al = __builtin_amdgcn_exp2f(m_s[r] - mu);
-      float sum = 0.f;
-      for (int t = 0; t < kTile; ++t) {
-        const float pv = __builtin_amdgcn_exp2f(ps[r * (kTile + 1) + t] - mu);
-        ps[r * (kTile + 1) + t] = pv;
-        sum += pv;
-      }
-      l_s[r] = l_s[r] * al + sum;
-      m_s[r] = mn;
-      al_s[r] = al;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kValuMaxAcc; ++k) {
-      const int idx = tid + k * kThreads;
-      if (idx < R * D) {
-        const int r = idx / D, d = idx - r * D;
-        float s = acc[k] * al_s[r];
-#pragma unroll 4
-        for (int t = 0; t < kTile; ++t) s += ps[r * (kTile + 1) + t] * vs[t * D + d];
-        acc[k] = s;
-      }
-    }
-  }
-  __syncthreads();
-  const int64_t pu = partial_index(a, plan);
-  for (int r = tid; r < R; r += kThreads) a.ws_ml[pu * R + r] = make_float2(m_s[r], l_s[r]);
-#pragma unroll
-  for (int k = 0; k < kValuMaxAcc; ++k) {
-    const int idx = tid + k * kThreads;
-    if (idx < R * D) a.ws_acc[pu * R * D + idx] = acc[k];
-  }
-  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
-}
-
 // ------------------------------------------------------------- MFMA kernel
 // bf16 pools, rows R = W*G <= 16*NT.  Each wave owns every 4th tile of the
 // workgroup's range and keeps its own (m, l, O^T) for all rows; the four
@@ -807,6 +693,381 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
 }
 
+// ------------------------------------------------------------- VALU kernel
+// Any pool dtype (fp32 or bf16), rows R = W*G <= 2*RG, fp32 arithmetic on
+// the vector ALUs.  Four waves per workgroup; each wave owns every 4th tile
+// of the unit's range and keeps a private (m, l, O) for all rows; the waves
+// are combined in LDS at the end like the MFMA kernel's.
+//
+// Scores: lane (token t = lane % 32, row group rg = lane / 32) loads token
+// t's key straight into registers and forms the dot products of rows
+// rg*RG .. rg*RG+RG-1 against the rotated queries, read from LDS (fp32,
+// broadcast to the 32 lanes of a row group).  Row max and sum over the tile
+// are DPP reductions inside each 32-lane half.  P.V: lane l owns output dims
+// DPL*l .. DPL*l+DPL-1 of every row and reads P and the rescale factors back
+// from a per-wave LDS buffer.
+template <typename T>
+struct ValuTraits;
+template <>
+struct ValuTraits<float> {
+  static constexpr int EPC = 4;  // elements per 16-byte chunk
+  __device__ static float elem(const u32x4& c, int e) { return __uint_as_float(c[e]); }
+};
+template <>
+struct ValuTraits<uint16_t> {
+  static constexpr int EPC = 8;
+  __device__ static float elem(const u32x4& c, int e) {
+    const uint32_t w = c[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+
+// max / sum over the 32 lanes of each half of the wave (every lane gets it)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_mov<0xb1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4e>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+  return fmaxf(x, __shfl_xor(x, 16));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_mov<0xb1>(x);
+  x += dpp_mov<0x4e>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return x + __shfl_xor(x, 16);
+}
+
+template <typename T, int D, int RG>
+__global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
+  constexpr int NTHR = kThreads, NWAVE = kWaves;
+  constexpr int EPC = ValuTraits<T>::EPC;
+  constexpr int KC = D / EPC;     // key chunks per token
+  constexpr int DPL = D / 64;     // output dims per lane
+  constexpr int RM = 2 * RG;      // rows held
+  constexpr int PS = 36;          // P row stride (floats), keeps float4 reads aligned
+  constexpr int kPWave = RM * PS + RM;  // one wave's P and rescale factors
+  constexpr int ACC_STRIDE = D + 4;
+  constexpr int kState = RM * ACC_STRIDE + 2 * RM;
+  constexpr int kQBlock = RM * D;      // rotated queries of one block (floats)
+  constexpr int kQfFloats = 40960 / 4;  // 40 KB of rotated queries per group
+  constexpr int kQfBlocks = kQfFloats / kQBlock > 0 ? kQfFloats / kQBlock : 1;
+  constexpr int kUnion = cmax(kQfBlocks * kQBlock, 2 * kState);
+  __shared__ Plan plan;
+  __shared__ __attribute__((aligned(16))) float qs[RM * D];  // raw query rows
+  // rotated queries during the loop; the waves' softmax states at the end
+  __shared__ __attribute__((aligned(16))) float ubuf[kUnion];
+  __shared__ __attribute__((aligned(16))) float pbuf_all[NWAVE * kPWave];  // P, rescale factors
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int tl = lane & 31, rg = lane >> 5;
+  {
+    int h0, u0;
+    plan_head_unit(a, &h0, &u0);
+    constexpr int kQVec = RM * D / 4;  // float4 of staged query
+    constexpr int kQRegs = (kQVec + NTHR - 1) / NTHR;
+    float4 qv[kQRegs];
+    const T* qg = static_cast<const T*>(a.q);
+    auto issue = [&] {
+#pragma unroll
+      for (int k = 0; k < kQRegs; ++k) {
+        const int x = tid + k * NTHR;
+        const int r = (4 * x) / D, d = 4 * x - r * D;
+        qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (x < kQVec && r < a.R) {
+          const int w = r / a.G, h = h0 * a.G + (r - w * a.G);
+          const T* src = qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d;
+          qv[k] = make_float4(load_elem(src, 0), load_elem(src, 1), load_elem(src, 2),
+                              load_elem(src, 3));
+        }
+      }
+    };
+    auto commit = [&] {
+#pragma unroll
+      for (int k = 0; k < kQRegs; ++k) {
+        const int x = tid + k * NTHR;
+        if (x < kQVec) *reinterpret_cast<float4*>(qs + 4 * x) = qv[k];
+      }
+    };
+    build_plan<NTHR>(a, plan, issue, commit);
+  }
+  const int g = plan.head;
+  const __amdgpu_buffer_rsrc_t krs =
+      plane_rsrc(static_cast<const T*>(a.k) + static_cast<int64_t>(g) * a.plane_elems, a.plane_bytes);
+  const __amdgpu_buffer_rsrc_t vrs =
+      plane_rsrc(static_cast<const T*>(a.v) + static_cast<int64_t>(g) * a.plane_elems, a.plane_bytes);
+  float* pbuf = pbuf_all + wave * kPWave;
+
+  float acc[RM][DPL];
+  float m_run[RG], l_run[RG];
+#pragma unroll
+  for (int i = 0; i < RG; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) acc[r][dd] = 0.f;
+
+  // (a2) rotated, scaled queries of blocks gb..ge-1: qr[(b-gb)*RM*D + r*D + d]
+  auto rotate_blocks = [&](int gb, int ge) {
+    const int half = D / 2;
+    const int items = (ge - gb) * RM * half;
+    for (int x = tid; x < items; x += NTHR) {
+      const int i = x % half;
+      const int r = (x / half) % RM;
+      const int bi = x / (half * RM);
+      const int b = gb + bi;
+      const int w = r / a.G;
+      const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
+      float c = 0.f, s = 0.f;
+      if (vis) rope_cos_sin(plan.iq[w] - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
+      const float x0 = qs[r * D + i], x1 = qs[r * D + i + half];
+      float* dst = ubuf + bi * kQBlock + r * D;
+      dst[i] = vis ? (x0 * c - x1 * s) * a.qscale : 0.f;
+      dst[i + half] = vis ? (x1 * c + x0 * s) * a.qscale : 0.f;
+    }
+  };
+
+  // this lane's key chunks (token tl) and value chunks (dims DPL*lane..)
+  auto load_k = [&](uint32_t tile, u32x4 (&kc)[KC]) {
+    const uint32_t base = ((tl >> 4) * 16 * D + (tl & 15) * 8) * sizeof(T);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      // chunk c covers dims EPC*c..: group (EPC*c)/8, offset (EPC*c)%8
+      const int d0 = EPC * c;
+      kc[c] = __builtin_amdgcn_raw_buffer_load_b128(
+          krs, base + ((d0 >> 3) * 128 + (d0 & 7)) * sizeof(T), tile, 0);
+    }
+  };
+  constexpr int VC = 8 / EPC;  // chunks per (group, dim): 1 (bf16) or 2 (fp32)
+  auto load_v = [&](uint32_t tile, u32x4 (&vc)[DPL][4][VC]) {
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int h = 0; h < VC; ++h) {
+          const int d = DPL * lane + dd;
+          vc[dd][gq][h] = __builtin_amdgcn_raw_buffer_load_b128(
+              vrs, (gq * 8 * D + d * 8 + h * EPC) * sizeof(T), tile, 0);
+        }
+  };
+
+  auto compute = [&](const u32x4 (&kc)[KC], const u32x4 (&vc)[DPL][4][VC], const float* qblk,
+                     uint32_t vismask, int valid) {
+    // ---- scores of rows rg*RG+i against token tl, into the P buffer (the
+    // row loop stays rolled so the queries are read from LDS as they are used)
+    float kv[D];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) kv[EPC * c + e] = ValuTraits<T>::elem(kc[c], e);
+#pragma unroll 1
+    for (int i = 0; i < RG; ++i) {
+      const int r = rg * RG + i;
+      const float* qr = qblk + r * D;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; d += 8) {
+        const float4 qa = *reinterpret_cast<const float4*>(qr + d);
+        const float4 qb = *reinterpret_cast<const float4*>(qr + d + 4);
+        s0 += qa.x * kv[d] + qa.y * kv[d + 1] + qa.z * kv[d + 2] + qa.w * kv[d + 3];
+        s1 += qb.x * kv[d + 4] + qb.y * kv[d + 5] + qb.z * kv[d + 6] + qb.w * kv[d + 7];
+      }
+      pbuf[r * PS + tl] = s0 + s1;
+    }
+    // ---- online softmax per row (exp2 domain), P and rescale factors to LDS
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int r = rg * RG + i;
+      const bool ok = tl < valid && r < a.R && ((vismask >> (r / a.G)) & 1u);
+      const float sv = ok ? pbuf[r * PS + tl] : -INFINITY;
+      const float mt = half_max(sv);
+      const float mn = fmaxf(m_run[i], mt);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float al = __builtin_amdgcn_exp2f(m_run[i] - mu);
+      const float p = __builtin_amdgcn_exp2f(sv - mu);
+      l_run[i] = l_run[i] * al + half_sum(p);
+      m_run[i] = mn;
+      pbuf[r * PS + tl] = p;
+      if (tl == 0) pbuf[RM * PS + r] = al;
+    }
+    // ---- P.V for every row on this lane's dims (tokens past `valid` are
+    // dropped from V: they may hold anything, even NaN)
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r >= a.R) continue;  // (uniform; keeps the trip count constant)
+      const float al = pbuf[RM * PS + r];
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) acc[r][dd] *= al;
+    }
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // chunk elements 4*hh..4*hh+3 of group gq hold tokens 16*hh + 4*gq + v
+        float vv[4][DPL];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int e = 4 * hh + v;
+          const int t = 16 * hh + 4 * gq + v;
+#pragma unroll
+          for (int dd = 0; dd < DPL; ++dd) {
+            const float x = ValuTraits<T>::elem(vc[dd][gq][e / EPC], e % EPC);
+            vv[v][dd] = t < valid ? x : 0.f;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+          if (r >= a.R) continue;  // (uniform; keeps the trip count constant)
+          const float4 p4 = *reinterpret_cast<const float4*>(pbuf + r * PS + 16 * hh + 4 * gq);
+#pragma unroll
+          for (int dd = 0; dd < DPL; ++dd)
+            acc[r][dd] += p4.x * vv[0][dd] + p4.y * vv[1][dd] + p4.z * vv[2][dd] + p4.w * vv[3][dd];
+        }
+      }
+    }
+  };
+
+  if (plan.lo < plan.hi) {
+    const int bq = kQfBlocks;
+    const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
+    const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
+    for (int gb = b_first; gb <= b_last; gb += bq) {
+      const int ge = min(gb + bq, b_last + 1);
+      const int t_lo = max(plan.lo, plan.tile0[gb]);
+      const int t_hi = min(plan.hi, plan.tile0[ge]);
+      int j = t_lo + wave;
+      int bcur = gb;
+      TileRef rt = {0, 0, 0};
+      u32x4 kc[KC], vc[DPL][4][VC];
+      if (j < t_hi) {
+        rt = tile_ref<D>(plan, a.NB, j, bcur);
+        const uint32_t tile =
+            __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * sizeof(T)));
+        load_k(tile, kc);
+        load_v(tile, vc);
+      }
+      if (gb != b_first) __syncthreads();  // the previous group's queries are consumed
+      rotate_blocks(gb, ge);
+      __syncthreads();
+      if (j < t_hi) {
+        for (;;) {
+          const float* qblk = ubuf + (rt.b - gb) * kQBlock;
+          const uint32_t vismask = plan.vis[rt.b];
+          const int jn = j + NWAVE;
+          if (jn >= t_hi) {
+            compute(kc, vc, qblk, vismask, rt.valid);
+            break;
+          }
+          const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
+          const uint32_t tn =
+              __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * sizeof(T)));
+          compute(kc, vc, qblk, vismask, rt.valid);
+          load_k(tn, kc);
+          load_v(tn, vc);
+          j = jn;
+          rt = rn;
+        }
+      }
+    }
+  }
+
+  // ---- combine the waves' states (two at a time) and store the partial
+  // state of row r: acc on every lane (dims), (m, l) on the row group's lanes
+  auto deposit = [&](float* buf) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r >= a.R) continue;  // (uniform; keeps the trip count constant)
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) buf[r * ACC_STRIDE + DPL * lane + dd] = acc[r][dd];
+    }
+    if (tl == 0) {
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+        const int r = rg * RG + i;
+        if (r < a.R) {
+          buf[RM * ACC_STRIDE + r] = m_run[i];
+          buf[RM * ACC_STRIDE + RM + r] = l_run[i];
+        }
+      }
+    }
+  };
+  __syncthreads();  // every wave is done with the queries and its P buffer
+  if (wave >= 2) deposit(ubuf + (wave - 2) * kState);
+  __syncthreads();
+  if (wave < 2) {
+    // fold in the partner wave's state: m, l of every row from LDS, acc by dims
+    const float* src = ubuf + wave * kState;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r >= a.R) continue;  // (uniform; keeps the trip count constant)
+      // own (m, l) of row r: held by the lanes of row group r / RG
+      float mo = -INFINITY, lo = 0.f;
+#pragma unroll
+      for (int k = 0; k < RG; ++k)
+        if (k == r % RG) {
+          mo = m_run[k];
+          lo = l_run[k];
+        }
+      // lanes of the other half hold another row: take row r's from lane (r/RG)*32
+      mo = __shfl(mo, (r / RG) * 32);
+      lo = __shfl(lo, (r / RG) * 32);
+      const float m2 = src[RM * ACC_STRIDE + r];
+      const float l2 = src[RM * ACC_STRIDE + RM + r];
+      const float M = fmaxf(mo, m2);
+      const float s1 = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - M);
+      const float s2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd)
+        acc[r][dd] = acc[r][dd] * s1 + src[r * ACC_STRIDE + DPL * lane + dd] * s2;
+      // the merged (m, l) go back to the row group's registers
+      const float lm = lo * s1 + l2 * s2;
+#pragma unroll
+      for (int k = 0; k < RG; ++k)
+        if (k == r % RG && rg == r / RG) {
+          m_run[k] = M;
+          l_run[k] = lm;
+        }
+    }
+  }
+  __syncthreads();
+  if (wave < 2) deposit(ubuf + wave * kState);
+  __syncthreads();
+  const int64_t pu = partial_index(a, plan);
+  for (int x = tid; x < a.R * (D / 4); x += NTHR) {
+    const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
+    const float m0 = ubuf[RM * ACC_STRIDE + r], m1 = ubuf[kState + RM * ACC_STRIDE + r];
+    const float M = fmaxf(m0, m1);
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 2; ++wv) {
+        const float* src = ubuf + wv * kState;
+        const float mw = wv ? m1 : m0;
+        const float sc = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        L += src[RM * ACC_STRIDE + RM + r] * sc;
+        const float4 v = *reinterpret_cast<const float4*>(src + r * ACC_STRIDE + d4);
+        O.x += v.x * sc;
+        O.y += v.y * sc;
+        O.z += v.z * sc;
+        O.w += v.w * sc;
+      }
+    }
+    *reinterpret_cast<float4*>(a.ws_acc + (pu * a.R + r) * D + d4) = O;
+    if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
+  }
+  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
+}
+
 // ----------------------------------------------------------- merge kernel
 // (a4) One workgroup per (kv head g, row r), one thread per output dim:
 // out = sum_u acc_u 2^(m_u - M) / L with M = max_u m_u and
@@ -870,13 +1131,27 @@ int occupancy(K kernel, int threads) {
 
 }  // namespace
 
+template <typename T, int D>
+hipError_t launch_valu_rows(const DecodeArgs& a, int grid, hipStream_t s) {
+  if (a.R <= 8)
+    hipLaunchKernelGGL((decode_valu<T, D, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.R <= 16)
+    hipLaunchKernelGGL((decode_valu<T, D, 8>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.R <= 20)
+    hipLaunchKernelGGL((decode_valu<T, D, 10>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (a.R <= 32)
+    hipLaunchKernelGGL((decode_valu<T, D, 16>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_valu<T, D, 32>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_valu(const DecodeArgs& a, int grid, hipStream_t s) {
   if ((a.D != 64 && a.D != 128) || a.R > HW_MAX_ROWS) return hipErrorInvalidValue;
   if (a.dtype == HW_F32)
-    hipLaunchKernelGGL(decode_valu<float>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_valu<uint16_t>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+    return a.D == 128 ? launch_valu_rows<float, 128>(a, grid, s) : launch_valu_rows<float, 64>(a, grid, s);
+  return a.D == 128 ? launch_valu_rows<uint16_t, 128>(a, grid, s)
+                    : launch_valu_rows<uint16_t, 64>(a, grid, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
@@ -911,8 +1186,8 @@ int decode_blocks_per_cu(int path, int dtype, int D, int rows) {
       return rows <= 16 ? occupancy(decode_mfma<128, 1>, t) : occupancy(decode_mfma<128, 2>, t);
     return rows <= 16 ? occupancy(decode_mfma<64, 1>, t) : occupancy(decode_mfma<64, 2>, t);
   }
-  return dtype == HW_F32 ? occupancy(decode_valu<float>, kThreads)
-                         : occupancy(decode_valu<uint16_t>, kThreads);
+  return dtype == HW_F32 ? occupancy(decode_valu<float, 128, 10>, kThreads)
+                         : occupancy(decode_valu<uint16_t, 128, 10>, kThreads);
 }
 
 }  // namespace hw
