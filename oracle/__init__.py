@@ -65,6 +65,8 @@ def lib():
                                       i64, P, P, P, P]
         L.hwo_block_append.restype = i32
         L.hwo_block_append.argtypes = [i32, i32, i32, i64, P, P, i32, P, P, P, i32, i32, d, i32]
+        L.hwo_block_write.restype = i32
+        L.hwo_block_write.argtypes = [i32, i32, i64, P, P, i32, P, P, i32, P, P, P, d, i32]
         _lib = L
     return _lib
 
@@ -159,6 +161,22 @@ def block_append(K, V, block_start, block_cap, block_len, src, dst, theta, dtype
     L, Hkv, S, D = K.shape
     return lib().hwo_block_append(L, Hkv, D, S, _p(K), _p(V), bl_n(block_len), _p(bs), _p(bc),
                                   _p(block_len), int(src), int(dst), float(theta), int(dtype))
+
+
+def block_write(K, V, block_start, block_len, blocks, k_new, v_new, theta, dtype):
+    """In place on float64 arrays K, V [Hkv][num_slots][D] of one layer: the new
+    token of every listed block at its slot block_len[b] - 1 (key design 1).
+    k_new, v_new: [n][Hkv][D].  Returns rc."""
+    assert K.dtype == np.float64 and K.flags.c_contiguous
+    assert V.dtype == np.float64 and V.flags.c_contiguous
+    bs = _c(block_start, np.int64)
+    bl = _c(block_len, np.int32)
+    bk = _c(blocks, np.int32)
+    kn = _c(k_new, np.float64)
+    vn = _c(v_new, np.float64)
+    Hkv, S, D = K.shape
+    return lib().hwo_block_write(Hkv, D, S, _p(K), _p(V), int(bl.shape[0]), _p(bs), _p(bl),
+                                 int(bk.shape[0]), _p(bk), _p(kn), _p(vn), float(theta), int(dtype))
 
 
 def bl_n(block_len) -> int:

@@ -241,4 +241,31 @@ int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, d
   return HWO_OK;
 }
 
+int32_t hwo_block_write(int32_t Hkv, int32_t D, int64_t num_slots, double* K, double* V,
+                        int32_t num_blocks, const int64_t* block_start, const int32_t* block_len,
+                        int32_t n, const int32_t* blocks, const double* k_new,
+                        const double* v_new, double theta, int32_t dtype) {
+  if (dtype != HWO_F32 && dtype != HWO_BF16) return HWO_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    if (blocks[i] < 0 || blocks[i] >= num_blocks) return HWO_EINVAL;
+    if (block_len[blocks[i]] < 1) return HWO_ENOTOKENS;
+  }
+  std::vector<double> enc(D);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    const int64_t pos = block_len[b] - 1;
+    for (int32_t g = 0; g < Hkv; ++g) {
+      const double* kr = k_new + (static_cast<int64_t>(i) * Hkv + g) * D;
+      const double* vr = v_new + (static_cast<int64_t>(i) * Hkv + g) * D;
+      const int64_t s = (static_cast<int64_t>(g) * num_slots + block_start[b] + pos) * D;
+      hwo_rope(kr, D, theta, static_cast<double>(pos), enc.data());
+      for (int32_t d = 0; d < D; ++d) {
+        K[s + d] = dtype == HWO_BF16 ? hwo_round_bf16(enc[d]) : hwo_round_f32(enc[d]);
+        V[s + d] = dtype == HWO_BF16 ? hwo_round_bf16(vr[d]) : hwo_round_f32(vr[d]);
+      }
+    }
+  }
+  return HWO_OK;
+}
+
 }  // extern "C"

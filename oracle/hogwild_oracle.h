@@ -114,6 +114,20 @@ int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, d
                          int32_t num_blocks, const int64_t* block_start, const int32_t* block_cap,
                          int32_t* block_len, int32_t src, int32_t dst, double theta, int32_t dtype);
 
+/*
+ * Token write for one layer (the new token of a decode step, stored at its
+ * local position, Hogwild! notes key design 1).  K, V: [Hkv][num_slots][D].
+ * For each listed block b with p = block_len[b] - 1: key slot p of kv head h
+ * receives k_new[i][h] encoded at position p (rounded to dtype) and value slot
+ * p receives v_new[i][h] (rounded to dtype).  Lengths are not changed.
+ * k_new, v_new: [n][Hkv][D].  Returns HWO_EINVAL for a block id out of range,
+ * HWO_ENOTOKENS when a listed block has length 0 (nothing is written then).
+ */
+int32_t hwo_block_write(int32_t Hkv, int32_t D, int64_t num_slots, double* K, double* V,
+                        int32_t num_blocks, const int64_t* block_start, const int32_t* block_len,
+                        int32_t n, const int32_t* blocks, const double* k_new,
+                        const double* v_new, double theta, int32_t dtype);
+
 #ifdef __cplusplus
 }
 #endif

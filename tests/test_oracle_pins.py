@@ -369,3 +369,78 @@ def test_append_errors():
     K0 = K.copy()
     assert oracle.block_append(K, V, starts, caps, lens, 1, 0, 1e4, 0) == oracle.HWO_ECAPACITY
     assert (K == K0).all() and lens.tolist() == [30, 7, 5]
+
+
+# ------------------------------------------------------- token write (a new token)
+@pytest.mark.parametrize("dtype", [oracle.HWO_F32, oracle.HWO_BF16])
+def test_token_write_encodes_at_local_position(dtype):
+    """The new token's key lands in slot len-1 of its block encoded at that local
+    position (key design 1), correctly rounded; its value rounded; nothing else moves."""
+    rnd = oracle.round_bf16 if dtype == oracle.HWO_BF16 else oracle.round_f32
+    rng = np.random.default_rng(20)
+    Hkv, D, theta = 2, 16, 1e4
+    starts = np.array([0, 64, 96], np.int64)
+    lens = np.array([40, 5, 17], np.int32)
+    S = 128
+    K = np.vectorize(rnd)(rng.standard_normal((Hkv, S, D)))
+    V = np.vectorize(rnd)(rng.standard_normal((Hkv, S, D)))
+    K0, V0 = K.copy(), V.copy()
+    blocks = np.array([2, 1], np.int32)
+    kn = rng.standard_normal((2, Hkv, D))
+    vn = rng.standard_normal((2, Hkv, D))
+    assert oracle.block_write(K, V, starts, lens, blocks, kn, vn, theta, dtype) == oracle.HWO_OK
+    assert lens.tolist() == [40, 5, 17]
+    written = np.zeros(S, bool)
+    half_ulp = 2.0 ** -9 if dtype == oracle.HWO_BF16 else 2.0 ** -24
+    for i, b in enumerate(blocks):
+        slot = starts[b] + lens[b] - 1
+        written[slot] = True
+        exact = rope_complex(kn[i], theta, lens[b] - 1)
+        got = K[:, slot]
+        assert (np.abs(got - exact) <= half_ulp * 2.0 ** np.ceil(np.log2(np.abs(exact)))).all()
+        assert (np.vectorize(rnd)(got) == got).all()
+        if dtype == oracle.HWO_F32:
+            assert (got == exact.astype(np.float32)).all()  # numpy's own rounding to nearest even
+            assert (V[:, slot] == vn[i].astype(np.float32)).all()
+        else:
+            assert (np.abs(V[:, slot] - vn[i]) <= half_ulp * 2.0 ** np.ceil(np.log2(np.abs(vn[i])))).all()
+    assert (K[:, ~written] == K0[:, ~written]).all() and (V[:, ~written] == V0[:, ~written]).all()
+
+
+def test_tokens_written_one_by_one_attend_like_textbook_decode():
+    """Build one block by writing raw keys token by token (advance, then write);
+    attention of one worker with one block at offset 0 is textbook decode over
+    the raw keys with RoPE at absolute positions 0..n-1 and the query at n-1."""
+    rng = np.random.default_rng(21)
+    Hkv, D, theta, n = 1, 8, 1e4, 23
+    starts = np.array([0], np.int64)
+    S = 32
+    K = np.zeros((Hkv, S, D))
+    V = np.zeros((Hkv, S, D))
+    lens = np.array([0], np.int32)
+    raw_k = rng.standard_normal((n, D))
+    raw_v = rng.standard_normal((n, D))
+    for t in range(n):
+        lens[0] += 1  # the slot reserved for token t
+        rc = oracle.block_write(K, V, starts, lens, np.array([0], np.int32), raw_k[t][None, None],
+                                raw_v[t][None, None], theta, oracle.HWO_F32)
+        assert rc == oracle.HWO_OK
+    q = rng.standard_normal(D)
+    tb, to, ne = np.array([[0]], np.int32), np.array([[0]], np.int32), np.array([1], np.int32)
+    got, rc = oracle.attn_one(oracle.FORM_METHOD, q, K[0], V[0], tb[0], to[0], lens, starts, theta)
+    assert rc == 0
+    Kabs = np.stack([rope_complex(raw_k[t], theta, t) for t in range(n)])
+    ref = textbook_decode(rope_complex(q, theta, n - 1), Kabs, V[0, :n])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6)
+
+
+def test_token_write_errors():
+    K = np.zeros((1, 32, 8))
+    V = np.zeros((1, 32, 8))
+    starts = np.array([0], np.int64)
+    one = np.ones((1, 1, 8))
+    assert oracle.block_write(K, V, starts, np.array([3], np.int32), np.array([1], np.int32), one,
+                              one, 1e4, 0) == oracle.HWO_EINVAL
+    assert oracle.block_write(K, V, starts, np.array([0], np.int32), np.array([0], np.int32), one,
+                              one, 1e4, 0) == oracle.HWO_ENOTOKENS
+    assert (K == 0).all() and (V == 0).all()
