@@ -156,12 +156,13 @@ def run_sweep(args):
 
 def run_loop(args):
     """Generation loop (Qwen3-8B heads: 36 layers, 32 q / 8 kv heads, D 128, bf16,
-    4 workers, common cache from 32768 tokens).  Each step the private blocks
-    grow by one token (a length bump over pre-filled random capacity: the K/V
-    written by the model for the new token is not part of this path), the
-    tables are rebuilt on the device and all 36 layers decode; every 64 steps
-    one worker's block is appended into the common block and reset (shuffled
-    round robin).  Eager launches, timed end to end with HIP events."""
+    4 workers, common cache from 32768 tokens), device-resident end to end.
+    One step: every worker's block reserves a slot for the new token
+    (hw_block_advance), the tables are rebuilt on the device, and each layer
+    writes the new tokens' K/V (hw_block_write; synthetic, seeded) and decodes.
+    The step is captured once as a HIP graph and replayed; every 64 steps one
+    worker's block is appended into the common block and reset (shuffled round
+    robin), launched between replays.  Timed end to end with HIP events."""
     import numpy as np
     import torch
 
@@ -179,24 +180,37 @@ def run_loop(args):
         pool.store_layer(layer, K, V)
         del K, V
     q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 11)
+    k_new = torch.randn(L, W, wl.Hkv, wl.D, generator=gen, device="cuda")
+    v_new = torch.randn(L, W, wl.Hkv, wl.D, generator=gen, device="cuda")
     out = torch.zeros(L, W, wl.Hq, wl.D, device="cuda")
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
     ws = hw.alloc_workspace(pool, W, wl.Hq)
     st = torch.cuda.Stream()
+
+    def step_body():
+        hw.hw_block_advance(pool, wl.worker_block, st)
+        hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
+        for layer in range(L):
+            hw.hw_block_write(pool, layer, wl.worker_block, k_new[layer], v_new[layer], wl.theta, st)
+            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+
     lens = np.array(wl.lens, np.int64)
     dec_bytes = 0
     torch.cuda.synchronize()
     with torch.cuda.stream(st):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            step_body()
+        st.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(st)
         for step in range(steps):
-            pool.block_len[1:] += 1  # harness: the new token of every worker
+            graph.replay()
             lens[1:] += 1
-            hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
-            for layer in range(L):
-                hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
             dec_bytes += L * (int(lens.sum()) * wl.Hkv * wl.D * 2 * 2 + W * wl.Hq * wl.D * 6)
             if step in sched:
                 b = wl.worker_block[sched[step]]
@@ -210,6 +224,7 @@ def run_loop(args):
     step_us = ms * 1e3 / steps
     res = {"config": "loop", "workload": wl.name, "steps": steps, "layers": L, "workers": W,
            "appends": len(sched), "common_tokens": [int(wl.lens[0]), int(lens[0])],
+           "step": "advance + tables + 36 x (token write + decode), HIP graph; appends between",
            "us_per_step": step_us, "us_per_layer": step_us / L,
            "worker_tokens_per_s_per_layer": W * L / (step_us * 1e-6),
            "decode_achieved_gbs": dec_bytes / (ms * 1e-3) / 1e9,

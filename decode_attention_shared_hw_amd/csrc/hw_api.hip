@@ -259,6 +259,44 @@ hw_status hw_block_reset(const hw_pool* pool, int32_t block, void* stream) {
              : HW_EHIP;
 }
 
+// Block lists of the token write: 1..HW_MAX_WORKERS distinct valid ids.
+static hw_status check_block_list(const hw_pool* pool, int32_t n, const int32_t* blocks) {
+  if (!blocks) return HW_EINVAL;
+  if (n < 1 || n > HW_MAX_WORKERS) return HW_ERANGE;
+  for (int i = 0; i < n; ++i) {
+    if (blocks[i] < 0 || blocks[i] >= pool->num_blocks) return HW_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (blocks[j] == blocks[i]) return HW_EINVAL;
+  }
+  return HW_OK;
+}
+
+hw_status hw_block_advance(const hw_pool* pool, int32_t n, const int32_t* blocks, void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  st = check_block_list(pool, n, blocks);
+  if (st != HW_OK) return st;
+  return launch_advance(*pool, n, blocks, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? HW_OK
+             : HW_EHIP;
+}
+
+hw_status hw_block_write(const hw_pool* pool, int32_t layer, int32_t n, const int32_t* blocks,
+                         const float* k_new, const float* v_new, double rope_theta,
+                         void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  st = check_block_list(pool, n, blocks);
+  if (st != HW_OK) return st;
+  if (!k_new || !v_new) return HW_EINVAL;
+  if (layer < 0 || layer >= pool->num_layers) return HW_EINVAL;
+  if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return HW_EINVAL;
+  return launch_write(*pool, layer, n, blocks, k_new, v_new, rope_theta,
+                      static_cast<hipStream_t>(stream)) == hipSuccess
+             ? HW_OK
+             : HW_EHIP;
+}
+
 hw_status hw_build_combined_tables(const hw_pool* pool, int32_t num_workers, int32_t common_block,
                                    const int32_t* worker_block, hw_entry* tables,
                                    int32_t* num_entries, void* stream) {

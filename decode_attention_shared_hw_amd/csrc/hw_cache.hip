@@ -232,7 +232,108 @@ __global__ void reset_kernel(int32_t* block_len, int32_t block) {
   if (threadIdx.x == 0) block_len[block] = 0;
 }
 
+// ------------------------------------------------------------ token write
+struct TokenArgs {
+  void* k;
+  void* v;
+  int32_t* block_len;
+  int32_t* status;
+  const float* k_new;  // [n][Hkv][D]
+  const float* v_new;
+  int64_t plane_elems;
+  int32_t n, Hkv, D;
+  int32_t blocks[HW_MAX_WORKERS];
+  int64_t start[HW_MAX_WORKERS];
+  int32_t cap[HW_MAX_WORKERS];
+  double inv_freq[kMaxHalf];
+};
+
+// Thread i reserves the next slot of block blocks[i].
+__global__ void advance_kernel(TokenArgs a) {
+  const int i = threadIdx.x;
+  if (i >= a.n) return;
+  const int32_t b = a.blocks[i];
+  const int32_t len = a.block_len[b];
+  if (len < 0 || len >= a.cap[i]) {
+    atomicOr(a.status, HW_DEV_WRITE_OVERFLOW);
+    return;
+  }
+  a.block_len[b] = len + 1;
+}
+
+// One workgroup per (listed block i, kv head g); thread t < D/2 writes the
+// rotate-half pair (t, t + D/2) of the key and of the value.
+template <typename T>
+__global__ void write_kernel(TokenArgs a) {
+#pragma clang fp contract(off)
+  const int i = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x - i * a.Hkv;
+  const int t = threadIdx.x;
+  const int half = a.D / 2;
+  const int32_t p = a.block_len[a.blocks[i]] - 1;
+  if (p < 0 || p >= a.cap[i]) {
+    if (t == 0) atomicOr(a.status, HW_DEV_WRITE_OVERFLOW);
+    return;
+  }
+  if (t >= half) return;
+  const int64_t slot = a.start[i] + p;
+  const float* kr = a.k_new + (static_cast<int64_t>(i) * a.Hkv + g) * a.D;
+  const float* vr = a.v_new + (static_cast<int64_t>(i) * a.Hkv + g) * a.D;
+  double s, c;
+  sincos(static_cast<double>(p) * a.inv_freq[t], &s, &c);
+  const double x0 = kr[t], x1 = kr[t + half];
+  T* kp = static_cast<T*>(a.k) + g * a.plane_elems;
+  T* vp = static_cast<T*>(a.v) + g * a.plane_elems;
+  kp[key_offset(slot, t, a.D)] = round_to<T>(x0 * c - x1 * s);
+  kp[key_offset(slot, t + half, a.D)] = round_to<T>(x1 * c + x0 * s);
+  vp[value_offset(slot, t, a.D)] = round_to<T>(static_cast<double>(vr[t]));
+  vp[value_offset(slot, t + half, a.D)] = round_to<T>(static_cast<double>(vr[t + half]));
+}
+
 }  // namespace
+
+hipError_t launch_advance(const hw_pool& pool, int32_t n, const int32_t* blocks, hipStream_t s) {
+  TokenArgs a{};
+  a.block_len = pool.block_len;
+  a.status = pool.status;
+  a.n = n;
+  for (int i = 0; i < n; ++i) {
+    a.blocks[i] = blocks[i];
+    a.cap[i] = pool.block_cap[blocks[i]];
+  }
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_write(const hw_pool& pool, int32_t layer, int32_t n, const int32_t* blocks,
+                        const float* k_new, const float* v_new, double theta, hipStream_t s) {
+  TokenArgs a{};
+  const size_t esz = pool.dtype == HW_F32 ? 4 : 2;
+  a.plane_elems = pool.num_slots * pool.head_dim;
+  const int64_t layer_off = static_cast<int64_t>(layer) * pool.num_kv_heads * a.plane_elems;
+  a.k = static_cast<char*>(pool.k) + layer_off * esz;
+  a.v = static_cast<char*>(pool.v) + layer_off * esz;
+  a.block_len = pool.block_len;
+  a.status = pool.status;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n = n;
+  a.Hkv = pool.num_kv_heads;
+  a.D = pool.head_dim;
+  for (int i = 0; i < n; ++i) {
+    a.blocks[i] = blocks[i];
+    a.start[i] = pool.block_start[blocks[i]];
+    a.cap[i] = pool.block_cap[blocks[i]];
+  }
+  for (int i = 0; i < pool.head_dim / 2; ++i)
+    a.inv_freq[i] = pow(theta, -2.0 * i / static_cast<double>(pool.head_dim));
+  const dim3 grid(static_cast<unsigned>(n * pool.num_kv_heads));
+  if (pool.dtype == HW_F32)
+    hipLaunchKernelGGL(write_kernel<float>, grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(write_kernel<uint16_t>, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_build_tables(int32_t* block_len, int32_t W, int32_t common,
                                const int32_t* worker_block, hw_entry* tables,

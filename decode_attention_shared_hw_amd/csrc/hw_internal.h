@@ -79,5 +79,8 @@ hipError_t launch_build_tables(int32_t* block_len, int32_t W, int32_t common,
 hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double theta,
                          hipStream_t s);
 hipError_t launch_reset(int32_t* block_len, int32_t block, hipStream_t s);
+hipError_t launch_advance(const hw_pool& pool, int32_t n, const int32_t* blocks, hipStream_t s);
+hipError_t launch_write(const hw_pool& pool, int32_t layer, int32_t n, const int32_t* blocks,
+                        const float* k_new, const float* v_new, double theta, hipStream_t s);
 
 }  // namespace hw

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libhogwild_attn.so")
 
 HW_OK, HW_EINVAL, HW_ERANGE, HW_ECAPACITY, HW_EUNSUPPORTED, HW_EWORKSPACE, HW_EHIP = range(7)
 HW_DEV_BAD_ENTRY, HW_DEV_BAD_LENGTH, HW_DEV_NO_TOKENS, HW_DEV_APPEND_OVERFLOW = 1, 2, 4, 8
+HW_DEV_WRITE_OVERFLOW = 16
 HW_F32, HW_BF16 = 0, 1
 HW_TILE_TOKENS = 32
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
@@ -54,8 +55,8 @@ class hw_pool(ctypes.Structure):
 
 EXPORTED = [
     "hw_abi_version", "hw_status_str", "hw_attn_workspace_bytes", "hw_attn_decode",
-    "hw_block_append", "hw_block_reset", "hw_build_combined_tables", "hw_pool_status",
-    "hw_set_tuning",
+    "hw_block_append", "hw_block_reset", "hw_block_advance", "hw_block_write",
+    "hw_build_combined_tables", "hw_pool_status", "hw_set_tuning",
 ]
 
 _lib = None
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.hw_block_append.argtypes = [PP, i32, i32, d, P]
         L.hw_block_reset.restype = i32
         L.hw_block_reset.argtypes = [PP, i32, P]
+        L.hw_block_advance.restype = i32
+        L.hw_block_advance.argtypes = [PP, i32, P, P]
+        L.hw_block_write.restype = i32
+        L.hw_block_write.argtypes = [PP, i32, i32, P, P, P, d, P]
         L.hw_build_combined_tables.restype = i32
         L.hw_build_combined_tables.argtypes = [PP, i32, i32, P, P, P, P]
         L.hw_pool_status.restype = i32
@@ -211,6 +216,28 @@ def hw_block_append(pool: Pool, src_block: int, dst_block: int, rope_theta: floa
 def hw_block_reset(pool: Pool, block: int, stream=None):
     _check(lib().hw_block_reset(ctypes.byref(pool.desc), int(block), _stream(stream)),
            "hw_block_reset")
+
+
+def _blocks(blocks):
+    arr = (ctypes.c_int32 * len(blocks))(*[int(b) for b in blocks])
+    return len(blocks), ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def hw_block_advance(pool: Pool, blocks, stream=None):
+    """Reserve the next slot of every listed block (block_len += 1 on the device)."""
+    n, p, keep = _blocks(blocks)
+    _check(lib().hw_block_advance(ctypes.byref(pool.desc), n, p, _stream(stream)),
+           "hw_block_advance")
+
+
+def hw_block_write(pool: Pool, layer: int, blocks, k_new: torch.Tensor, v_new: torch.Tensor,
+                   rope_theta: float, stream=None):
+    """Store each listed block's new token of `layer` in slot block_len - 1.
+    k_new, v_new: device fp32 [len(blocks)][num_kv_heads][head_dim]."""
+    n, p, keep = _blocks(blocks)
+    _check(lib().hw_block_write(ctypes.byref(pool.desc), int(layer), n, p, _ptr(k_new),
+                                _ptr(v_new), float(rope_theta), _stream(stream)),
+           "hw_block_write")
 
 
 def hw_build_combined_tables(pool: Pool, num_workers: int, common_block: int, worker_block,

@@ -75,6 +75,7 @@ typedef int32_t hw_status;
 #define HW_DEV_BAD_LENGTH 2      /* block_len < 0 or > capacity                                      */
 #define HW_DEV_NO_TOKENS 4       /* a worker sees no token; its rows are written as zeros            */
 #define HW_DEV_APPEND_OVERFLOW 8 /* len_dst + len_src > cap_dst at run time; nothing was moved        */
+#define HW_DEV_WRITE_OVERFLOW 16 /* advance past a block's capacity, or a token write into an empty block */
 
 /* Storage types. */
 #define HW_F32 0
@@ -179,6 +180,32 @@ hw_status hw_block_append(const hw_pool* pool, int32_t src_block, int32_t dst_bl
 
 /* Sets block_len[block] = 0 on the device (a worker starts a new step). */
 hw_status hw_block_reset(const hw_pool* pool, int32_t block, void* stream);
+
+/*
+ * Token write, part 1: reserves the next slot of every listed block for the
+ * decode step's new token: block_len[b] += 1 on the device.  A block already
+ * at capacity keeps its length and sets HW_DEV_WRITE_OVERFLOW.
+ *   blocks (host) [n], 1 <= n <= HW_MAX_WORKERS, distinct ids.
+ * Host-checked: HW_EINVAL (null, ids out of range or repeated), HW_ERANGE (n).
+ */
+hw_status hw_block_advance(const hw_pool* pool, int32_t n, const int32_t* blocks, void* stream);
+
+/*
+ * Token write, part 2, for one layer: stores each listed block's new token in
+ * the slot reserved by hw_block_advance, p = block_len[b] - 1, read on the
+ * device.  Keys are stored encoded at their local position (Hogwild! notes,
+ * key design 1: a block holds its keys at positions 0..len-1): key slot p of
+ * kv head h receives rho(k_new[i][h], p), computed with fp64 intermediates and
+ * rounded to nearest even in the pool type; value slot p receives v_new[i][h]
+ * rounded the same way.  Lengths are not changed.  A listed block of length 0
+ * is skipped and sets HW_DEV_WRITE_OVERFLOW.
+ *   blocks (host) [n], as for hw_block_advance.
+ *   k_new, v_new (device) [n][num_kv_heads][head_dim] fp32.
+ * Host-checked: HW_EINVAL (null, ids, layer, theta), HW_ERANGE (n).
+ */
+hw_status hw_block_write(const hw_pool* pool, int32_t layer, int32_t n, const int32_t* blocks,
+                         const float* k_new, const float* v_new, double rope_theta,
+                         void* stream);
 
 /*
  * Combined layout (key design 2) built on the device from the current

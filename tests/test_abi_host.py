@@ -145,3 +145,23 @@ def test_layout_positions_follow_the_documented_formula():
                 assert pv[vo] == slot * D + d
         assert torch.equal(layout.unpack_keys(layout.pack_keys(x)), x)
         assert torch.equal(layout.unpack_values(layout.pack_values(x)), x)
+
+
+def test_token_write_host_validation(lib):
+    pool = FakePool()
+    P = ctypes.byref(pool.desc)
+    p = ctypes.c_void_p(0x5000)
+    ok = (ctypes.c_int32 * 2)(1, 2)
+    dup = (ctypes.c_int32 * 2)(1, 1)
+    bad = (ctypes.c_int32 * 2)(1, 3)
+    cast = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert lib.hw_block_advance(P, 2, cast(dup), None) == hw.HW_EINVAL
+    assert lib.hw_block_advance(P, 2, cast(bad), None) == hw.HW_EINVAL
+    assert lib.hw_block_advance(P, 0, cast(ok), None) == hw.HW_ERANGE
+    assert lib.hw_block_advance(P, 33, cast(ok), None) == hw.HW_ERANGE
+    assert lib.hw_block_advance(P, 2, None, None) == hw.HW_EINVAL
+    assert lib.hw_block_write(P, 0, 2, cast(dup), p, p, 1e4, None) == hw.HW_EINVAL
+    assert lib.hw_block_write(P, 1, 2, cast(ok), p, p, 1e4, None) == hw.HW_EINVAL   # layer
+    assert lib.hw_block_write(P, 0, 2, cast(ok), None, p, 1e4, None) == hw.HW_EINVAL
+    assert lib.hw_block_write(P, 0, 2, cast(ok), p, p, 0.0, None) == hw.HW_EINVAL
+    assert lib.hw_block_write(P, 0, 0, cast(ok), p, p, 1e4, None) == hw.HW_ERANGE

@@ -344,15 +344,67 @@ def test_qwq_step_full_size_sampled():
     assert hw.hw_pool_status(pool) == 0
 
 
+# ------------------------------------------------------- token write (NEXT-1)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_token_write_matches_oracle_bit_exact(dtype):
+    theta = 1e6 if dtype == torch.bfloat16 else 1e4
+    lens = [300, 31, 64, 0]
+    wl = workloads.Workload("write", 3, 6, 2, 128, theta, dtype, 2, lens, [512, 64, 96, 32], 0.5, 13)
+    s = Setup(wl, n_layers=2)
+    blocks = [1, 2, 3]
+    g = torch.Generator().manual_seed(5)
+    kn = [torch.randn(3, wl.Hkv, wl.D, generator=g) for _ in range(2)]
+    vn = [torch.randn(3, wl.Hkv, wl.D, generator=g) for _ in range(2)]
+    hw.hw_block_advance(s.pool, blocks)
+    for layer in range(2):
+        hw.hw_block_write(s.pool, layer, blocks, kn[layer].cuda(), vn[layer].cuda(), theta)
+    torch.cuda.synchronize()
+    lo = np.array(lens, np.int32)
+    lo[blocks] += 1
+    assert s.pool.block_len.cpu().tolist() == lo.tolist()
+    assert hw.hw_pool_status(s.pool) == 0
+    dt = oracle.HWO_BF16 if dtype == torch.bfloat16 else oracle.HWO_F32
+    for layer in range(2):
+        Ko = s.K[layer].double().numpy().copy()
+        Vo = s.V[layer].double().numpy().copy()
+        rc = oracle.block_write(Ko, Vo, s.pool.block_start, lo, blocks, kn[layer].double().numpy(),
+                                vn[layer].double().numpy(), theta, dt)
+        assert rc == 0
+        Kg, Vg = s.pool.load_layer(layer)
+        Kg, Vg = Kg.cpu().double().numpy(), Vg.cpu().double().numpy()
+        assert np.array_equal(Vg, Vo)
+        if dtype == torch.bfloat16:
+            assert np.array_equal(Kg, Ko)
+        else:
+            diff = Kg != Ko
+            if diff.any():  # at most one ulp of fp32, and rarely
+                ulp = np.spacing(np.abs(Ko[diff]).astype(np.float32)).astype(np.float64)
+                assert (np.abs(Kg[diff] - Ko[diff]) <= ulp).all() and diff.sum() <= 4
+
+
+def test_token_write_overflow_and_empty_block():
+    wl = _custom(1, 2, 2, 64, [32, 0], caps=[32, 32])
+    s = Setup(wl)
+    K0, _ = s.pool.load_layer(0)
+    hw.hw_block_advance(s.pool, [0])          # block 0 is full: nothing reserved
+    one = torch.ones(1, wl.Hkv, wl.D, device="cuda")
+    hw.hw_block_write(s.pool, 0, [1], one, one, wl.theta)   # block 1 is empty: nothing written
+    torch.cuda.synchronize()
+    assert s.pool.block_len.cpu().tolist() == [32, 0]
+    assert hw.hw_pool_status(s.pool, clear=True) == hw.HW_DEV_WRITE_OVERFLOW
+    K1, _ = s.pool.load_layer(0)
+    assert torch.equal(K0, K1)
+
+
 # ------------------------------------------------- generation loop (config 5)
 def test_generation_loop_matches_oracle():
-    """A shortened config-5 loop (Qwen3-8B heads, 4 workers): every step the
-    private blocks grow by one token (length bump over pre-filled capacity),
-    the tables are rebuilt on the device and every layer decodes; every 64
-    steps one worker's block is appended into the common block and reset.
-    The oracle replays the same appends on its own fp64 copy of the pool;
-    attention is checked at several steps and the whole pool bit-exactly at
-    the end."""
+    """A shortened config-5 loop (Qwen3-8B heads, 4 workers): every step each
+    worker's block reserves a slot for its new token (hw_block_advance), the
+    tables are rebuilt on the device, and every layer writes the new tokens'
+    K/V (hw_block_write) and decodes; every 64 steps one worker's block is
+    appended into the common block and reset.  The oracle replays the writes
+    and appends on its own fp64 copy of the pool; attention is checked at
+    several steps and the whole pool bit-exactly at the end."""
     steps, L = 256, 2
     wl = workloads.qwen3_loop(layers=L, common0=2048, steps=steps)
     sched = workloads.loop_appends(wl, steps)
@@ -364,12 +416,22 @@ def test_generation_loop_matches_oracle():
     out = torch.zeros(L, wl.W, wl.Hq, wl.D, device="cuda")
     checks = {0, 63, 64, 130, 255}
     worst = 0.0
+    gk = torch.Generator().manual_seed(17)
+    kn = [torch.randn(wl.W, wl.Hkv, wl.D, generator=gk) for _ in range(L)]
+    vn = [torch.randn(wl.W, wl.Hkv, wl.D, generator=gk) for _ in range(L)]
+    kn_d = [k.cuda() for k in kn]
+    vn_d = [v.cuda() for v in vn]
     for step in range(steps):
         lens[1:] += 1
-        s.pool.block_len[1:] += 1
+        hw.hw_block_advance(s.pool, wl.worker_block)
         hw.hw_build_combined_tables(s.pool, wl.W, wl.common_block, wl.worker_block, s.tables,
                                     s.num_entries)
         for layer in range(L):
+            hw.hw_block_write(s.pool, layer, wl.worker_block, kn_d[layer], vn_d[layer], wl.theta)
+            rc = oracle.block_write(Kh[layer], Vh[layer], starts, lens, wl.worker_block,
+                                    kn[layer].double().numpy(), vn[layer].double().numpy(),
+                                    wl.theta, oracle.HWO_BF16)
+            assert rc == 0
             hw.hw_attn_decode(s.pool, layer, s.q[layer].cuda(), s.tables, s.num_entries, wl.theta,
                               out[layer], s.ws)
         if step in checks:
