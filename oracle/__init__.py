@@ -65,6 +65,8 @@ def lib():
                                       i64, P, P, P, P]
         L.hwo_block_append.restype = i32
         L.hwo_block_append.argtypes = [i32, i32, i32, i64, P, P, i32, P, P, P, i32, i32, d, i32]
+        L.hwo_build_interleaved_tables.restype = i32
+        L.hwo_build_interleaved_tables.argtypes = L.hwo_build_combined_tables.argtypes
         L.hwo_block_write.restype = i32
         L.hwo_block_write.argtypes = [i32, i32, i64, P, P, i32, P, P, i32, P, P, P, d, i32]
         _lib = L
@@ -106,6 +108,22 @@ def build_combined_tables(common_block: int, worker_block, block_len):
                                          _p(tb), _p(to), _p(ne))
     if rc != HWO_OK:
         raise ValueError(f"hwo_build_combined_tables: code {rc}")
+    return tb, to, ne
+
+
+def build_interleaved_tables(common_block: int, worker_block, block_len):
+    """Interleaved layout: [common, own] per worker.  Same return shapes as
+    build_combined_tables."""
+    wb = _c(worker_block, np.int32)
+    bl = _c(block_len, np.int32)
+    W = wb.shape[0]
+    tb = np.zeros((W, W + 1), np.int32)
+    to = np.zeros((W, W + 1), np.int32)
+    ne = np.zeros((W,), np.int32)
+    rc = lib().hwo_build_interleaved_tables(W, int(common_block), _p(wb), bl.shape[0], _p(bl),
+                                            _p(tb), _p(to), _p(ne))
+    if rc != HWO_OK:
+        raise ValueError(f"hwo_build_interleaved_tables: code {rc}")
     return tb, to, ne
 
 

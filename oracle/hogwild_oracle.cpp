@@ -103,6 +103,28 @@ int32_t hwo_build_combined_tables(int32_t W, int32_t common_block, const int32_t
   return HWO_OK;
 }
 
+int32_t hwo_build_interleaved_tables(int32_t W, int32_t common_block, const int32_t* worker_block,
+                                     int32_t num_blocks, const int32_t* block_len,
+                                     int32_t* tbl_block, int32_t* tbl_off, int32_t* num_entries) {
+  // same arguments and checks as the combined layout; only the entries differ
+  const int32_t rc = hwo_build_combined_tables(W, common_block, worker_block, num_blocks,
+                                               block_len, tbl_block, tbl_off, num_entries);
+  if (rc != HWO_OK) return rc;
+  const int32_t E = W + 1;
+  for (int32_t w = 0; w < W; ++w) {
+    for (int32_t e = 0; e < E; ++e) {
+      tbl_block[w * E + e] = 0;
+      tbl_off[w * E + e] = 0;
+    }
+    tbl_block[w * E] = common_block;
+    tbl_off[w * E] = 0;
+    tbl_block[w * E + 1] = worker_block[w];
+    tbl_off[w * E + 1] = block_len[common_block];
+    num_entries[w] = 2;
+  }
+  return HWO_OK;
+}
+
 // The query sits at the last position of its own view (its K/V was written
 // before attention, as in ordinary decode).
 int64_t hwo_query_position(int32_t n_entries, const int32_t* tbl_block, const int32_t* tbl_off,

@@ -73,6 +73,17 @@ int32_t hwo_build_combined_tables(int32_t W, int32_t common_block, const int32_t
                                   int32_t num_blocks, const int32_t* block_len,
                                   int32_t* tbl_block, int32_t* tbl_off, int32_t* num_entries);
 
+/*
+ * Interleaved layout (the Hogwild! notes' layout ablation: step-level
+ * synchronization only): worker w sees the common history of finished steps
+ * and its own block, [common @ 0, worker_block[w] @ len(common)]; the other
+ * workers' current blocks are not visible.  Same arguments, checks and table
+ * shape as hwo_build_combined_tables (entries past num_entries[w] = 2 are 0).
+ */
+int32_t hwo_build_interleaved_tables(int32_t W, int32_t common_block, const int32_t* worker_block,
+                                     int32_t num_blocks, const int32_t* block_len,
+                                     int32_t* tbl_block, int32_t* tbl_off, int32_t* num_entries);
+
 /* i_q of one worker's view: max over entries with len > 0 of (off + len) - 1; -1 if none. */
 int64_t hwo_query_position(int32_t n_entries, const int32_t* tbl_block, const int32_t* tbl_off,
                            const int32_t* block_len);

@@ -444,3 +444,38 @@ def test_token_write_errors():
     assert oracle.block_write(K, V, starts, np.array([0], np.int32), np.array([0], np.int32), one,
                               one, 1e4, 0) == oracle.HWO_ENOTOKENS
     assert (K == 0).all() and (V == 0).all()
+
+
+# ------------------------------------------------- interleaved layout (NEXT-2)
+def test_interleaved_tables_hand_example():
+    """Step-level sync only (the notes' layout ablation): each worker sees the
+    common history and its own block, nothing of the others' current steps."""
+    tb, to, ne = oracle.build_interleaved_tables(0, [1, 2], np.array([10, 3, 4], np.int32))
+    assert ne.tolist() == [2, 2]
+    assert tb[:, :2].tolist() == [[0, 1], [0, 2]]
+    assert to[:, :2].tolist() == [[0, 10], [0, 10]]
+
+
+def test_interleaved_equals_combined_with_other_steps_empty():
+    """Worker w's interleaved view is its combined view with every other
+    worker's current block emptied (empty blocks add no tokens and no offset)."""
+    rng = np.random.default_rng(30)
+    D, Hkv, Hq, theta, W = 16, 2, 4, 1e4, 3
+    starts = np.array([0, 64, 96, 128], np.int64)
+    lens = np.array([50, 7, 19, 12], np.int32)
+    S = 160
+    K = rng.standard_normal((Hkv, S, D))
+    V = rng.standard_normal((Hkv, S, D))
+    q = rng.standard_normal((W, Hq, D))
+    tb, to, ne = oracle.build_interleaved_tables(0, [1, 2, 3], lens)
+    inter, rc = oracle.attn_decode(1, q, K, V, tb, to, ne, lens, starts, theta)
+    assert rc == 0
+    for w in range(W):
+        l2 = lens.copy()
+        for v in range(W):
+            if v != w:
+                l2[1 + v] = 0
+        tb2, to2, ne2 = oracle.build_combined_tables(0, [1, 2, 3], l2)
+        comb, rc = oracle.attn_decode(1, q, K, V, tb2, to2, ne2, l2, starts, theta)
+        assert rc == 0
+        np.testing.assert_allclose(inter[w], comb[w], rtol=0, atol=1e-12)
