@@ -300,6 +300,16 @@ hw_status hw_block_write(const hw_pool* pool, int32_t layer, int32_t n, const in
 hw_status hw_build_combined_tables(const hw_pool* pool, int32_t num_workers, int32_t common_block,
                                    const int32_t* worker_block, hw_entry* tables,
                                    int32_t* num_entries, void* stream) {
+  return hw_build_view_tables(pool, HW_LAYOUT_COMBINED, num_workers, common_block, worker_block,
+                              tables, num_entries, stream);
+}
+
+hw_status hw_build_view_tables(const hw_pool* pool, int32_t layout, int32_t num_workers,
+                               int32_t common_block, const int32_t* worker_block,
+                               hw_entry* tables, int32_t* num_entries, void* stream) {
+  if (layout != HW_LAYOUT_COMBINED && layout != HW_LAYOUT_INTERLEAVED &&
+      layout != HW_LAYOUT_CONTIGUOUS)
+    return HW_EINVAL;
   hw_status st = check_pool(pool);
   if (st != HW_OK) return st;
   if (!worker_block || !tables || !num_entries) return HW_EINVAL;
@@ -312,7 +322,8 @@ hw_status hw_build_combined_tables(const hw_pool* pool, int32_t num_workers, int
     for (int v = 0; v < w; ++v)
       if (worker_block[v] == b) return HW_EINVAL;
   }
-  const hipError_t e = launch_build_tables(pool->block_len, num_workers, common_block, worker_block,
+  const hipError_t e = launch_build_tables(pool->block_len, layout, num_workers, common_block,
+                                           worker_block,
                                            tables, num_entries, pool->num_blocks,
                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? HW_OK : HW_EHIP;

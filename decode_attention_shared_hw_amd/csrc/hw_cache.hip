@@ -12,12 +12,15 @@ struct TableArgs {
   const int32_t* block_len;
   hw_entry* tables;  // [W][W+1]
   int32_t* num_entries;
-  int32_t W, common, num_blocks;
+  int32_t W, common, num_blocks, layout;
   int32_t worker_block[HW_MAX_WORKERS];
 };
 
-// Thread w writes worker w's view: common cache, the other workers' blocks in
-// increasing worker id, its own block last; view_offset = running length sum.
+// Thread w writes worker w's view; view_offset = running length sum.
+//   combined / contiguous: common cache, the other workers' blocks in
+//     increasing worker id, its own block last;
+//   interleaved: common cache, its own block (the others' current steps are
+//     not visible); unused entries are zeroed.
 __global__ void build_tables_kernel(TableArgs a) {
   const int w = threadIdx.x;
   if (w >= a.W) return;
@@ -33,10 +36,15 @@ __global__ void build_tables_kernel(TableArgs a) {
     ++e;
   };
   put(a.common);
-  for (int v = 0; v < a.W; ++v)
-    if (v != w) put(a.worker_block[v]);
+  if (a.layout != HW_LAYOUT_INTERLEAVED)
+    for (int v = 0; v < a.W; ++v)
+      if (v != w) put(a.worker_block[v]);
   put(a.worker_block[w]);
   a.num_entries[w] = e;
+  for (int k = e; k < E; ++k) {
+    row[k].block_id = 0;
+    row[k].view_offset = 0;
+  }
 }
 
 // ------------------------------------------------------------- append (a5)
@@ -335,11 +343,12 @@ hipError_t launch_write(const hw_pool& pool, int32_t layer, int32_t n, const int
   return hipGetLastError();
 }
 
-hipError_t launch_build_tables(int32_t* block_len, int32_t W, int32_t common,
+hipError_t launch_build_tables(int32_t* block_len, int32_t layout, int32_t W, int32_t common,
                                const int32_t* worker_block, hw_entry* tables,
                                int32_t* num_entries, int32_t num_blocks, hipStream_t s) {
   TableArgs a{};
   a.block_len = block_len;
+  a.layout = layout;
   a.tables = tables;
   a.num_entries = num_entries;
   a.W = W;

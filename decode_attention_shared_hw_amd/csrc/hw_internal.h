@@ -73,7 +73,7 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 int decode_blocks_per_cu(int path, int dtype, int D, int rows);
 
 // Launchers (hw_cache.hip).
-hipError_t launch_build_tables(int32_t* block_len, int32_t W, int32_t common,
+hipError_t launch_build_tables(int32_t* block_len, int32_t layout, int32_t W, int32_t common,
                                const int32_t* worker_block, hw_entry* tables,
                                int32_t* num_entries, int32_t num_blocks, hipStream_t s);
 hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double theta,

@@ -23,6 +23,7 @@ HW_DEV_WRITE_OVERFLOW = 16
 HW_F32, HW_BF16 = 0, 1
 HW_TILE_TOKENS = 32
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+HW_LAYOUT_COMBINED, HW_LAYOUT_INTERLEAVED, HW_LAYOUT_CONTIGUOUS = 0, 1, 2
 
 
 class HWError(RuntimeError):
@@ -56,7 +57,7 @@ class hw_pool(ctypes.Structure):
 EXPORTED = [
     "hw_abi_version", "hw_status_str", "hw_attn_workspace_bytes", "hw_attn_decode",
     "hw_block_append", "hw_block_reset", "hw_block_advance", "hw_block_write",
-    "hw_build_combined_tables", "hw_pool_status", "hw_set_tuning",
+    "hw_build_combined_tables", "hw_build_view_tables", "hw_pool_status", "hw_set_tuning",
 ]
 
 _lib = None
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.hw_block_write.argtypes = [PP, i32, i32, P, P, P, d, P]
         L.hw_build_combined_tables.restype = i32
         L.hw_build_combined_tables.argtypes = [PP, i32, i32, P, P, P, P]
+        L.hw_build_view_tables.restype = i32
+        L.hw_build_view_tables.argtypes = [PP, i32, i32, i32, P, P, P, P]
         L.hw_pool_status.restype = i32
         L.hw_pool_status.argtypes = [PP, P, i32]
         L.hw_set_tuning.restype = i32
@@ -248,6 +251,17 @@ def hw_build_combined_tables(pool: Pool, num_workers: int, common_block: int, wo
                                           int(common_block), ctypes.cast(wb, ctypes.c_void_p),
                                           _ptr(tables), _ptr(num_entries), _stream(stream)),
            "hw_build_combined_tables")
+
+
+def hw_build_view_tables(pool: Pool, layout: int, num_workers: int, common_block: int,
+                         worker_block, tables: torch.Tensor, num_entries: torch.Tensor,
+                         stream=None):
+    """View tables of one of the HW_LAYOUT_* layouts; shapes as hw_build_combined_tables."""
+    wb = (ctypes.c_int32 * num_workers)(*[int(b) for b in worker_block])
+    _check(lib().hw_build_view_tables(ctypes.byref(pool.desc), int(layout), int(num_workers),
+                                      int(common_block), ctypes.cast(wb, ctypes.c_void_p),
+                                      _ptr(tables), _ptr(num_entries), _stream(stream)),
+           "hw_build_view_tables")
 
 
 def hw_pool_status(pool: Pool, clear: bool = False) -> int:

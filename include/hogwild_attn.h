@@ -221,6 +221,27 @@ hw_status hw_build_combined_tables(const hw_pool* pool, int32_t num_workers, int
                                    int32_t* num_entries, void* stream);
 
 /*
+ * The cache layouts of the Hogwild! notes' layout ablation, as view tables
+ * built on the device (same arguments and table shape as
+ * hw_build_combined_tables; entries past num_entries[w] are zeroed):
+ *   HW_LAYOUT_COMBINED     token-wise sync plus step history: the combined
+ *                          layout above.
+ *   HW_LAYOUT_INTERLEAVED  step-level sync only: [common_block @ 0,
+ *                          worker_block[w] @ len(common)]; the other workers'
+ *                          current steps are not visible until appended.
+ *   HW_LAYOUT_CONTIGUOUS   token-level sync only: each worker's whole output
+ *                          stays in its own block (no step history is ever
+ *                          appended); the tables have the combined order.
+ * Host-checked: as hw_build_combined_tables, plus HW_EINVAL for the layout.
+ */
+#define HW_LAYOUT_COMBINED 0
+#define HW_LAYOUT_INTERLEAVED 1
+#define HW_LAYOUT_CONTIGUOUS 2
+hw_status hw_build_view_tables(const hw_pool* pool, int32_t layout, int32_t num_workers,
+                               int32_t common_block, const int32_t* worker_block,
+                               hw_entry* tables, int32_t* num_entries, void* stream);
+
+/*
  * Reads the pool's sticky HW_DEV_* bits into *flags (host).  Synchronizes the
  * device first.  clear != 0 zeroes the word afterwards.
  */

@@ -165,3 +165,13 @@ def test_token_write_host_validation(lib):
     assert lib.hw_block_write(P, 0, 2, cast(ok), None, p, 1e4, None) == hw.HW_EINVAL
     assert lib.hw_block_write(P, 0, 2, cast(ok), p, p, 0.0, None) == hw.HW_EINVAL
     assert lib.hw_block_write(P, 0, 0, cast(ok), p, p, 1e4, None) == hw.HW_ERANGE
+
+
+def test_view_tables_host_validation(lib):
+    pool = FakePool()
+    P = ctypes.byref(pool.desc)
+    p = ctypes.c_void_p(0x5000)
+    wb = (ctypes.c_int32 * 2)(1, 2)
+    cast = ctypes.cast(wb, ctypes.c_void_p)
+    assert lib.hw_build_view_tables(P, 3, 2, 0, cast, p, p, None) == hw.HW_EINVAL
+    assert lib.hw_build_view_tables(P, -1, 2, 0, cast, p, p, None) == hw.HW_EINVAL

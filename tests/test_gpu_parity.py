@@ -344,6 +344,38 @@ def test_qwq_step_full_size_sampled():
     assert hw.hw_pool_status(pool) == 0
 
 
+# ------------------------------------------------------ cache layouts (NEXT-2)
+@pytest.mark.parametrize("layout", [hw.HW_LAYOUT_COMBINED, hw.HW_LAYOUT_INTERLEAVED,
+                                    hw.HW_LAYOUT_CONTIGUOUS])
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_view_tables_match_oracle(layout, W):
+    lens = [700] + [37 * (w + 1) for w in range(W)]
+    wl = _custom(W, 2 * W, W, 64, lens)
+    s = Setup(wl)
+    hw.hw_build_view_tables(s.pool, layout, W, 0, wl.worker_block, s.tables, s.num_entries)
+    torch.cuda.synchronize()
+    build = (oracle.build_interleaved_tables if layout == hw.HW_LAYOUT_INTERLEAVED
+             else oracle.build_combined_tables)
+    tb, to, ne = build(0, wl.worker_block, np.array(lens, np.int32))
+    t = s.tables.cpu().numpy()
+    assert s.num_entries.cpu().tolist() == ne.tolist()
+    assert np.array_equal(t[:, :, 0], tb) and np.array_equal(t[:, :, 1], to)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_interleaved_layout_attention_matches_oracle(path):
+    hw.hw_set_tuning(path, 0)
+    wl = _custom(4, 40, 8, 128, [3000, 500, 77, 300, 129])
+    s = Setup(wl, poison_unused=True)
+    hw.hw_build_view_tables(s.pool, hw.HW_LAYOUT_INTERLEAVED, wl.W, 0, wl.worker_block, s.tables,
+                            s.num_entries)
+    got = s.decode()
+    lens = np.array(wl.lens, np.int32)
+    ref, rc = s.oracle_decode(tables=oracle.build_interleaved_tables(0, wl.worker_block, lens))
+    assert rc == 0
+    assert_close(got, ref, torch.bfloat16, f"interleaved path {path}")
+
+
 # ------------------------------------------------------- token write (NEXT-1)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_token_write_matches_oracle_bit_exact(dtype):
