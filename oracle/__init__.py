@@ -65,6 +65,9 @@ def lib():
                                       i64, P, P, P, P]
         L.hwo_block_append.restype = i32
         L.hwo_block_append.argtypes = [i32, i32, i32, i64, P, P, i32, P, P, P, i32, i32, d, i32]
+        L.hwo_attn_chunk.restype = i32
+        L.hwo_attn_chunk.argtypes = [i32, i32, i32, i32, i32, i32, d, i32, P, P, P, i32, P, P, i64,
+                                     P, P, P, P]
         L.hwo_build_interleaved_tables.restype = i32
         L.hwo_build_interleaved_tables.argtypes = L.hwo_build_combined_tables.argtypes
         L.hwo_block_write.restype = i32
@@ -168,6 +171,27 @@ def attn_decode(form, q, K, V, tbl_block, tbl_off, num_entries, block_len, block
                                _p(V), _p(out))
     return out, rc
 
+
+
+def attn_chunk(form, q, K, V, tbl_block, tbl_off, num_entries, block_len, block_start, theta):
+    """Query chunk: q [W][n][Hq][D]; K, V [Hkv][num_slots][D]; tables [W][E].
+    Query j of worker w sits at i_q[w] - (n - 1 - j) with a causal mask over
+    the view.  Returns (out [W][n][Hq][D], rc)."""
+    q = _c(q, np.float64)
+    K = _c(K, np.float64)
+    V = _c(V, np.float64)
+    tb = _c(tbl_block, np.int32)
+    to = _c(tbl_off, np.int32)
+    ne = _c(num_entries, np.int32)
+    bl = _c(block_len, np.int32)
+    bs = _c(block_start, np.int64)
+    W, n, Hq, D = q.shape
+    Hkv, S, _ = K.shape
+    out = np.zeros_like(q)
+    rc = lib().hwo_attn_chunk(int(form), W, n, Hq, Hkv, D, float(theta), tb.shape[1], _p(tb),
+                              _p(to), _p(ne), bl.shape[0], _p(bl), _p(bs), S, _p(q), _p(K),
+                              _p(V), _p(out))
+    return out, rc
 
 def block_append(K, V, block_start, block_cap, block_len, src, dst, theta, dtype):
     """In place on float64 arrays K, V [L][Hkv][num_slots][D] and int32 block_len.  Returns rc."""

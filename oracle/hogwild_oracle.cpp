@@ -139,10 +139,13 @@ int64_t hwo_query_position(int32_t n_entries, const int32_t* tbl_block, const in
   return iq;
 }
 
-int32_t hwo_attn_one(int32_t form, int32_t D, double theta, int32_t n_entries,
-                     const int32_t* tbl_block, const int32_t* tbl_off, int32_t num_blocks,
-                     const int32_t* block_len, const int64_t* block_start, const double* q,
-                     const double* K_plane, const double* V_plane, double* out) {
+// One query row at view position i_q - lag (lag = 0: the decode query), over
+// the view's tokens at view positions <= that position.
+static int32_t attn_row(int32_t form, int32_t D, double theta, int32_t n_entries,
+                        const int32_t* tbl_block, const int32_t* tbl_off, int32_t num_blocks,
+                        const int32_t* block_len, const int64_t* block_start, int32_t lag,
+                        const double* q, const double* K_plane, const double* V_plane,
+                        double* out) {
   for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
   if (D <= 0 || D % 2 != 0 || (form != 0 && form != 1)) return HWO_EINVAL;
   for (int32_t e = 0; e < n_entries; ++e) {
@@ -151,8 +154,8 @@ int32_t hwo_attn_one(int32_t form, int32_t D, double theta, int32_t n_entries,
     for (int32_t f = 0; f < e; ++f)
       if (tbl_block[f] == b) return HWO_EINVAL;
   }
-  const int64_t iq = hwo_query_position(n_entries, tbl_block, tbl_off, block_len);
-  if (iq < 0) return HWO_ENOTOKENS;
+  const int64_t iq = hwo_query_position(n_entries, tbl_block, tbl_off, block_len) - lag;
+  if (iq < 0 || lag < 0) return HWO_ENOTOKENS;
 
   const double scale = 1.0 / std::sqrt(static_cast<double>(D));
   std::vector<double> scores;  // concatenation over blocks, in table order
@@ -165,7 +168,7 @@ int32_t hwo_attn_one(int32_t form, int32_t D, double theta, int32_t n_entries,
     for (int32_t e = 0; e < n_entries; ++e) {
       const int32_t b = tbl_block[e];
       const int64_t off = tbl_off[e];
-      for (int32_t j = 0; j < block_len[b]; ++j) {
+      for (int32_t j = 0; j < block_len[b] && off + j <= iq; ++j) {
         const double* kst = K_plane + (block_start[b] + j) * static_cast<int64_t>(D);
         // ... and every key at its absolute view position off + j: undo the
         // local encoding at j (storage convention: local positions 0..len-1),
@@ -181,9 +184,9 @@ int32_t hwo_attn_one(int32_t form, int32_t D, double theta, int32_t n_entries,
     for (int32_t e = 0; e < n_entries; ++e) {
       const int32_t b = tbl_block[e];
       const int64_t off = tbl_off[e];
-      if (block_len[b] <= 0) continue;
+      if (block_len[b] <= 0 || off > iq) continue;
       hwo_rope(q, D, theta, static_cast<double>(iq - off), qr.data());
-      for (int32_t j = 0; j < block_len[b]; ++j) {
+      for (int32_t j = 0; j < block_len[b] && off + j <= iq; ++j) {
         const double* kst = K_plane + (block_start[b] + j) * static_cast<int64_t>(D);
         scores.push_back(dot(qr.data(), kst, D) * scale);
         values.push_back(V_plane + (block_start[b] + j) * static_cast<int64_t>(D));
@@ -200,11 +203,20 @@ int32_t hwo_attn_one(int32_t form, int32_t D, double theta, int32_t n_entries,
     p[t] = std::exp(scores[t] - m);
     denom += p[t];
   }
+  if (scores.empty()) return HWO_ENOTOKENS;
   for (size_t t = 0; t < scores.size(); ++t) {
     const double w = p[t] / denom;
     for (int32_t d = 0; d < D; ++d) out[d] += w * values[t][d];
   }
   return HWO_OK;
+}
+
+int32_t hwo_attn_one(int32_t form, int32_t D, double theta, int32_t n_entries,
+                     const int32_t* tbl_block, const int32_t* tbl_off, int32_t num_blocks,
+                     const int32_t* block_len, const int64_t* block_start, const double* q,
+                     const double* K_plane, const double* V_plane, double* out) {
+  return attn_row(form, D, theta, n_entries, tbl_block, tbl_off, num_blocks, block_len,
+                  block_start, 0, q, K_plane, V_plane, out);
 }
 
 int32_t hwo_attn_decode(int32_t form, int32_t W, int32_t Hq, int32_t Hkv, int32_t D, double theta,
@@ -225,6 +237,30 @@ int32_t hwo_attn_decode(int32_t form, int32_t W, int32_t Hq, int32_t Hkv, int32_
                                      q + (static_cast<int64_t>(w) * Hq + h) * D, K + plane,
                                      V + plane, out + (static_cast<int64_t>(w) * Hq + h) * D);
       if (r != HWO_OK && rc == HWO_OK) rc = r;
+    }
+  }
+  return rc;
+}
+
+int32_t hwo_attn_chunk(int32_t form, int32_t W, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                       double theta, int32_t E, const int32_t* tbl_block, const int32_t* tbl_off,
+                       const int32_t* num_entries, int32_t num_blocks, const int32_t* block_len,
+                       const int64_t* block_start, int64_t num_slots, const double* q,
+                       const double* K, const double* V, double* out) {
+  if (W <= 0 || n <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return HWO_EINVAL;
+  const int32_t G = Hq / Hkv;
+  int32_t rc = HWO_OK;
+  for (int32_t w = 0; w < W; ++w) {
+    if (num_entries[w] < 0 || num_entries[w] > E) return HWO_EINVAL;
+    for (int32_t j = 0; j < n; ++j) {
+      for (int32_t h = 0; h < Hq; ++h) {
+        const int64_t plane = static_cast<int64_t>(h / G) * num_slots * D;
+        const int64_t row = (static_cast<int64_t>(w) * n + j) * Hq + h;
+        const int32_t r = attn_row(form, D, theta, num_entries[w], tbl_block + w * E,
+                                   tbl_off + w * E, num_blocks, block_len, block_start,
+                                   n - 1 - j, q + row * D, K + plane, V + plane, out + row * D);
+        if (r != HWO_OK && rc == HWO_OK) rc = r;
+      }
     }
   }
   return rc;

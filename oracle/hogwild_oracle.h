@@ -116,6 +116,20 @@ int32_t hwo_attn_decode(int32_t form, int32_t W, int32_t Hq, int32_t Hkv, int32_
                         const double* K, const double* V, double* out);
 
 /*
+ * Multi-token query chunk: every worker attends with its last n tokens at
+ * once (a prompt injected into, or a header prefilled in, its own block).
+ * q, out: [W][n][Hq][D].  Query j of worker w sits at view position
+ * i_q[w] - (n - 1 - j) and sees the view's tokens at positions up to its own
+ * (a causal mask over the view); n = 1 is hwo_attn_decode.  A row that sees
+ * no token is zero and the call returns HWO_ENOTOKENS.
+ */
+int32_t hwo_attn_chunk(int32_t form, int32_t W, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                       double theta, int32_t E, const int32_t* tbl_block, const int32_t* tbl_off,
+                       const int32_t* num_entries, int32_t num_blocks, const int32_t* block_len,
+                       const int64_t* block_start, int64_t num_slots, const double* q,
+                       const double* K, const double* V, double* out);
+
+/*
  * Step completion (a5) over all layers.  K, V: [L][Hkv][num_slots][D].
  * For j < len_src: dst token len_dst + j gets the src key re-encoded at that
  * local position (rounded to dtype) and the src value; then

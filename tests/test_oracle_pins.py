@@ -479,3 +479,66 @@ def test_interleaved_equals_combined_with_other_steps_empty():
         comb, rc = oracle.attn_decode(1, q, K, V, tb2, to2, ne2, l2, starts, theta)
         assert rc == 0
         np.testing.assert_allclose(inter[w], comb[w], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------- multi-token query chunks (NEXT-3)
+def test_chunk_of_one_token_is_decode():
+    rng = np.random.default_rng(40)
+    D, Hkv, Hq, theta = 16, 2, 4, 1e4
+    starts = np.array([0, 64, 96], np.int64)
+    lens = np.array([50, 9, 13], np.int32)
+    K = rng.standard_normal((Hkv, 128, D))
+    V = rng.standard_normal((Hkv, 128, D))
+    q = rng.standard_normal((2, Hq, D))
+    tb, to, ne = oracle.build_combined_tables(0, [1, 2], lens)
+    dec, rc = oracle.attn_decode(1, q, K, V, tb, to, ne, lens, starts, theta)
+    ch, rc2 = oracle.attn_chunk(1, q[:, None], K, V, tb, to, ne, lens, starts, theta)
+    assert rc == 0 and rc2 == 0
+    assert np.array_equal(ch[:, 0], dec)
+
+
+@pytest.mark.parametrize("form", [0, 1])
+def test_chunk_row_equals_decode_on_the_truncated_view(form):
+    """Row j of a chunk of n sits lag = n-1-j tokens before the end of its
+    worker's own block (the last entry of a combined view): it equals decode
+    on the same view with that block shortened by lag."""
+    rng = np.random.default_rng(41)
+    D, Hkv, Hq, theta, n = 16, 2, 4, 1e4, 5
+    starts = np.array([0, 64, 96], np.int64)
+    lens = np.array([40, 11, 14], np.int32)
+    K = rng.standard_normal((Hkv, 128, D))
+    V = rng.standard_normal((Hkv, 128, D))
+    q = rng.standard_normal((2, n, Hq, D))
+    tb, to, ne = oracle.build_combined_tables(0, [1, 2], lens)
+    ch, rc = oracle.attn_chunk(form, q, K, V, tb, to, ne, lens, starts, theta)
+    assert rc == 0
+    for w in range(2):
+        for j in range(n):
+            l2 = lens.copy()
+            l2[1 + w] -= n - 1 - j
+            tb2, to2, ne2 = oracle.build_combined_tables(0, [1, 2], l2)
+            ref, rc = oracle.attn_decode(form, q[:, j], K, V, tb2, to2, ne2, l2, starts, theta)
+            assert rc == 0
+            np.testing.assert_allclose(ch[w, j], ref[w], rtol=0, atol=1e-12)
+
+
+def test_chunk_one_block_is_causal_textbook_attention():
+    """One worker, one block at offset 0, the last n tokens as queries: row j
+    is textbook attention with RoPE at absolute positions over tokens
+    0..L-n+j (a causal mask)."""
+    rng = np.random.default_rng(42)
+    D, theta, L, n = 8, 1e4, 30, 6
+    raw = rng.standard_normal((L, D))
+    K = np.stack([rope_complex(raw[t], theta, t) for t in range(L)])[None]  # stored at local t
+    V = rng.standard_normal((1, L + 2, D))
+    K = np.concatenate([K, np.zeros((1, 2, D))], axis=1)
+    q = rng.standard_normal((1, n, 1, D))
+    lens = np.array([L], np.int32)
+    tb, to, ne = np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), np.array([1], np.int32)
+    got, rc = oracle.attn_chunk(1, q, K, V, tb, to, ne, lens, np.array([0], np.int64), theta)
+    assert rc == 0
+    for j in range(n):
+        p = L - n + j
+        Kabs = np.stack([rope_complex(raw[t], theta, t) for t in range(p + 1)])
+        ref = textbook_decode(rope_complex(q[0, j, 0], theta, p), Kabs, V[0, :p + 1])
+        np.testing.assert_allclose(got[0, j, 0], ref, rtol=0, atol=1e-12)
