@@ -147,7 +147,7 @@ hw_status hw_set_tuning(int32_t path, int32_t units_per_head) {
 
 size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t num_q_heads) {
   if (check_pool(pool) != HW_OK) return 0;
-  if (num_workers < 1 || num_workers > HW_MAX_WORKERS || num_q_heads < 1 ||
+  if (num_workers < 1 || num_workers > HW_MAX_ROWS || num_q_heads < 1 ||
       num_q_heads % pool->num_kv_heads != 0)
     return 0;
   const int rows = num_workers * (num_q_heads / pool->num_kv_heads);
@@ -157,10 +157,32 @@ size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t
       .total;
 }
 
+static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                           int32_t nq, int32_t num_q_heads, const hw_entry* tables,
+                           int32_t max_entries, const int32_t* num_entries, double rope_theta,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
                          int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
                          const int32_t* num_entries, double rope_theta, float* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_call(pool, layer, q, num_workers, 1, num_q_heads, tables, max_entries, num_entries,
+                   rope_theta, out, workspace, workspace_bytes, stream);
+}
+
+hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                        int32_t chunk, int32_t num_q_heads, const hw_entry* tables,
+                        int32_t max_entries, const int32_t* num_entries, double rope_theta,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (chunk < 1 || chunk > HW_MAX_ROWS) return HW_ERANGE;
+  return attn_call(pool, layer, q, num_workers, chunk, num_q_heads, tables, max_entries,
+                   num_entries, rope_theta, out, workspace, workspace_bytes, stream);
+}
+
+static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                           int32_t nq, int32_t num_q_heads, const hw_entry* tables,
+                           int32_t max_entries, const int32_t* num_entries, double rope_theta,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
   hw_status st = check_pool(pool);
   if (st != HW_OK) return st;
   if (!q || !tables || !num_entries || !out) return HW_EINVAL;
@@ -170,7 +192,8 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
   if (max_entries < 1 || max_entries > HW_MAX_ENTRIES) return HW_ERANGE;
   if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return HW_EINVAL;
   const int G = num_q_heads / pool->num_kv_heads;
-  const int rows = num_workers * G;
+  if (static_cast<int64_t>(num_workers) * nq * G > HW_MAX_ROWS) return HW_ERANGE;
+  const int rows = num_workers * nq * G;
   if (rows > HW_MAX_ROWS) return HW_ERANGE;
   const int path = select_path(pool, rows);
   if (path == 2 && (pool->dtype != HW_BF16 || rows > 32)) return HW_EUNSUPPORTED;
@@ -213,6 +236,7 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
   a.Hkv = pool->num_kv_heads;
   a.G = G;
   a.R = rows;
+  a.nq = nq;
   a.E = max_entries;
   a.NB = pool->num_blocks;
   a.P = static_cast<int32_t>(P);

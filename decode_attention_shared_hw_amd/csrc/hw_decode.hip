@@ -76,6 +76,14 @@ __device__ __forceinline__ void rope_cos_sin_fx(int64_t delta, uint64_t frac, fl
   *c = __builtin_amdgcn_cosf(fr);
 }
 
+// Stacked rows of kv head g: r = (w * nq + j) * G + (h - g * G) for worker w,
+// query token j < nq and q-head h.  Query j of worker w sits lag = nq - 1 - j
+// positions before the worker's query position i_q (n = 1: the decode query).
+__device__ __forceinline__ int row_worker(const DecodeArgs& a, int r) { return r / (a.G * a.nq); }
+__device__ __forceinline__ int row_lag(const DecodeArgs& a, int r) {
+  return a.nq - 1 - (r / a.G) % a.nq;
+}
+
 // ----------------------------------------------------------------- prologue
 struct Plan {
   int32_t len[HW_MAX_BLOCKS];
@@ -257,6 +265,7 @@ __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan
 struct TileRef {
   int b;          // block
   int valid;      // tokens of the tile inside the block's length
+  int first;      // local position of the tile's first token in its block
   int64_t base;   // element offset of the tile in the kv-head plane
 };
 
@@ -267,6 +276,7 @@ __device__ __forceinline__ TileRef tile_ref(const Plan& p, int nb, int j, int& b
   TileRef r;
   r.b = bcur;
   r.valid = min(kTile, p.len[bcur] - tl * kTile);
+  r.first = tl * kTile;
   r.base = (p.start[bcur] + static_cast<int64_t>(tl) * kTile) * D;
   return r;
 }
@@ -349,10 +359,12 @@ __device__ __forceinline__ void tile_scores(const u32x4 (&kf)[2][D / 32], const 
 }
 
 // Online softmax of one tile's scores and the P.V update of the running
-// (m, l, O^T); tokens at or past `valid` are dropped, their values zeroed.
+// (m, l, O^T).  Row t keeps the tile's tokens up to rowlim[t] (its causal
+// limit, below `valid`); values of tokens at or past `valid` are zeroed.
 template <int D, int NT>
 __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT], u32x4 (&vf)[D / 16],
-                                            const bool (&rowvis)[NT], int valid, int q4,
+                                            const bool (&rowvis)[NT], const int (&rowlim)[NT],
+                                            int valid, int q4,
                                             f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
                                             float (&l_run)[NT]) {
   constexpr int MT = D / 16;
@@ -365,7 +377,7 @@ __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT], u32x4 (&vf
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int tok = 16 * h2 + 4 * q4 + v;
-        sv[4 * h2 + v] = (rowvis[t] && tok < valid) ? sc[h2][t][v] : -INFINITY;
+        sv[4 * h2 + v] = (rowvis[t] && tok <= rowlim[t]) ? sc[h2][t][v] : -INFINITY;
       }
     float mt = sv[0];
 #pragma unroll
@@ -512,10 +524,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       const int bi = y / ((KS / 2) * NT);
       const int b = gb + bi;
       const int r = 16 * t + (ln & 15);
-      const int w = r / a.G;
+      const int w = row_worker(a, r);
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
       const int wc = vis ? w : 0;
-      const int64_t delta = plan.iq[wc] - plan.off[wc * a.NB + b];
+      const int64_t delta = plan.iq[wc] - row_lag(a, r) - plan.off[wc * a.NB + b];
       const float sc = vis ? a.qscale : 0.f;
       const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner block is d0 + HALF
       const u32x4 xv = *reinterpret_cast<const u32x4*>(qs + r * D + d0);
@@ -553,7 +565,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       const int t_hi = min(plan.hi, plan.tile0[ge]);
       int j = t_lo + wave;
       int bcur = gb;
-      TileRef rt = {0, 0, 0};
+      TileRef rt = {0, 0, 0, 0};
       if (j < t_hi) {
         rt = tile_ref<D>(plan, a.NB, j, bcur);
         const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
@@ -568,6 +580,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       __syncthreads();
       if (j < t_hi) {
         int qb = -1;
+        int rowend[NT];
         const bf16x8* qf = qfs;
         for (;;) {
           if (rt.b != qb) {
@@ -576,14 +589,22 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const int r = 16 * t + li;
-              rowvis[t] = r < a.R && ((plan.vis[qb] >> (r / a.G)) & 1u);
+              const int w = row_worker(a, r);
+              rowvis[t] = r < a.R && ((plan.vis[qb] >> w) & 1u);
+              // last local position row r may see in this block (causal limit)
+              rowend[t] = rowvis[t]
+                              ? static_cast<int>(plan.iq[w] - row_lag(a, r) - plan.off[w * a.NB + qb])
+                              : -1;
             }
           }
+          int rowlim[NT];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) rowlim[t] = min(rt.valid - 1, rowend[t] - rt.first);
           f32x4 sc[2][NT];
           const int jn = j + NWAVE;
           if (jn >= t_hi) {
             tile_scores<D, NT>(kf, qf, lane, sc);
-            tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
+            tile_update<D, NT>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
             break;
           }
           const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
@@ -592,7 +613,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
           __builtin_amdgcn_sched_barrier(0);
           load_keys<D>(krs, tn, koff, kf);
           __builtin_amdgcn_sched_barrier(0);
-          tile_update<D, NT>(sc, vf, rowvis, rt.valid, q4, acc, m_run, l_run);
+          tile_update<D, NT>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
           __builtin_amdgcn_sched_barrier(0);
           load_values<D>(vrs, tn, voff, vf);
           __builtin_amdgcn_sched_barrier(0);
@@ -824,10 +845,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       const int r = (x / half) % RM;
       const int bi = x / (half * RM);
       const int b = gb + bi;
-      const int w = r / a.G;
+      const int w = row_worker(a, r);
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
       float c = 0.f, s = 0.f;
-      if (vis) rope_cos_sin(plan.iq[w] - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
+      if (vis) rope_cos_sin(plan.iq[w] - row_lag(a, r) - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
       const float x0 = qs[r * D + i], x1 = qs[r * D + i + half];
       float* dst = ubuf + bi * kQBlock + r * D;
       dst[i] = vis ? (x0 * c - x1 * s) * a.qscale : 0.f;
@@ -860,8 +881,18 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
         }
   };
 
+  // last local position of block b that row rg*RG+i may see (-1: none)
+  auto row_ends = [&](int b, int (&rowend)[RG]) {
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int r = rg * RG + i;
+      const int w = row_worker(a, r);
+      const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
+      rowend[i] = vis ? static_cast<int>(plan.iq[w] - row_lag(a, r) - plan.off[w * a.NB + b]) : -1;
+    }
+  };
   auto compute = [&](const u32x4 (&kc)[KC], const u32x4 (&vc)[DPL][4][VC], const float* qblk,
-                     uint32_t vismask, int valid) {
+                     const int (&rowend)[RG], int valid, int first) {
     // ---- scores of rows rg*RG+i against token tl, into the P buffer (the
     // row loop stays rolled so the queries are read from LDS as they are used)
     float kv[D];
@@ -887,7 +918,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       const int r = rg * RG + i;
-      const bool ok = tl < valid && r < a.R && ((vismask >> (r / a.G)) & 1u);
+      const bool ok = tl <= min(valid - 1, rowend[i] - first);
       const float sv = ok ? pbuf[r * PS + tl] : -INFINITY;
       const float mt = half_max(sv);
       const float mn = fmaxf(m_run[i], mt);
@@ -946,7 +977,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       const int t_hi = min(plan.hi, plan.tile0[ge]);
       int j = t_lo + wave;
       int bcur = gb;
-      TileRef rt = {0, 0, 0};
+      TileRef rt = {0, 0, 0, 0};
       u32x4 kc[KC], vc[DPL][4][VC];
       if (j < t_hi) {
         rt = tile_ref<D>(plan, a.NB, j, bcur);
@@ -961,16 +992,17 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       if (j < t_hi) {
         for (;;) {
           const float* qblk = ubuf + (rt.b - gb) * kQBlock;
-          const uint32_t vismask = plan.vis[rt.b];
+          int rowend[RG];
+          row_ends(rt.b, rowend);
           const int jn = j + NWAVE;
           if (jn >= t_hi) {
-            compute(kc, vc, qblk, vismask, rt.valid);
+            compute(kc, vc, qblk, rowend, rt.valid, rt.first);
             break;
           }
           const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
           const uint32_t tn =
               __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * sizeof(T)));
-          compute(kc, vc, qblk, vismask, rt.valid);
+          compute(kc, vc, qblk, rowend, rt.valid, rt.first);
           load_k(tn, kc);
           load_v(tn, vc);
           j = jn;

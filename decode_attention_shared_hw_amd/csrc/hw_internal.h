@@ -60,6 +60,7 @@ struct alignas(16) DecodeArgs {
   int64_t plane_elems;      // num_slots * D
   int32_t plane_bytes;      // plane_elems * element size (< 2^31)
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
+  int32_t nq;               // query tokens per worker (1: decode); rows are (w*nq + j)*G + h
   int32_t dtype;            // HW_F32 / HW_BF16
   int32_t xcd_map;          // 1: map consecutive work units to one XCD
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain

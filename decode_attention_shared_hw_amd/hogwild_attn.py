@@ -55,7 +55,7 @@ class hw_pool(ctypes.Structure):
 
 
 EXPORTED = [
-    "hw_abi_version", "hw_status_str", "hw_attn_workspace_bytes", "hw_attn_decode",
+    "hw_abi_version", "hw_status_str", "hw_attn_workspace_bytes", "hw_attn_decode", "hw_attn_chunk",
     "hw_block_append", "hw_block_reset", "hw_block_advance", "hw_block_write",
     "hw_build_combined_tables", "hw_build_view_tables", "hw_pool_status", "hw_set_tuning",
 ]
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.hw_attn_workspace_bytes.argtypes = [PP, i32, i32]
         L.hw_attn_decode.restype = i32
         L.hw_attn_decode.argtypes = [PP, i32, P, i32, i32, P, i32, P, d, P, P, sz, P]
+        L.hw_attn_chunk.restype = i32
+        L.hw_attn_chunk.argtypes = [PP, i32, P, i32, i32, i32, P, i32, P, d, P, P, sz, P]
         L.hw_block_append.restype = i32
         L.hw_block_append.argtypes = [PP, i32, i32, d, P]
         L.hw_block_reset.restype = i32
@@ -209,6 +211,19 @@ def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor
                                 int(tables.shape[1]), _ptr(num_entries), float(rope_theta),
                                 _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(code, "hw_attn_decode")
+
+
+def hw_attn_chunk(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
+                  num_entries: torch.Tensor, rope_theta: float, out: torch.Tensor,
+                  workspace: torch.Tensor, stream=None):
+    """q [W][n][Hq][D] (pool dtype): each worker's last n tokens as queries, causal over the
+    view; out fp32 [W][n][Hq][D]; workspace sized for W * n workers."""
+    W, n, Hq, _ = q.shape
+    code = lib().hw_attn_chunk(ctypes.byref(pool.desc), int(layer), _ptr(q), W, n, Hq,
+                               _ptr(tables), int(tables.shape[1]), _ptr(num_entries),
+                               float(rope_theta), _ptr(out), _ptr(workspace), workspace.numel(),
+                               _stream(stream))
+    _check(code, "hw_attn_chunk")
 
 
 def hw_block_append(pool: Pool, src_block: int, dst_block: int, rope_theta: float, stream=None):

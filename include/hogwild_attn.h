@@ -135,8 +135,13 @@ const char* hw_status_str(hw_status status);
 
 /*
  * Bytes of device workspace hw_attn_decode needs for this pool and call
- * shape under the current tuning (split partials for the log-sum-exp merge).
- * Returns 0 if the shape is invalid.  The workspace needs no initialisation.
+ * shape under the current tuning: split partials for the log-sum-exp merge
+ * and per-wave first-tile hints (the tiles the previous call started with,
+ * requested before the plan is known and verified against it).  For
+ * hw_attn_chunk pass num_workers * chunk.  Returns 0 if the shape is invalid
+ * (more than HW_MAX_ROWS stacked rows).  The workspace needs no
+ * initialisation, and one workspace serves any sequence of calls on one
+ * stream; calls that may overlap need distinct workspaces.
  */
 size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t num_q_heads);
 
@@ -163,6 +168,25 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
                          int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
                          const int32_t* num_entries, double rope_theta, float* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-token query chunk: every worker attends with its last `chunk` tokens
+ * at once (a prompt injected into, or a header prefilled in, its own block,
+ * whose K/V are already stored).  Query j of worker w sits at view position
+ * i_q[w] - (chunk - 1 - j) and sees the view's tokens at positions up to its
+ * own (a causal mask over the view); chunk = 1 is hw_attn_decode.
+ *   q    (device) [num_workers][chunk][num_q_heads][head_dim], pool dtype.
+ *   out  (device) [num_workers][chunk][num_q_heads][head_dim] fp32.
+ *   workspace: hw_attn_workspace_bytes(pool, num_workers * chunk, num_q_heads).
+ * Other arguments, errors and limits as hw_attn_decode, with
+ * num_workers * chunk * (num_q_heads / num_kv_heads) <= HW_MAX_ROWS
+ * (HW_ERANGE otherwise, or for chunk < 1).  Rows that see no token are zero
+ * and set HW_DEV_NO_TOKENS.
+ */
+hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                        int32_t chunk, int32_t num_q_heads, const hw_entry* tables,
+                        int32_t max_entries, const int32_t* num_entries, double rope_theta,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Step completion (key design 2: a finished step's KV is rotated and moved

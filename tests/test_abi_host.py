@@ -175,3 +175,15 @@ def test_view_tables_host_validation(lib):
     cast = ctypes.cast(wb, ctypes.c_void_p)
     assert lib.hw_build_view_tables(P, 3, 2, 0, cast, p, p, None) == hw.HW_EINVAL
     assert lib.hw_build_view_tables(P, -1, 2, 0, cast, p, p, None) == hw.HW_EINVAL
+
+
+def test_chunk_host_validation(lib):
+    pool = FakePool()
+    P = ctypes.byref(pool.desc)
+    p = ctypes.c_void_p(0x5000)
+    call = lambda W, n, Hq: lib.hw_attn_chunk(P, 0, p, W, n, Hq, p, 3, p, 1e4, p, p, 1 << 30, None)
+    assert call(2, 0, 4) == hw.HW_ERANGE          # chunk < 1
+    assert call(2, 17, 4) == hw.HW_ERANGE         # 2 * 17 * 2 rows > 64
+    assert call(2, 16, 3) == hw.HW_EINVAL         # Hq % Hkv
+    assert lib.hw_attn_workspace_bytes(P, 64, 2) > 0      # 64 stacked rows (chunk of 64, G = 1)
+    assert lib.hw_attn_workspace_bytes(P, 65, 2) == 0

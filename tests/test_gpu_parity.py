@@ -376,6 +376,50 @@ def test_interleaved_layout_attention_matches_oracle(path):
     assert_close(got, ref, torch.bfloat16, f"interleaved path {path}")
 
 
+# --------------------------------------------- multi-token query chunks (NEXT-3)
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", [
+    # (W, n, Hq, Hkv, D, lens): rows = W * n * Hq / Hkv
+    (2, 4, 4, 2, 128, [900, 70, 45]),
+    (4, 8, 8, 8, 64, [300, 9, 33, 64, 1]),        # chunk longer than some own blocks
+    (1, 16, 16, 4, 128, [2048, 100]),            # 64 rows: VALU only
+    (2, 3, 40, 8, 128, [4000, 333, 517]),        # QwQ heads, 30 rows
+])
+def test_chunk_matches_oracle(path, case):
+    W, n, Hq, Hkv, D, lens = case
+    hw.hw_set_tuning(path, 0)
+    wl = _custom(W, Hq, Hkv, D, lens)
+    if path == hw.PATH_MFMA and W * n * (Hq // Hkv) > 32:
+        pytest.skip("MFMA path holds at most 32 rows")
+    s = Setup(wl, poison_unused=True)
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(W, n, Hq, D, generator=g).to(wl.dtype)
+    out = torch.full((W, n, Hq, D), float("nan"), device="cuda")
+    ws = hw.alloc_workspace(s.pool, W * n, Hq)
+    hw.hw_attn_chunk(s.pool, 0, q.cuda(), s.tables, s.num_entries, wl.theta, out, ws)
+    torch.cuda.synchronize()
+    tb, to, ne = s.oracle_tables()
+    ref, rc = oracle.attn_chunk(oracle.FORM_METHOD, q.double().numpy(), s.K[0].double().numpy(),
+                                s.V[0].double().numpy(), tb, to, ne, np.array(lens, np.int32),
+                                np.asarray(s.pool.block_start, np.int64), wl.theta)
+    assert rc == 0
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, torch.bfloat16, f"chunk {case} path {path}")
+    assert hw.hw_pool_status(s.pool) == 0
+
+
+def test_chunk_of_one_equals_decode():
+    wl = _custom(4, 40, 8, 128, [2000, 300, 31, 64, 5])
+    s = Setup(wl)
+    dec = s.decode()
+    out = torch.zeros(wl.W, 1, wl.Hq, wl.D, device="cuda")
+    hw.hw_attn_chunk(s.pool, 0, s.q[0][:, None].contiguous().cuda(), s.tables, s.num_entries,
+                     wl.theta, out, s.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy()[:, 0], dec)
+
+
 # ------------------------------------------------------- token write (NEXT-1)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_token_write_matches_oracle_bit_exact(dtype):
