@@ -469,8 +469,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   const uint32_t spec = *hint;  // uniform: a scalar load
   u32x4 kf[2][KS], vf[MT];
   {
-    // the plan's and the query's loads go first: loads complete in issue
-    // order, so the plan can consume them while the tile is still in flight
     auto issue = [&] {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
@@ -483,9 +481,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
               *reinterpret_cast<const u32x4*>(qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      load_tile_checked<D>(krs, vrs, spec, koff, voff, kf, vf);
-      __builtin_amdgcn_sched_barrier(0);
     };
     auto commit = [&] {
 #pragma unroll
@@ -493,6 +488,11 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         const int x = tid + k * NTHR;
         if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
       }
+      // the speculative tile once the plan's own loads are back, so that its
+      // traffic does not queue ahead of them
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile_checked<D>(krs, vrs, spec, koff, voff, kf, vf);
+      __builtin_amdgcn_sched_barrier(0);
     };
     build_plan<NTHR>(a, plan, issue, commit);
   }
