@@ -243,9 +243,6 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   a.D = pool->head_dim;
   a.dtype = pool->dtype;
   const int64_t grid = P * pool->num_kv_heads;
-  // Work units stay in dispatch order (each head spread over all 8 XCDs):
-  // measured slightly faster than keeping a head's units on one XCD.
-  a.xcd_map = 0;
   a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
   for (int b = 0; b < pool->num_blocks; ++b) {
     a.tab.block_start[b] = pool->block_start[b];

@@ -39,6 +39,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -79,10 +87,8 @@ __device__ __forceinline__ void rope_cos_sin_fx(int64_t delta, uint64_t frac, fl
 // Stacked rows of kv head g: r = (w * nq + j) * G + (h - g * G) for worker w,
 // query token j < nq and q-head h.  Query j of worker w sits lag = nq - 1 - j
 // positions before the worker's query position i_q (n = 1: the decode query).
-__device__ __forceinline__ int row_worker(const DecodeArgs& a, int r) { return r / (a.G * a.nq); }
-__device__ __forceinline__ int row_lag(const DecodeArgs& a, int r) {
-  return a.nq - 1 - (r / a.G) % a.nq;
-}
+// The plan holds each row's worker and lag (row_w, row_lag), so the kernels
+// divide by G and nq once.
 
 // ----------------------------------------------------------------- prologue
 struct Plan {
@@ -90,6 +96,8 @@ struct Plan {
   uint32_t vis[HW_MAX_BLOCKS];        // bit w set: worker w sees block b
   int32_t tile0[HW_MAX_BLOCKS + 1];   // tiles of visible blocks, prefix sums
   long long iq[HW_MAX_WORKERS];       // query position per worker, -1: none
+  int32_t row_w[HW_MAX_ROWS];         // worker of each stacked row (0 past R)
+  int32_t row_lag[HW_MAX_ROWS];       // positions before i_q of each row's query
   int32_t off[HW_MAX_WORKERS * HW_MAX_BLOCKS];
   int64_t start[HW_MAX_BLOCKS];       // first slot of each block
   double invf[kMaxHalf];              // theta^(-2i/D)
@@ -113,124 +121,128 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
-// Every global load of the prologue is issued before its first barrier, so
-// the plan costs one memory round trip.  Each thread keeps up to kEntryRegs
-// table entries in registers between the load and the visibility pass.
-// issue(): the kernel's own loads, issued with the plan's; commit(): their
-// LDS stores, run before the first barrier.
-template <int NTHR>
-constexpr int entry_regs() { return (HW_MAX_WORKERS * HW_MAX_ENTRIES + NTHR - 1) / NTHR; }
-static_assert(kTablesVec <= kThreads, "per-call arrays exceed one vector per thread");
-
+// Workgroup -> (kv head, work unit): the units of a head are consecutive
+// workgroups.
 __device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, int* unit) {
-  int lin = blockIdx.x;
-  if (a.xcd_map) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  *head = lin / a.P;
-  *unit = lin - *head * a.P;
+  *head = blockIdx.x / a.P;
+  *unit = blockIdx.x - *head * a.P;
 }
 
+// Table entry i (worker i / E, slot i % E): marks its block visible to the
+// worker and records the view offset.  A malformed table (entry count out of
+// range, block id out of range, a block listed twice) marks its worker bad.
+__device__ __forceinline__ void plan_entry(const DecodeArgs& a, Plan& p, int i, hw_entry e,
+                                           int ne) {
+  const int w = i / a.E, slot = i - w * a.E;
+  const uint32_t bit = 1u << w;
+  if (ne < 0 || ne > a.E) {
+    atomicOr(&p.bad_workers, bit);
+    return;
+  }
+  if (slot >= ne) return;
+  const int b = e.block_id;
+  if (b < 0 || b >= a.NB) {
+    atomicOr(&p.bad_workers, bit);
+    return;
+  }
+  if (atomicOr(&p.vis[b], bit) & bit) atomicOr(&p.bad_workers, bit);
+  p.off[w * a.NB + b] = e.view_offset;
+}
+
+// The plan costs one memory round trip: every global load is issued before
+// the first wait.  A kernel's code is fetched cold at every launch, so the
+// prologue is kept short and rolled: block-level work runs on wave 0 with one
+// lane per block, table entries on one thread each.
+// issue(): the kernel's own loads, issued with the plan's; commit(): their
+// LDS stores, run once they have arrived.
 template <int NTHR, typename Issue, typename Commit>
 __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
-  constexpr int kEntryRegs = entry_regs<NTHR>();
   const int tid = threadIdx.x;
   const int WE = a.W * a.E;
-  // ---- loads (independent, all in flight together)
-  const int len_raw = tid < a.NB ? a.block_len[tid] : 0;
-  u32x4 tabv = u32x4{0u, 0u, 0u, 0u};
-  if (tid < kTablesVec) tabv = reinterpret_cast<const u32x4*>(&a.tab)[tid];
-  hw_entry ent[kEntryRegs];
-  int ent_ne[kEntryRegs];
-#pragma unroll
-  for (int k = 0; k < kEntryRegs; ++k) {
-    const int i = tid + k * NTHR;
-    ent[k].block_id = -1;
-    ent[k].view_offset = 0;
-    ent_ne[k] = 0;
-    if (i < WE) {
-      ent[k] = a.tables[i];
-      ent_ne[k] = a.num_entries[i / a.E];
-    }
+  // ---- loads: per block (lanes of wave 0) length, capacity and first slot;
+  // per frequency its two forms; one table entry per thread.  The per-call
+  // arrays are read from the kernel-argument segment through a pointer
+  // (indexing the argument itself would copy it to scratch).
+  const char* tabp = reinterpret_cast<const char*>(&a.tab);
+  int len = 0, cap = 0;
+  int64_t start = 0;
+  if (tid < a.NB) {
+    len = a.block_len[tid];
+    cap = reinterpret_cast<const int32_t*>(tabp + offsetof(DecodeTables, block_cap))[tid];
+    start = reinterpret_cast<const int64_t*>(tabp + offsetof(DecodeTables, block_start))[tid];
+  }
+  double invf = 0.0;
+  uint64_t frac = 0u;
+  if (tid < a.D / 2) {
+    invf = reinterpret_cast<const double*>(tabp + offsetof(DecodeTables, inv_freq))[tid];
+    frac = reinterpret_cast<const uint64_t*>(tabp + offsetof(DecodeTables, rope_frac))[tid];
+  }
+  hw_entry ent = {-1, 0};
+  int ne = 0;
+  if (tid < WE) {
+    ent = a.tables[tid];
+    ne = a.num_entries[tid / a.E];
   }
   issue();
-  // ---- phase A: zeroed state, copied per-call arrays
-  __shared__ DecodeTables tab;
+  // ---- state that needs none of the loads
+  if (tid < a.NB) p.vis[tid] = 0u;
+  if (tid < a.W) p.iq[tid] = -1;
+  if (tid < HW_MAX_ROWS) {
+    const bool row = tid < a.R;
+    p.row_w[tid] = row ? tid / (a.G * a.nq) : 0;
+    p.row_lag[tid] = row ? a.nq - 1 - (tid / a.G) % a.nq : 0;
+  }
+  for (int i = tid; i < a.W * a.NB; i += NTHR) p.off[i] = 0;
   if (tid == 0) {
     p.flags = 0;
     p.bad_workers = 0u;
     plan_head_unit(a, &p.head, &p.unit);
   }
-  if (tid < kTablesVec) reinterpret_cast<u32x4*>(&tab)[tid] = tabv;
-  if (tid < a.NB) p.vis[tid] = 0u;
-  if (tid < a.W) p.iq[tid] = -1;
-  for (int i = tid; i < a.W * a.NB; i += NTHR) p.off[i] = 0;
+  __syncthreads();
+  // ---- visibility and view offsets from the tables
   commit();
-  __syncthreads();
-  // ---- phase B: lengths, visibility and view offsets from the tables
-  if (tid < a.NB) {
-    int len = len_raw;
-    if (len < 0 || len > tab.block_cap[tid]) {
-      atomicOr(&p.flags, HW_DEV_BAD_LENGTH);
-      len = 0;
-    }
-    p.len[tid] = len;
-    p.start[tid] = tab.block_start[tid];
-  }
+  if (tid < WE) plan_entry(a, p, tid, ent, ne);
+#pragma unroll 1
+  for (int i = tid + NTHR; i < WE; i += NTHR) plan_entry(a, p, i, a.tables[i], a.num_entries[i / a.E]);
   if (tid < a.D / 2) {
-    p.invf[tid] = tab.inv_freq[tid];
-    p.rope_frac[tid] = tab.rope_frac[tid];
+    p.invf[tid] = invf;
+    p.rope_frac[tid] = frac;
   }
-#pragma unroll
-  for (int k = 0; k < kEntryRegs; ++k) {
-    const int i = tid + k * NTHR;
-    if (i >= WE) continue;
-    const int w = i / a.E, e = i - w * a.E;
-    const int ne = ent_ne[k];
-    if (ne < 0 || ne > a.E) {
-      atomicOr(&p.bad_workers, 1u << w);
-      continue;
-    }
-    if (e >= ne) continue;
-    const int b = ent[k].block_id;
-    if (b < 0 || b >= a.NB) {
-      atomicOr(&p.bad_workers, 1u << w);
-      continue;
-    }
-    const uint32_t old = atomicOr(&p.vis[b], 1u << w);
-    if (old & (1u << w)) atomicOr(&p.bad_workers, 1u << w);
-    p.off[w * a.NB + b] = ent[k].view_offset;
-  }
+  if (tid < a.NB) p.start[tid] = start;
   __syncthreads();
-  if (p.bad_workers) {
-    // a worker with a malformed table sees nothing: its rows come out as zeros
-    if (tid < a.NB) p.vis[tid] &= ~p.bad_workers;
-    if (tid == 0) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
-    __syncthreads();
-  }
-  // ---- phase C: query positions (entry-parallel max) and the tile split
-  // (one wave scans the blocks)
-#pragma unroll
-  for (int k = 0; k < kEntryRegs; ++k) {
-    const int i = tid + k * NTHR;
-    if (i >= WE) continue;
-    const int w = i / a.E, e = i - w * a.E;
-    if (e >= ent_ne[k] || ((p.bad_workers >> w) & 1u)) continue;
-    const int b = ent[k].block_id;
-    if (p.len[b] > 0)
-      atomicMax(&p.iq[w], static_cast<long long>(ent[k].view_offset) + p.len[b] - 1);
-  }
-  if (tid >= 64 && tid < 128) {
-    // one wave scans the blocks (NB <= 64, one per lane)
-    const int b = tid - 64;
+  // ---- wave 0, lane b = block b: checked length, visibility without the
+  // bad workers, the tile prefix over the visible blocks, and each worker's
+  // query position (the last position of any block it sees)
+  if (tid < 64) {
+    const int b = tid;
     int v = 0;
-    if (b < a.NB && p.vis[b] != 0u && p.len[b] > 0) v = (p.len[b] + kTile - 1) / kTile;
+    if (b < a.NB) {
+      if (len < 0 || len > cap) {
+        atomicOr(&p.flags, HW_DEV_BAD_LENGTH);
+        len = 0;
+      }
+      const uint32_t vis = p.vis[b] & ~p.bad_workers;
+      p.vis[b] = vis;
+      p.len[b] = len;
+      if (vis != 0u && len > 0) {
+        v = (len + kTile - 1) / kTile;
+#pragma unroll 1
+        for (uint32_t m = vis; m != 0u; m &= m - 1u) {
+          const int w = __builtin_ctz(m);
+          atomicMax(&p.iq[w], static_cast<long long>(p.off[w * a.NB + b]) + len - 1);
+        }
+      }
+    }
     const int incl = wave_inclusive_scan(v);
-    if (b < a.NB) p.tile0[b] = incl - v;
     const int nt = __builtin_amdgcn_readlane(incl, 63);
+    if (b < a.NB) p.tile0[b] = incl - v;
     if (b == 0) {
       p.tile0[a.NB] = nt;
-      const int64_t n = nt;
-      p.lo = static_cast<int>(n * p.unit / a.P);
-      p.hi = static_cast<int>(n * (p.unit + 1) / a.P);
+      // n * (unit + 1) < 2^31: a plane holds under 2^31 bytes, so under 2^18
+      // tiles, and there are at most kMaxUnits units
+      p.lo = static_cast<int>(static_cast<uint32_t>(nt * p.unit) / static_cast<uint32_t>(a.P));
+      p.hi = static_cast<int>(static_cast<uint32_t>(nt * (p.unit + 1)) / static_cast<uint32_t>(a.P));
+      if (p.bad_workers) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
     }
   }
   __syncthreads();
@@ -516,6 +528,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   bf16x8* qfs = reinterpret_cast<bf16x8*>(ubuf);
   auto rotate_blocks = [&](int gb, int ge) {
     const int items = (ge - gb) * NT * (KS / 2) * 64;
+#pragma unroll 1
     for (int x = tid; x < items; x += NTHR) {
       const int ln = x & 63;
       const int y = x >> 6;
@@ -524,27 +537,28 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       const int bi = y / ((KS / 2) * NT);
       const int b = gb + bi;
       const int r = 16 * t + (ln & 15);
-      const int w = row_worker(a, r);
+      const int w = plan.row_w[r];
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
       const int wc = vis ? w : 0;
-      const int64_t delta = plan.iq[wc] - row_lag(a, r) - plan.off[wc * a.NB + b];
+      const int64_t delta = plan.iq[wc] - plan.row_lag[r] - plan.off[wc * a.NB + b];
       const float sc = vis ? a.qscale : 0.f;
       const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner block is d0 + HALF
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(qs + r * D + d0);
-      const u32x4 yv = *reinterpret_cast<const u32x4*>(qs + r * D + d0 + HALF);
-      bf16x8 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t xw = xv[e >> 1], yw = yv[e >> 1];
-        const float x0 = __uint_as_float((e & 1) ? (xw & 0xffff0000u) : (xw << 16));
-        const float y0 = __uint_as_float((e & 1) ? (yw & 0xffff0000u) : (yw << 16));
-        float c, sn;
-        rope_cos_sin_fx(delta, plan.rope_frac[d0 + e], &c, &sn);
-        lo[e] = static_cast<__bf16>((x0 * c - y0 * sn) * sc);
-        hi[e] = static_cast<__bf16>((y0 * c + x0 * sn) * sc);
+      // two dims per step: bf16 pairs (x, x+1) of the first half and their
+      // partners in the second half, rotated and stored as one 32-bit word each
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
+      uint32_t* lo = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh) * 64 + ln);
+      uint32_t* hi = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh + KS / 2) * 64 + ln);
+#pragma unroll 1
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t xw = qw[e2], yw = qw[e2 + HALF / 2];
+        const float x0 = __uint_as_float(xw << 16), x1 = __uint_as_float(xw & 0xffff0000u);
+        const float y0 = __uint_as_float(yw << 16), y1 = __uint_as_float(yw & 0xffff0000u);
+        float c0, s0, c1, s1;
+        rope_cos_sin_fx(delta, plan.rope_frac[d0 + 2 * e2], &c0, &s0);
+        rope_cos_sin_fx(delta, plan.rope_frac[d0 + 2 * e2 + 1], &c1, &s1);
+        lo[e2] = pack_bf16x2((x0 * c0 - y0 * s0) * sc, (x1 * c1 - y1 * s1) * sc);
+        hi[e2] = pack_bf16x2((y0 * c0 + x0 * s0) * sc, (y1 * c1 + x1 * s1) * sc);
       }
-      qfs[((bi * NT + t) * KS + sh) * 64 + ln] = lo;
-      qfs[((bi * NT + t) * KS + sh + KS / 2) * 64 + ln] = hi;
     }
   };
 
@@ -589,11 +603,11 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const int r = 16 * t + li;
-              const int w = row_worker(a, r);
+              const int w = plan.row_w[r];
               rowvis[t] = r < a.R && ((plan.vis[qb] >> w) & 1u);
               // last local position row r may see in this block (causal limit)
               rowend[t] = rowvis[t]
-                              ? static_cast<int>(plan.iq[w] - row_lag(a, r) - plan.off[w * a.NB + qb])
+                              ? static_cast<int>(plan.iq[w] - plan.row_lag[r] - plan.off[w * a.NB + qb])
                               : -1;
             }
           }
@@ -845,10 +859,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       const int r = (x / half) % RM;
       const int bi = x / (half * RM);
       const int b = gb + bi;
-      const int w = row_worker(a, r);
+      const int w = plan.row_w[r];
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
       float c = 0.f, s = 0.f;
-      if (vis) rope_cos_sin(plan.iq[w] - row_lag(a, r) - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
+      if (vis) rope_cos_sin(plan.iq[w] - plan.row_lag[r] - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
       const float x0 = qs[r * D + i], x1 = qs[r * D + i + half];
       float* dst = ubuf + bi * kQBlock + r * D;
       dst[i] = vis ? (x0 * c - x1 * s) * a.qscale : 0.f;
@@ -886,9 +900,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       const int r = rg * RG + i;
-      const int w = row_worker(a, r);
+      const int w = plan.row_w[r];
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
-      rowend[i] = vis ? static_cast<int>(plan.iq[w] - row_lag(a, r) - plan.off[w * a.NB + b]) : -1;
+      rowend[i] = vis ? static_cast<int>(plan.iq[w] - plan.row_lag[r] - plan.off[w * a.NB + b]) : -1;
     }
   };
   auto compute = [&](const u32x4 (&kc)[KC], const u32x4 (&vc)[DPL][4][VC], const float* qblk,

@@ -33,16 +33,14 @@ __host__ __device__ inline int64_t value_offset(int64_t slot, int d, int D) {
   return tile * 32 * D + ((t & 15) >> 2) * 8 * D + d * 8 + ((t >> 4) << 2) + (t & 3);
 }
 
-// Per-call arrays of the decode kernels, copied into LDS at kernel start with
-// one 16-byte vector load per thread (dynamic indexing of kernel arguments
-// would otherwise cost one serialized memory round trip per array).
+// Per-call arrays of the decode kernels, passed in the kernel arguments and
+// read at kernel start with one load per array element per thread.
 struct alignas(16) DecodeTables {
   int64_t block_start[HW_MAX_BLOCKS];
   int32_t block_cap[HW_MAX_BLOCKS];
   double inv_freq[kMaxHalf];  // theta^(-2i/D), i < D/2
   uint64_t rope_frac[kMaxHalf];  // frac(theta^(-2i/D) / (2 pi)) * 2^64, i < D/2
 };
-constexpr int kTablesVec = static_cast<int>(sizeof(DecodeTables) / 16);
 
 // Kernel arguments of the fused decode kernels (passed by value).
 struct alignas(16) DecodeArgs {
@@ -62,7 +60,6 @@ struct alignas(16) DecodeArgs {
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
   int32_t nq;               // query tokens per worker (1: decode); rows are (w*nq + j)*G + h
   int32_t dtype;            // HW_F32 / HW_BF16
-  int32_t xcd_map;          // 1: map consecutive work units to one XCD
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
   DecodeTables tab;
 };
