@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "hogwild_oracle.cpp")
 _LIB = os.path.join(_HERE, "libhogwild_oracle.so")
 
 HWO_OK, HWO_EINVAL, HWO_ENOTOKENS, HWO_ECAPACITY = 0, 1, 2, 3
-HWO_F32, HWO_BF16 = 0, 1
+HWO_F32, HWO_BF16, HWO_FP8 = 0, 1, 2
 FORM_DEFINITION, FORM_METHOD = 0, 1
 
 
@@ -52,6 +52,10 @@ def lib():
         L.hwo_round_bf16.argtypes = [d]
         L.hwo_round_f32.restype = d
         L.hwo_round_f32.argtypes = [d]
+        L.hwo_e4m3_value.restype = d
+        L.hwo_e4m3_value.argtypes = [i32]
+        L.hwo_round_e4m3.restype = d
+        L.hwo_round_e4m3.argtypes = [d]
         L.hwo_rope.restype = None
         L.hwo_rope.argtypes = [P, i32, d, d, P]
         L.hwo_build_combined_tables.restype = i32
@@ -64,14 +68,14 @@ def lib():
         L.hwo_attn_decode.argtypes = [i32, i32, i32, i32, i32, d, i32, P, P, P, i32, P, P,
                                       i64, P, P, P, P]
         L.hwo_block_append.restype = i32
-        L.hwo_block_append.argtypes = [i32, i32, i32, i64, P, P, i32, P, P, P, i32, i32, d, i32]
+        L.hwo_block_append.argtypes = [i32, i32, i32, i64, P, P, i32, P, P, P, i32, i32, d, i32, P]
         L.hwo_attn_chunk.restype = i32
         L.hwo_attn_chunk.argtypes = [i32, i32, i32, i32, i32, i32, d, i32, P, P, P, i32, P, P, i64,
                                      P, P, P, P]
         L.hwo_build_interleaved_tables.restype = i32
         L.hwo_build_interleaved_tables.argtypes = L.hwo_build_combined_tables.argtypes
         L.hwo_block_write.restype = i32
-        L.hwo_block_write.argtypes = [i32, i32, i64, P, P, i32, P, P, i32, P, P, P, d, i32]
+        L.hwo_block_write.argtypes = [i32, i32, i64, P, P, i32, P, P, i32, P, P, P, d, i32, P, P]
         _lib = L
     return _lib
 
@@ -90,6 +94,23 @@ def round_bf16(x: float) -> float:
 
 def round_f32(x: float) -> float:
     return lib().hwo_round_f32(float(x))
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code (0..255)."""
+    return lib().hwo_e4m3_value(int(code))
+
+
+def round_e4m3(x: float) -> float:
+    """Nearest OCP FP8 E4M3 value (ties to even, saturating at +-448)."""
+    return lib().hwo_round_e4m3(float(x))
+
+
+def _scales(s):
+    if s is None:
+        return None, None
+    a = _c(s, np.float64).reshape(-1)
+    return a, _p(a)
 
 
 def rope(x, theta: float, pos: float) -> np.ndarray:
@@ -193,22 +214,25 @@ def attn_chunk(form, q, K, V, tbl_block, tbl_off, num_entries, block_len, block_
                               _p(V), _p(out))
     return out, rc
 
-def block_append(K, V, block_start, block_cap, block_len, src, dst, theta, dtype):
-    """In place on float64 arrays K, V [L][Hkv][num_slots][D] and int32 block_len.  Returns rc."""
+def block_append(K, V, block_start, block_cap, block_len, src, dst, theta, dtype, k_scale=None):
+    """In place on float64 arrays K, V [L][Hkv][num_slots][D] and int32 block_len.  Returns rc.
+    FP8 pools: K, V hold code * scale and k_scale is [L][Hkv]."""
     assert K.dtype == np.float64 and K.flags.c_contiguous
     assert V.dtype == np.float64 and V.flags.c_contiguous
     assert block_len.dtype == np.int32 and block_len.flags.c_contiguous
     bs = _c(block_start, np.int64)
     bc = _c(block_cap, np.int32)
     L, Hkv, S, D = K.shape
+    ks, ksp = _scales(k_scale)
     return lib().hwo_block_append(L, Hkv, D, S, _p(K), _p(V), bl_n(block_len), _p(bs), _p(bc),
-                                  _p(block_len), int(src), int(dst), float(theta), int(dtype))
+                                  _p(block_len), int(src), int(dst), float(theta), int(dtype), ksp)
 
 
-def block_write(K, V, block_start, block_len, blocks, k_new, v_new, theta, dtype):
+def block_write(K, V, block_start, block_len, blocks, k_new, v_new, theta, dtype, k_scale=None,
+                v_scale=None):
     """In place on float64 arrays K, V [Hkv][num_slots][D] of one layer: the new
     token of every listed block at its slot block_len[b] - 1 (key design 1).
-    k_new, v_new: [n][Hkv][D].  Returns rc."""
+    k_new, v_new: [n][Hkv][D].  FP8 pools: k_scale, v_scale [Hkv].  Returns rc."""
     assert K.dtype == np.float64 and K.flags.c_contiguous
     assert V.dtype == np.float64 and V.flags.c_contiguous
     bs = _c(block_start, np.int64)
@@ -217,8 +241,11 @@ def block_write(K, V, block_start, block_len, blocks, k_new, v_new, theta, dtype
     kn = _c(k_new, np.float64)
     vn = _c(v_new, np.float64)
     Hkv, S, D = K.shape
+    ks, ksp = _scales(k_scale)
+    vs, vsp = _scales(v_scale)
     return lib().hwo_block_write(Hkv, D, S, _p(K), _p(V), int(bl.shape[0]), _p(bs), _p(bl),
-                                 int(bk.shape[0]), _p(bk), _p(kn), _p(vn), float(theta), int(dtype))
+                                 int(bk.shape[0]), _p(bk), _p(kn), _p(vn), float(theta), int(dtype),
+                                 ksp, vsp)
 
 
 def bl_n(block_len) -> int:

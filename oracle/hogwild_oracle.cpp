@@ -16,6 +16,20 @@
 
 namespace {
 
+// The stored value of x in a pool of type dtype (scale: the plane's FP8 scale).
+double store_round(int32_t dtype, double x, double scale) {
+  if (dtype == HWO_BF16) return hwo_round_bf16(x);
+  if (dtype == HWO_FP8) return scale * hwo_round_e4m3(x / scale);
+  return static_cast<double>(static_cast<float>(x));
+}
+
+bool scales_ok(const double* s, int64_t n) {
+  if (!s) return false;
+  for (int64_t i = 0; i < n; ++i)
+    if (!(s[i] > 0.0) || !std::isfinite(s[i])) return false;
+  return true;
+}
+
 // Inverse frequency of pair i for head size D:  theta^(-2i/D)
 // (omica.com.cn news 1114328, section 2.1, rotate_query: 1/base^(arange(0,dim,2)/dim)).
 double inv_freq(double theta, int32_t i, int32_t D) {
@@ -55,6 +69,37 @@ double hwo_round_bf16(double x) {
 }
 
 double hwo_round_f32(double x) { return static_cast<double>(static_cast<float>(x)); }
+
+// OCP FP8 E4M3 (e4m3fn), read off its definition: sign, exponent field e
+// (bias 7), mantissa m; e = 0 is subnormal; e = 15 with m = 7 is NaN.
+double hwo_e4m3_value(int32_t code) {
+  const int32_t c = code & 0xff;
+  const int32_t e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return std::nan("");
+  const double v = e == 0 ? std::ldexp(static_cast<double>(m), -9)
+                          : std::ldexp(static_cast<double>(8 + m), e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+// Nearest E4M3 value, ties to even, in one step from the double.  The grid
+// at |x| in [2^(k-1), 2^k) has 3 fraction bits, quantum 2^(k-4); below 2^-6
+// the subnormal quantum 2^-9.  Magnitudes past 448 saturate to 448 (the
+// format has no infinity).
+double hwo_round_e4m3(double x) {
+  if (std::isnan(x) || x == 0.0) return x;
+  if (std::isinf(x)) return std::copysign(448.0, x);
+  int k = 0;
+  std::frexp(x, &k);
+  int qexp = k - 4;
+  if (qexp < -9) qexp = -9;
+  const int saved = std::fegetround();
+  std::fesetround(FE_TONEAREST);
+  const double r = std::nearbyint(std::ldexp(x, -qexp));  // ties to even
+  std::fesetround(saved);
+  const double y = std::ldexp(r, qexp);
+  if (std::fabs(y) > 448.0) return std::copysign(448.0, x);
+  return y;
+}
 
 // RoPE with rotate-half pairing: element i rotates with element i + D/2 by the
 // angle pos * theta^(-2i/D)  (omica 1114328 section 2.1: q*cos + rotate_half(q)*sin,
@@ -272,9 +317,11 @@ int32_t hwo_attn_chunk(int32_t form, int32_t W, int32_t n, int32_t Hq, int32_t H
 // len_dst + j, round to the storage type.
 int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, double* K, double* V,
                          int32_t num_blocks, const int64_t* block_start, const int32_t* block_cap,
-                         int32_t* block_len, int32_t src, int32_t dst, double theta, int32_t dtype) {
+                         int32_t* block_len, int32_t src, int32_t dst, double theta, int32_t dtype,
+                         const double* k_scale) {
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return HWO_EINVAL;
-  if (dtype != HWO_F32 && dtype != HWO_BF16) return HWO_EINVAL;
+  if (dtype != HWO_F32 && dtype != HWO_BF16 && dtype != HWO_FP8) return HWO_EINVAL;
+  if (dtype == HWO_FP8 && !scales_ok(k_scale, static_cast<int64_t>(L) * Hkv)) return HWO_EINVAL;
   const int32_t ls = block_len[src];
   const int32_t ld = block_len[dst];
   if (static_cast<int64_t>(ld) + ls > block_cap[dst]) return HWO_ECAPACITY;
@@ -282,13 +329,14 @@ int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, d
   for (int32_t l = 0; l < L; ++l) {
     for (int32_t g = 0; g < Hkv; ++g) {
       const int64_t plane = (static_cast<int64_t>(l) * Hkv + g) * num_slots * D;
+      const double ks = dtype == HWO_FP8 ? k_scale[l * Hkv + g] : 1.0;
       for (int32_t j = 0; j < ls; ++j) {
         const int64_t s_src = plane + (block_start[src] + j) * static_cast<int64_t>(D);
         const int64_t s_dst = plane + (block_start[dst] + ld + j) * static_cast<int64_t>(D);
         hwo_rope(K + s_src, D, theta, -static_cast<double>(j), raw.data());
         hwo_rope(raw.data(), D, theta, static_cast<double>(ld) + j, enc.data());
         for (int32_t d = 0; d < D; ++d) {
-          K[s_dst + d] = dtype == HWO_BF16 ? hwo_round_bf16(enc[d]) : hwo_round_f32(enc[d]);
+          K[s_dst + d] = store_round(dtype, enc[d], ks);
           V[s_dst + d] = V[s_src + d];
         }
       }
@@ -302,8 +350,10 @@ int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, d
 int32_t hwo_block_write(int32_t Hkv, int32_t D, int64_t num_slots, double* K, double* V,
                         int32_t num_blocks, const int64_t* block_start, const int32_t* block_len,
                         int32_t n, const int32_t* blocks, const double* k_new,
-                        const double* v_new, double theta, int32_t dtype) {
-  if (dtype != HWO_F32 && dtype != HWO_BF16) return HWO_EINVAL;
+                        const double* v_new, double theta, int32_t dtype, const double* k_scale,
+                        const double* v_scale) {
+  if (dtype != HWO_F32 && dtype != HWO_BF16 && dtype != HWO_FP8) return HWO_EINVAL;
+  if (dtype == HWO_FP8 && (!scales_ok(k_scale, Hkv) || !scales_ok(v_scale, Hkv))) return HWO_EINVAL;
   for (int32_t i = 0; i < n; ++i) {
     if (blocks[i] < 0 || blocks[i] >= num_blocks) return HWO_EINVAL;
     if (block_len[blocks[i]] < 1) return HWO_ENOTOKENS;
@@ -317,9 +367,11 @@ int32_t hwo_block_write(int32_t Hkv, int32_t D, int64_t num_slots, double* K, do
       const double* vr = v_new + (static_cast<int64_t>(i) * Hkv + g) * D;
       const int64_t s = (static_cast<int64_t>(g) * num_slots + block_start[b] + pos) * D;
       hwo_rope(kr, D, theta, static_cast<double>(pos), enc.data());
+      const double ks = dtype == HWO_FP8 ? k_scale[g] : 1.0;
+      const double vs = dtype == HWO_FP8 ? v_scale[g] : 1.0;
       for (int32_t d = 0; d < D; ++d) {
-        K[s + d] = dtype == HWO_BF16 ? hwo_round_bf16(enc[d]) : hwo_round_f32(enc[d]);
-        V[s + d] = dtype == HWO_BF16 ? hwo_round_bf16(vr[d]) : hwo_round_f32(vr[d]);
+        K[s + d] = store_round(dtype, enc[d], ks);
+        V[s + d] = store_round(dtype, vr[d], vs);
       }
     }
   }

@@ -54,11 +54,25 @@ extern "C" {
 /* Storage types for rounding the appended keys. */
 #define HWO_F32 0
 #define HWO_BF16 1
+#define HWO_FP8 2 /* OCP FP8 E4M3 codes times a per-(layer, kv head) scale */
 
 /* Round a double to the nearest bf16 value (ties to even), returned as double. */
 double hwo_round_bf16(double x);
 /* Round a double to the nearest fp32 value (ties to even), returned as double. */
 double hwo_round_f32(double x);
+
+/*
+ * OCP FP8 E4M3 (the "e4m3fn" variant): 1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; codes
+ * 0x7f and 0xff are NaN and there are no infinities, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448.  The FP8 pool of the future-work note on
+ * mixed precision (news 1114328 sec. 6) stores code * scale.
+ */
+/* The value of code & 0xff. */
+double hwo_e4m3_value(int32_t code);
+/* Round a double to the nearest E4M3 value (ties to even), saturating at +-448;
+ * NaN stays NaN. */
+double hwo_round_e4m3(double x);
 
 /* RoPE, rotate-half pairing: y = rho(x, pos).  x, y: [D]; may alias. */
 void hwo_rope(const double* x, int32_t D, double theta, double pos, double* y);
@@ -134,10 +148,14 @@ int32_t hwo_attn_chunk(int32_t form, int32_t W, int32_t n, int32_t Hq, int32_t H
  * For j < len_src: dst token len_dst + j gets the src key re-encoded at that
  * local position (rounded to dtype) and the src value; then
  * len_dst += len_src, len_src = 0.  src data is left as it was.
+ * dtype HWO_FP8: K, V hold code * scale; a key is stored as s * e4m3(x / s)
+ * with s = k_scale[l * Hkv + g] (k_scale [L][Hkv], required, > 0); values
+ * move unchanged.  k_scale is ignored for the other types (may be NULL).
  */
 int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, double* K, double* V,
                          int32_t num_blocks, const int64_t* block_start, const int32_t* block_cap,
-                         int32_t* block_len, int32_t src, int32_t dst, double theta, int32_t dtype);
+                         int32_t* block_len, int32_t src, int32_t dst, double theta, int32_t dtype,
+                         const double* k_scale);
 
 /*
  * Token write for one layer (the new token of a decode step, stored at its
@@ -147,11 +165,14 @@ int32_t hwo_block_append(int32_t L, int32_t Hkv, int32_t D, int64_t num_slots, d
  * p receives v_new[i][h] (rounded to dtype).  Lengths are not changed.
  * k_new, v_new: [n][Hkv][D].  Returns HWO_EINVAL for a block id out of range,
  * HWO_ENOTOKENS when a listed block has length 0 (nothing is written then).
+ * dtype HWO_FP8: key s_k * e4m3(x / s_k), value s_v * e4m3(v / s_v) with
+ * s_k = k_scale[g], s_v = v_scale[g] (this layer's scales, required, > 0).
  */
 int32_t hwo_block_write(int32_t Hkv, int32_t D, int64_t num_slots, double* K, double* V,
                         int32_t num_blocks, const int64_t* block_start, const int32_t* block_len,
                         int32_t n, const int32_t* blocks, const double* k_new,
-                        const double* v_new, double theta, int32_t dtype);
+                        const double* v_new, double theta, int32_t dtype, const double* k_scale,
+                        const double* v_scale);
 
 #ifdef __cplusplus
 }

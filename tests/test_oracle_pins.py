@@ -542,3 +542,153 @@ def test_chunk_one_block_is_causal_textbook_attention():
         Kabs = np.stack([rope_complex(raw[t], theta, t) for t in range(p + 1)])
         ref = textbook_decode(rope_complex(q[0, j, 0], theta, p), Kabs, V[0, :p + 1])
         np.testing.assert_allclose(got[0, j, 0], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------- FP8 E4M3 pools (NEXT-4)
+def _e4m3_table():
+    """Every finite non-negative E4M3 value with its code (codes 0x00..0x7e)."""
+    return [(c, oracle.e4m3_value(c)) for c in range(0x7f)]
+
+
+def test_e4m3_codes_match_torch():
+    """All 256 codes decode as torch's float8_e4m3fn (a library routine) does."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all() and nan.sum() == 2  # 0x7f and 0xff
+    assert (got[~nan] == ref[~nan]).all()
+    assert oracle.e4m3_value(0x7e) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6 and oracle.e4m3_value(0x38) == 1.0
+
+
+def _nearest_even_brute(x, table):
+    """Nearest value by exhaustive search; equidistant candidates go to the even code."""
+    a = abs(x)
+    best = None
+    for c, v in table:
+        d = abs(a - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c, v)
+    v = min(best[2], 448.0)
+    return math.copysign(v, x) if v != 0.0 else math.copysign(0.0, x)
+
+
+def test_round_e4m3_brute_force():
+    rng = np.random.default_rng(30)
+    table = _e4m3_table()
+    xs = np.concatenate([
+        rng.standard_normal(3000) * 10.0 ** rng.uniform(-4, 2.6, 3000),
+        rng.uniform(-448, 448, 500),
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 300),       # subnormal range
+    ])
+    for x in xs:
+        assert oracle.round_e4m3(float(x)) == _nearest_even_brute(float(x), table), x
+
+
+def test_round_e4m3_ties_and_saturation():
+    table = _e4m3_table()
+    for (c0, v0), (c1, v1) in zip(table[:-1], table[1:]):
+        mid = (v0 + v1) / 2.0  # exact in double
+        want = v0 if c0 % 2 == 0 else v1
+        assert oracle.round_e4m3(mid) == want and oracle.round_e4m3(-mid) == -want
+    # past the largest finite value: 464 is the tie between 448 (even code) and
+    # 480 (not representable); larger magnitudes saturate to 448
+    for x, want in [(448.0, 448.0), (464.0, 448.0), (465.0, 448.0), (1e9, 448.0),
+                    (-500.0, -448.0), (math.inf, 448.0), (2.0 ** -10, 0.0),
+                    (3 * 2.0 ** -11, 2.0 ** -9)]:
+        assert oracle.round_e4m3(x) == want, x
+    assert math.isnan(oracle.round_e4m3(math.nan))
+
+
+def test_round_e4m3_matches_torch_in_range():
+    rng = np.random.default_rng(31)
+    x = np.concatenate([rng.standard_normal(20000) * 30.0, rng.standard_normal(2000) * 1e-3]
+                       ).astype(np.float32)
+    x = x[np.abs(x) <= 448.0]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.round_e4m3(float(v)) for v in x])
+    assert (got == ref).all()
+
+
+def _fp8_grid(x, s):
+    """True where every x / s is an E4M3 value."""
+    r = np.vectorize(oracle.round_e4m3)(x / s)
+    return (r == x / s).all()
+
+
+def test_append_fp8_moves_and_rerotates():
+    """FP8 pool: a moved key is s * (the E4M3 value nearest to its exact rotation / s),
+    values move bit for bit, nothing else changes."""
+    rng = np.random.default_rng(32)
+    L, Hkv, D, S = 2, 2, 8, 96
+    starts = np.array([0, 32, 64], np.int64)
+    caps = np.array([32, 32, 32], np.int32)
+    lens = np.array([11, 7, 5], np.int32)
+    ks = np.array([[0.02, 0.05], [0.011, 0.3]])
+    codes = rng.integers(0, 0x7f, (L, Hkv, S, D)) | (rng.integers(0, 2, (L, Hkv, S, D)) << 7)
+    K = np.vectorize(oracle.e4m3_value)(codes) * ks[:, :, None, None]
+    l, g, s, d = np.meshgrid(np.arange(L), np.arange(Hkv), np.arange(S), np.arange(D),
+                             indexing="ij")
+    V = (l * 1_000_000 + g * 10_000 + s * 10 + d).astype(np.float64)
+    K0, V0, lens0 = K.copy(), V.copy(), lens.copy()
+    theta, src, dst = 1e4, 2, 0
+    assert oracle.block_append(K, V, starts, caps, lens, src, dst, theta, oracle.HWO_FP8,
+                               k_scale=ks) == oracle.HWO_OK
+    assert lens.tolist() == [16, 7, 0]
+    ld, ls = int(lens0[dst]), int(lens0[src])
+    moved = np.zeros(S, bool)
+    moved[starts[dst] + ld: starts[dst] + ld + ls] = True
+    assert (K[:, :, ~moved] == K0[:, :, ~moved]).all() and (V[:, :, ~moved] == V0[:, :, ~moved]).all()
+    table = _e4m3_table()
+    for j in range(ls):
+        assert (V[:, :, starts[dst] + ld + j] == V0[:, :, starts[src] + j]).all()
+        exact = rope_complex(K0[:, :, starts[src] + j], theta, ld)
+        got = K[:, :, starts[dst] + ld + j]
+        for li in range(L):
+            for gi in range(Hkv):
+                sc = ks[li, gi]
+                want = [sc * _nearest_even_brute(x / sc, table) for x in exact[li, gi]]
+                # the exact rotation lies off every rounding boundary here, so the
+                # brute-force nearest value is the unique answer
+                assert np.allclose(got[li, gi], want, rtol=0, atol=0), (j, li, gi)
+
+
+def test_append_fp8_needs_positive_scales():
+    rng = np.random.default_rng(33)
+    L, Hkv, D, S, starts, caps, lens, K, V = _append_fixture(rng, oracle.round_f32)
+    assert oracle.block_append(K, V, starts, caps, lens, 1, 0, 1e4, oracle.HWO_FP8) == oracle.HWO_EINVAL
+    bad = np.array([[1.0, 0.0], [1.0, 1.0]])
+    assert oracle.block_append(K, V, starts, caps, lens, 1, 0, 1e4, oracle.HWO_FP8,
+                               k_scale=bad) == oracle.HWO_EINVAL
+
+
+def test_token_write_fp8():
+    """FP8 pool: the new key is s_k * e4m3(rho(k, p) / s_k) at slot len-1, the value
+    s_v * e4m3(v / s_v), both the brute-force nearest grid values."""
+    rng = np.random.default_rng(34)
+    Hkv, D, theta = 2, 16, 1e4
+    starts = np.array([0, 64, 96], np.int64)
+    lens = np.array([40, 5, 17], np.int32)
+    S = 128
+    K = np.zeros((Hkv, S, D))
+    V = np.zeros((Hkv, S, D))
+    ks, vs = np.array([0.01, 0.04]), np.array([0.02, 0.005])
+    blocks = np.array([2, 1], np.int32)
+    kn = rng.standard_normal((2, Hkv, D))
+    vn = rng.standard_normal((2, Hkv, D)) * 0.5
+    assert oracle.block_write(K, V, starts, lens, blocks, kn, vn, theta, oracle.HWO_FP8,
+                              k_scale=ks, v_scale=vs) == oracle.HWO_OK
+    table = _e4m3_table()
+    written = np.zeros(S, bool)
+    for i, b in enumerate(blocks):
+        slot = starts[b] + lens[b] - 1
+        written[slot] = True
+        exact = rope_complex(kn[i], theta, lens[b] - 1)
+        for g in range(Hkv):
+            want_k = [ks[g] * _nearest_even_brute(x / ks[g], table) for x in exact[g]]
+            want_v = [vs[g] * _nearest_even_brute(x / vs[g], table) for x in vn[i, g]]
+            assert (K[g, slot] == want_k).all() and (V[g, slot] == want_v).all()
+    assert (K[:, ~written] == 0).all() and (V[:, ~written] == 0).all()
+    assert oracle.block_write(K, V, starts, lens, blocks, kn, vn, theta, oracle.HWO_FP8,
+                              k_scale=ks) == oracle.HWO_EINVAL
