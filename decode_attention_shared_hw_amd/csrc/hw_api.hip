@@ -19,7 +19,7 @@ int g_units_per_head = 0;  // 0 automatic
 
 struct DeviceInfo {
   int cus = 0;
-  int occ[3][2][2][2] = {};  // [path][dtype][D==128][rows>16] resident workgroups per CU
+  int occ[3][3][2][2] = {};  // [path][dtype][D==128][rows>16] resident workgroups per CU
 };
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
@@ -35,10 +35,11 @@ hw_status device_info(DeviceInfo** out) {
     DeviceInfo& d = g_dev[dev];
     d.cus = p.multiProcessorCount;
     for (int path = 1; path <= 2; ++path)
-      for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < 3; ++dt)
         for (int dd = 0; dd < 2; ++dd)
           for (int rr = 0; rr < 2; ++rr) {
-            if (path == 2 && dt != HW_BF16) continue;
+            if (path == 2 && dt == HW_F32) continue;
+            if (path == 1 && dt == HW_FP8) continue;
             d.occ[path][dt][dd][rr] = decode_blocks_per_cu(path, dt, dd ? 128 : 64, rr ? 32 : 16);
           }
     g_dev_ready[dev] = true;
@@ -49,16 +50,24 @@ hw_status device_info(DeviceInfo** out) {
 
 hw_status check_pool(const hw_pool* p) {
   if (!p) return HW_EINVAL;
-  if (p->dtype != HW_F32 && p->dtype != HW_BF16) return HW_EUNSUPPORTED;
+  if (p->dtype != HW_F32 && p->dtype != HW_BF16 && p->dtype != HW_FP8) return HW_EUNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return HW_EUNSUPPORTED;
   if (p->num_layers < 1 || p->num_kv_heads < 1 || p->reserved != 0) return HW_EINVAL;
   if (p->num_blocks < 1 || p->num_blocks > HW_MAX_BLOCKS) return HW_ERANGE;
   if (p->num_slots <= 0 || p->num_slots % HW_TILE_TOKENS != 0) return HW_EINVAL;
   // one (layer, kv head) plane is addressed with 32-bit byte offsets
-  if (p->num_slots * p->head_dim * (p->dtype == HW_F32 ? 4 : 2) >= (int64_t(1) << 31))
-    return HW_ERANGE;
+  if (p->num_slots * p->head_dim * elem_bytes(p->dtype) >= (int64_t(1) << 31)) return HW_ERANGE;
   if (!p->k || !p->v || !p->block_len || !p->status || !p->block_start || !p->block_cap)
     return HW_EINVAL;
+  if (p->dtype == HW_FP8) {
+    if (p->num_kv_heads > HW_MAX_FP8_KV_HEADS) return HW_ERANGE;
+    if (!p->k_scale || !p->v_scale) return HW_EINVAL;
+    const int64_t n = static_cast<int64_t>(p->num_layers) * p->num_kv_heads;
+    for (int64_t i = 0; i < n; ++i)
+      if (!(p->k_scale[i] > 0.f) || !isfinite(p->k_scale[i]) || !(p->v_scale[i] > 0.f) ||
+          !isfinite(p->v_scale[i]))
+        return HW_EINVAL;
+  }
   for (int b = 0; b < p->num_blocks; ++b) {
     const int64_t s = p->block_start[b];
     const int32_t c = p->block_cap[b];
@@ -86,6 +95,7 @@ uint64_t rope_fraction(double w) {
 int select_path(const hw_pool* p, int rows) {
   if (g_path == 1) return 1;
   if (g_path == 2) return 2;
+  if (p->dtype == HW_FP8) return 2;
   return (p->dtype == HW_BF16 && rows <= 32) ? 2 : 1;
 }
 
@@ -196,7 +206,8 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   const int rows = num_workers * nq * G;
   if (rows > HW_MAX_ROWS) return HW_ERANGE;
   const int path = select_path(pool, rows);
-  if (path == 2 && (pool->dtype != HW_BF16 || rows > 32)) return HW_EUNSUPPORTED;
+  if (path == 2 && (pool->dtype == HW_F32 || rows > 32)) return HW_EUNSUPPORTED;
+  if (path == 1 && pool->dtype == HW_FP8) return HW_EUNSUPPORTED;
   const int P_ws = units_per_head_setting(pool->num_kv_heads);
   const WsLayout wl = ws_layout(pool->num_kv_heads, P_ws, rows, pool->head_dim);
   if (!workspace || workspace_bytes < wl.total) return HW_EWORKSPACE;
@@ -213,7 +224,7 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
 
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
-  const size_t esz = pool->dtype == HW_F32 ? 4 : 2;
+  const size_t esz = elem_bytes(pool->dtype);
   const int64_t plane = pool->num_slots * pool->head_dim;
   a.q = q;
   a.k = static_cast<const char*>(pool->k) +
@@ -252,6 +263,13 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
     const double w = pow(rope_theta, -2.0 * i / static_cast<double>(pool->head_dim));
     a.tab.inv_freq[i] = w;
     a.tab.rope_frac[i] = rope_fraction(w);
+  }
+  if (pool->dtype == HW_FP8) {
+    const int64_t l0 = static_cast<int64_t>(layer) * pool->num_kv_heads;
+    for (int g = 0; g < pool->num_kv_heads; ++g) {
+      a.tab.k_scale[g] = pool->k_scale[l0 + g];
+      a.tab.v_scale[g] = pool->v_scale[l0 + g];
+    }
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = path == 2 ? launch_decode_mfma(a, static_cast<int>(grid), hs)

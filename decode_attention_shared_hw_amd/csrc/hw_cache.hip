@@ -2,6 +2,8 @@
 // block reset.  (Hogwild! Inference notes, key design 2.)
 #include <math.h>
 
+#include <type_traits>
+
 #include "hw_internal.h"
 
 namespace hw {
@@ -83,34 +85,80 @@ __device__ uint16_t f64_to_bf16_bits(double x) {
   return static_cast<uint16_t>(__float_as_uint(static_cast<float>(y)) >> 16);
 }
 
+// Nearest OCP FP8 E4M3 code (ties to even) in one step from the double.  The
+// grid at |x| in [2^(k-1), 2^k) has 3 fraction bits (quantum 2^(k-4)); below
+// 2^-6 the subnormal quantum 2^-9.  The format has no infinity: magnitudes
+// from 448 up saturate to 448 (code 0x7e; 464 is the tie between 448 and the
+// unrepresentable 480 and goes to the even code 0x7e).  Codes are monotonic in
+// the magnitude, so the code is the exponent field and the rounded mantissa
+// added together.
+__device__ uint8_t f64_to_e4m3(double x) {
+  if (x != x) return 0x7f;
+  const uint32_t sign = signbit(x) ? 0x80u : 0u;
+  const double a = fabs(x);
+  if (a >= 448.0) return static_cast<uint8_t>(sign | 0x7eu);
+  if (a == 0.0) return static_cast<uint8_t>(sign);
+  int k = 0;
+  frexp(a, &k);
+  const int qexp = k - 4 < -9 ? -9 : k - 4;
+  const int r = static_cast<int>(rint(ldexp(a, -qexp)));  // 0..16
+  const int code = qexp == -9 ? r : ((qexp + 10) << 3) + r - 8;
+  return static_cast<uint8_t>(sign | static_cast<uint32_t>(code));
+}
+
+// Value of an E4M3 code (bias 7, 3 mantissa bits, subnormals below 2^-6).
+__device__ __forceinline__ double e4m3_to_f64(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return __longlong_as_double(0x7ff8000000000000ll);
+  const double v = e == 0 ? ldexp(static_cast<double>(m), -9)
+                          : ldexp(static_cast<double>(8 + m), e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
 __device__ __forceinline__ double to_f64(float x) { return x; }
 __device__ __forceinline__ double to_f64(uint16_t b) {
   return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
 }
+__device__ __forceinline__ double to_f64(uint8_t c) { return e4m3_to_f64(c); }
 template <typename T>
 __device__ __forceinline__ T round_to(double x);
 template <>
 __device__ __forceinline__ float round_to<float>(double x) { return static_cast<float>(x); }
 template <>
 __device__ __forceinline__ uint16_t round_to<uint16_t>(double x) { return f64_to_bf16_bits(x); }
+template <>
+__device__ __forceinline__ uint8_t round_to<uint8_t>(double x) { return f64_to_e4m3(x); }
+
+// Data moves in chunks of consecutive elements of one layout unit (a key
+// token's dims, a value dim's tokens): 16 bytes, or 8 for FP8 pools, whose
+// 16-byte runs would span two units.
+template <typename T>
+struct ChunkOf {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  static constexpr int kBytes = sizeof(T) == 1 ? 8 : 16;
+  static constexpr int kElems = kBytes / static_cast<int>(sizeof(T));
+  typedef typename std::conditional<kBytes == 16, u32x4, u32x2>::type type;
+};
 
 // One workgroup per (layer*kv head plane, destination tile).  A src key at
 // local position j moves to dst position len_dst + j: rotating it by len_dst
 // re-encodes it there (rho(rho(x, j), n) = rho(x, j + n)).
 //
-// Data move in 16-byte chunks (kChunk elements).  In the key layout a chunk
+// Data move in chunks (kChunk elements, ChunkOf).  In the key layout a chunk
 // holds consecutive dims of one token, so a lane loads a chunk and its
 // rotate-half partner chunk (dims + D/2) of one src token, rotates the pairs
 // in fp64 and stores both rounded.  In the value layout a chunk holds one dim
 // of several tokens, and the shift by len_dst mixes tokens of two src tiles:
 // the run's src values are staged in LDS (token-major), then every dst chunk
 // the run touches is rebuilt, keeping the tokens outside the run, and stored
-// whole.
+// whole.  FP8 pools: src and dst share the plane's scale, so the codes
+// themselves are rotated and rounded.
 template <typename T>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma clang fp contract(off)
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  constexpr int kChunk = 16 / static_cast<int>(sizeof(T));
+  typedef typename ChunkOf<T>::type Chunk;
+  constexpr int kChunk = ChunkOf<T>::kElems;
   const int tid = threadIdx.x;
   // consecutive dst tiles of one plane on one XCD (they share src tiles)
   int lin = blockIdx.x;
@@ -148,7 +196,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int64_t st = st_lo + x / cpt;
     const int off = (x % cpt) * kChunk;  // element offset inside the tile
     const int g = off / (8 * D), d = (off % (8 * D)) / 8, r0 = off % 8;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(vp + st * 32 * D + off);
+    const Chunk raw = *reinterpret_cast<const Chunk*>(vp + st * 32 * D + off);
     const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
@@ -164,11 +212,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   for (int x = tid; x < n * cph; x += 256) {
     const int j = x / cph;
     const int d0 = (x % cph) * kChunk;
-    const u32x4 r0 = *reinterpret_cast<const u32x4*>(kp + key_offset(ss0 + j, d0, D));
-    const u32x4 r1 = *reinterpret_cast<const u32x4*>(kp + key_offset(ss0 + j, d0 + half, D));
+    const Chunk r0 = *reinterpret_cast<const Chunk*>(kp + key_offset(ss0 + j, d0, D));
+    const Chunk r1 = *reinterpret_cast<const Chunk*>(kp + key_offset(ss0 + j, d0 + half, D));
     const T* e0 = reinterpret_cast<const T*>(&r0);
     const T* e1 = reinterpret_cast<const T*>(&r1);
-    u32x4 w0, w1;
+    Chunk w0, w1;
     T* o0 = reinterpret_cast<T*>(&w0);
     T* o1 = reinterpret_cast<T*>(&w1);
 #pragma unroll
@@ -178,8 +226,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       o0[i] = round_to<T>(x0 * c - x1 * s);
       o1[i] = round_to<T>(x1 * c + x0 * s);
     }
-    *reinterpret_cast<u32x4*>(kp + key_offset(s_begin + j, d0, D)) = w0;
-    *reinterpret_cast<u32x4*>(kp + key_offset(s_begin + j, d0 + half, D)) = w1;
+    *reinterpret_cast<Chunk*>(kp + key_offset(s_begin + j, d0, D)) = w0;
+    *reinterpret_cast<Chunk*>(kp + key_offset(s_begin + j, d0 + half, D)) = w1;
   }
   // ---- values, phase 2: every chunk of the dst tile holding a run token
   const int tb = static_cast<int>(s_begin - t0), te = static_cast<int>(s_end - t0);
@@ -198,7 +246,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
     if (tmax < 0) continue;  // no run token in this chunk
     T* dst = vp + t0 * D + off;
-    u32x4 raw = u32x4{0u, 0u, 0u, 0u};
+    Chunk raw = {};
     bool whole = true;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
@@ -206,7 +254,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
       whole = whole && t >= tb && t < te;
     }
-    if (!whole) raw = *reinterpret_cast<const u32x4*>(dst);  // keep tokens outside the run
+    if (!whole) raw = *reinterpret_cast<const Chunk*>(dst);  // keep tokens outside the run
     T* e = reinterpret_cast<T*>(&raw);
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
@@ -214,7 +262,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
       if (t >= tb && t < te) e[i] = vstage[(t - tb) * D + d];
     }
-    *reinterpret_cast<u32x4*>(dst) = raw;
+    *reinterpret_cast<Chunk*>(dst) = raw;
   }
 }
 
@@ -254,6 +302,8 @@ struct TokenArgs {
   int64_t start[HW_MAX_WORKERS];
   int32_t cap[HW_MAX_WORKERS];
   double inv_freq[kMaxHalf];
+  float k_scale[HW_MAX_FP8_KV_HEADS];  // FP8 pools: this layer's scales per kv head
+  float v_scale[HW_MAX_FP8_KV_HEADS];
 };
 
 // Thread i reserves the next slot of block blocks[i].
@@ -270,7 +320,8 @@ __global__ void advance_kernel(TokenArgs a) {
 }
 
 // One workgroup per (listed block i, kv head g); thread t < D/2 writes the
-// rotate-half pair (t, t + D/2) of the key and of the value.
+// rotate-half pair (t, t + D/2) of the key and of the value.  FP8 pools store
+// the codes nearest to x / scale (the division in fp64).
 template <typename T>
 __global__ void write_kernel(TokenArgs a) {
 #pragma clang fp contract(off)
@@ -292,10 +343,15 @@ __global__ void write_kernel(TokenArgs a) {
   const double x0 = kr[t], x1 = kr[t + half];
   T* kp = static_cast<T*>(a.k) + g * a.plane_elems;
   T* vp = static_cast<T*>(a.v) + g * a.plane_elems;
-  kp[key_offset(slot, t, a.D)] = round_to<T>(x0 * c - x1 * s);
-  kp[key_offset(slot, t + half, a.D)] = round_to<T>(x1 * c + x0 * s);
-  vp[value_offset(slot, t, a.D)] = round_to<T>(static_cast<double>(vr[t]));
-  vp[value_offset(slot, t + half, a.D)] = round_to<T>(static_cast<double>(vr[t + half]));
+  const bool f8 = sizeof(T) == 1;
+  const double ks = f8 ? static_cast<double>(a.k_scale[g]) : 1.0;
+  const double vs = f8 ? static_cast<double>(a.v_scale[g]) : 1.0;
+  const double k0 = x0 * c - x1 * s, k1 = x1 * c + x0 * s;
+  const double v0 = vr[t], v1 = vr[t + half];
+  kp[key_offset(slot, t, a.D)] = round_to<T>(f8 ? k0 / ks : k0);
+  kp[key_offset(slot, t + half, a.D)] = round_to<T>(f8 ? k1 / ks : k1);
+  vp[value_offset(slot, t, a.D)] = round_to<T>(f8 ? v0 / vs : v0);
+  vp[value_offset(slot, t + half, a.D)] = round_to<T>(f8 ? v1 / vs : v1);
 }
 
 }  // namespace
@@ -316,7 +372,7 @@ hipError_t launch_advance(const hw_pool& pool, int32_t n, const int32_t* blocks,
 hipError_t launch_write(const hw_pool& pool, int32_t layer, int32_t n, const int32_t* blocks,
                         const float* k_new, const float* v_new, double theta, hipStream_t s) {
   TokenArgs a{};
-  const size_t esz = pool.dtype == HW_F32 ? 4 : 2;
+  const size_t esz = elem_bytes(pool.dtype);
   a.plane_elems = pool.num_slots * pool.head_dim;
   const int64_t layer_off = static_cast<int64_t>(layer) * pool.num_kv_heads * a.plane_elems;
   a.k = static_cast<char*>(pool.k) + layer_off * esz;
@@ -335,11 +391,20 @@ hipError_t launch_write(const hw_pool& pool, int32_t layer, int32_t n, const int
   }
   for (int i = 0; i < pool.head_dim / 2; ++i)
     a.inv_freq[i] = pow(theta, -2.0 * i / static_cast<double>(pool.head_dim));
+  if (pool.dtype == HW_FP8) {
+    const int64_t l0 = static_cast<int64_t>(layer) * pool.num_kv_heads;
+    for (int g = 0; g < pool.num_kv_heads; ++g) {
+      a.k_scale[g] = pool.k_scale[l0 + g];
+      a.v_scale[g] = pool.v_scale[l0 + g];
+    }
+  }
   const dim3 grid(static_cast<unsigned>(n * pool.num_kv_heads));
   if (pool.dtype == HW_F32)
     hipLaunchKernelGGL(write_kernel<float>, grid, dim3(64), 0, s, a);
-  else
+  else if (pool.dtype == HW_BF16)
     hipLaunchKernelGGL(write_kernel<uint16_t>, grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(write_kernel<uint8_t>, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -386,11 +451,13 @@ hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double t
   }
   if (a.cap_src > 0 && grid > 0) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 g(static_cast<unsigned>(grid));
     if (pool.dtype == HW_F32)
-      hipLaunchKernelGGL(append_kernel<float>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(append_kernel<float>, g, dim3(256), 0, s, a);
+    else if (pool.dtype == HW_BF16)
+      hipLaunchKernelGGL(append_kernel<uint16_t>, g, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                         a);
+      hipLaunchKernelGGL(append_kernel<uint8_t>, g, dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

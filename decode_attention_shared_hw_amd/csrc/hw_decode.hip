@@ -38,6 +38,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -305,54 +306,79 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* p, int3
                                            0x00020000);
 }
 
-// (a3) one 16-byte buffer load per lane per fragment: every key load of a
-// wave is one contiguous 1 KB, every value load four contiguous 256 B runs.
-// koff / voff: this lane's byte offsets inside a tile; tile: the tile's byte
-// offset in the plane (wave-uniform, kept in an SGPR).
-template <int D>
-__device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t tile,
-                                          uint32_t koff, u32x4 (&kf)[2][D / 32]) {
+// Stored K/V elements as MFMA A fragments (8 elements per lane): bf16 pools
+// load 16 bytes and use them as they are; FP8 E4M3 pools load 8 bytes, which
+// are widened to bf16 (exactly: every E4M3 value is a bf16 value) just before
+// the product that consumes them, so the registers of a tile in flight hold
+// the narrow codes.
+template <typename E>
+struct KvFrag;
+template <>
+struct KvFrag<uint16_t> {
+  typedef u32x4 type;
+  static constexpr int kBytes = 2;
+  __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+  }
+  __device__ static u32x4 widen(const type& f) { return f; }
+};
+template <>
+struct KvFrag<uint8_t> {
+  typedef u32x2 type;
+  static constexpr int kBytes = 1;
+  __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+  }
+  template <bool HI>
+  __device__ static uint32_t pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  __device__ static u32x4 widen(const type& f) {
+    return u32x4{pair<false>(f[0]), pair<true>(f[0]), pair<false>(f[1]), pair<true>(f[1])};
+  }
+};
+
+// (a3) one buffer load per lane per fragment: every key load of a wave is one
+// contiguous run (1 KB bf16, 512 B FP8), every value load four contiguous
+// runs.  koff / voff: this lane's byte offsets inside a tile; tile: the tile's
+// byte offset in the plane (wave-uniform, kept in an SGPR).
+template <int D, typename E>
+__device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t tile, uint32_t koff,
+                                          typename KvFrag<E>::type (&kf)[2][D / 32]) {
+  constexpr int B = KvFrag<E>::kBytes;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      kf[h2][s] = __builtin_amdgcn_raw_buffer_load_b128(
-          krs, koff + (h2 * 16 * D + 4 * s * 128) * 2, tile, 0);
+      kf[h2][s] = KvFrag<E>::load(krs, koff + (h2 * 16 * D + 4 * s * 128) * B, tile);
 }
 
-template <int D>
+template <int D, typename E>
 __device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t tile,
-                                            uint32_t voff, u32x4 (&vf)[D / 16]) {
+                                            uint32_t voff, typename KvFrag<E>::type (&vf)[D / 16]) {
+  constexpr int B = KvFrag<E>::kBytes;
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m)
-    vf[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + 16 * m * 8 * 2, tile, 0);
+  for (int m = 0; m < D / 16; ++m) vf[m] = KvFrag<E>::load(vrs, voff + 16 * m * 8 * B, tile);
 }
 
 // The same loads with the tile offset in the range-checked lane offset: a
 // tile offset past the plane reads zeros, so any value may be passed (used
 // for the speculative first tile, whose offset comes from the last call).
-template <int D>
+template <int D, typename E>
 __device__ __forceinline__ void load_tile_checked(__amdgpu_buffer_rsrc_t krs,
                                                   __amdgpu_buffer_rsrc_t vrs, uint32_t tile,
                                                   uint32_t koff, uint32_t voff,
-                                                  u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16]) {
-  const uint32_t kb = koff + tile, vb = voff + tile;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      kf[h2][s] = __builtin_amdgcn_raw_buffer_load_b128(
-          krs, kb + (h2 * 16 * D + 4 * s * 128) * 2, 0, 0);
-#pragma unroll
-  for (int m = 0; m < D / 16; ++m)
-    vf[m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vb + 16 * m * 8 * 2, 0, 0);
+                                                  typename KvFrag<E>::type (&kf)[2][D / 32],
+                                                  typename KvFrag<E>::type (&vf)[D / 16]) {
+  load_keys<D, E>(krs, 0, koff + tile, kf);
+  load_values<D, E>(vrs, 0, voff + tile, vf);
 }
 
 // S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
 // qf: this lane's rotated-query B fragments, [NT][KS] x 64 lanes in LDS.
-template <int D, int NT>
-__device__ __forceinline__ void tile_scores(const u32x4 (&kf)[2][D / 32], const bf16x8* qf,
-                                            int lane, f32x4 (&sc)[2][NT]) {
+template <int D, int NT, typename E>
+__device__ __forceinline__ void tile_scores(const typename KvFrag<E>::type (&kf)[2][D / 32],
+                                            const bf16x8* qf, int lane, f32x4 (&sc)[2][NT]) {
   constexpr int KS = D / 32;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -360,10 +386,10 @@ __device__ __forceinline__ void tile_scores(const u32x4 (&kf)[2][D / 32], const 
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8 qv = qf[(t * KS + s) * 64 + lane];
-      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[0][s]), qv, c0,
-                                                   0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[1][s]), qv, c1,
-                                                   0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, KvFrag<E>::widen(kf[0][s])), qv, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, KvFrag<E>::widen(kf[1][s])), qv, c1, 0, 0, 0);
     }
     sc[0][t] = c0;
     sc[1][t] = c1;
@@ -373,8 +399,9 @@ __device__ __forceinline__ void tile_scores(const u32x4 (&kf)[2][D / 32], const 
 // Online softmax of one tile's scores and the P.V update of the running
 // (m, l, O^T).  Row t keeps the tile's tokens up to rowlim[t] (its causal
 // limit, below `valid`); values of tokens at or past `valid` are zeroed.
-template <int D, int NT>
-__device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT], u32x4 (&vf)[D / 16],
+template <int D, int NT, typename E>
+__device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
+                                            const typename KvFrag<E>::type (&vf)[D / 16],
                                             const bool (&rowvis)[NT], const int (&rowlim)[NT],
                                             int valid, int q4,
                                             f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
@@ -413,28 +440,30 @@ __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT], u32x4 (&vf
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m][t] *= al;
   }
+  // tokens past the block's length may hold anything (even NaN): zero them
+  u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
   if (valid < kTile) {
-    // tokens past the block's length may hold anything (even NaN): zero them
-    u32x4 keep;
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
       const int t0 = 16 * ((2 * e2) >> 2) + 4 * q4 + ((2 * e2) & 3);
       const int t1 = 16 * ((2 * e2 + 1) >> 2) + 4 * q4 + ((2 * e2 + 1) & 3);
       keep[e2] = (t0 < valid ? 0x0000ffffu : 0u) | (t1 < valid ? 0xffff0000u : 0u);
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) vf[m] &= keep;
   }
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m) {
+    const u32x4 v = KvFrag<E>::widen(vf[m]) & keep;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[m]), pf[t],
+      acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pf[t],
                                                           acc[m][t], 0, 0, 0);
+  }
 }
 
-template <int D, int NT>
+template <int D, int NT, typename E>
 __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
+  typedef typename KvFrag<E>::type Frag;
+  constexpr int EB = KvFrag<E>::kBytes;
   constexpr int NTHR = kMfmaThreads;
   constexpr int NWAVE = kMfmaWaves;
   constexpr int NSTATE = NWAVE / 2;  // wave states held in LDS at once
@@ -470,16 +499,20 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // before the plan is built, and kept if the plan confirms it.
   int h0, u0;
   plan_head_unit(a, &h0, &u0);
-  const uint32_t koff = (q4 * 128 + li * 8) * 2;
-  const uint32_t voff = (q4 * 8 * D + li * 8) * 2;
+  const uint32_t koff = (q4 * 128 + li * 8) * EB;
+  const uint32_t voff = (q4 * 8 * D + li * 8) * EB;
   const __amdgpu_buffer_rsrc_t krs = plane_rsrc(
-      static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(h0) * a.plane_elems, a.plane_bytes);
+      static_cast<const char*>(a.k) + static_cast<int64_t>(h0) * a.plane_elems * EB, a.plane_bytes);
   const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(
-      static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(h0) * a.plane_elems, a.plane_bytes);
+      static_cast<const char*>(a.v) + static_cast<int64_t>(h0) * a.plane_elems * EB, a.plane_bytes);
+  // FP8 pools: the key scale of this kv head is folded into the rotated queries
+  float qsc = a.qscale;
+  if (EB == 1) qsc *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
+                                                     offsetof(DecodeTables, k_scale))[h0];
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t* hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
   const uint32_t spec = *hint;  // uniform: a scalar load
-  u32x4 kf[2][KS], vf[MT];
+  Frag kf[2][KS], vf[MT];
   {
     auto issue = [&] {
 #pragma unroll
@@ -503,7 +536,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       // the speculative tile once the plan's own loads are back, so that its
       // traffic does not queue ahead of them
       __builtin_amdgcn_sched_barrier(0);
-      load_tile_checked<D>(krs, vrs, spec, koff, voff, kf, vf);
+      load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
       __builtin_amdgcn_sched_barrier(0);
     };
     build_plan<NTHR>(a, plan, issue, commit);
@@ -541,7 +574,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
       const int wc = vis ? w : 0;
       const int64_t delta = plan.iq[wc] - plan.row_lag[r] - plan.off[wc * a.NB + b];
-      const float sc = vis ? a.qscale : 0.f;
+      const float sc = vis ? qsc : 0.f;
       const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner block is d0 + HALF
       // two dims per step: bf16 pairs (x, x+1) of the first half and their
       // partners in the second half, rotated and stored as one 32-bit word each
@@ -582,11 +615,11 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       TileRef rt = {0, 0, 0, 0};
       if (j < t_hi) {
         rt = tile_ref<D>(plan, a.NB, j, bcur);
-        const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * 2));
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * EB));
         if (gb == b_first) first = tile;
         if (gb != b_first || tile != spec) {
-          load_keys<D>(krs, tile, koff, kf);
-          load_values<D>(vrs, tile, voff, vf);
+          load_keys<D, E>(krs, tile, koff, kf);
+          load_values<D, E>(vrs, tile, voff, vf);
         }
       }
       if (gb != b_first) __syncthreads();  // the previous group's fragments are consumed
@@ -617,19 +650,19 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
           f32x4 sc[2][NT];
           const int jn = j + NWAVE;
           if (jn >= t_hi) {
-            tile_scores<D, NT>(kf, qf, lane, sc);
-            tile_update<D, NT>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
+            tile_scores<D, NT, E>(kf, qf, lane, sc);
+            tile_update<D, NT, E>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
             break;
           }
           const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
-          const uint32_t tn = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * 2));
-          tile_scores<D, NT>(kf, qf, lane, sc);
+          const uint32_t tn = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * EB));
+          tile_scores<D, NT, E>(kf, qf, lane, sc);
           __builtin_amdgcn_sched_barrier(0);
-          load_keys<D>(krs, tn, koff, kf);
+          load_keys<D, E>(krs, tn, koff, kf);
           __builtin_amdgcn_sched_barrier(0);
-          tile_update<D, NT>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
+          tile_update<D, NT, E>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
           __builtin_amdgcn_sched_barrier(0);
-          load_values<D>(vrs, tn, voff, vf);
+          load_values<D, E>(vrs, tn, voff, vf);
           __builtin_amdgcn_sched_barrier(0);
           j = jn;
           rt = rn;
@@ -1164,7 +1197,11 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
     M = Mc;
   }
   const int w = r / a.G, h = g * a.G + (r - w * a.G);
-  a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = L > 0.f ? s / L : 0.f;
+  float o = L > 0.f ? s / L : 0.f;
+  if (a.dtype == HW_FP8)  // FP8 pools: values are code * scale of the kv head
+    o *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
+                                        offsetof(DecodeTables, v_scale))[g];
+  a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = o;
   if (tid == 0 && !(L > 0.f)) atomicOr(a.status, HW_DEV_NO_TOKENS);
 }
 
@@ -1193,29 +1230,37 @@ hipError_t launch_valu_rows(const DecodeArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int grid, hipStream_t s) {
-  if ((a.D != 64 && a.D != 128) || a.R > HW_MAX_ROWS) return hipErrorInvalidValue;
+  if ((a.D != 64 && a.D != 128) || a.R > HW_MAX_ROWS || a.dtype == HW_FP8)
+    return hipErrorInvalidValue;
   if (a.dtype == HW_F32)
     return a.D == 128 ? launch_valu_rows<float, 128>(a, grid, s) : launch_valu_rows<float, 64>(a, grid, s);
   return a.D == 128 ? launch_valu_rows<uint16_t, 128>(a, grid, s)
                     : launch_valu_rows<uint16_t, 64>(a, grid, s);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
-  if (a.dtype != HW_BF16 || a.R > 32) return hipErrorInvalidValue;
+template <typename E>
+hipError_t launch_mfma_elem(const DecodeArgs& a, int grid, hipStream_t s) {
   if (a.D == 128) {
     if (a.R <= 16)
-      hipLaunchKernelGGL((decode_mfma<128, 1>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<128, 1, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_mfma<128, 2>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<128, 2, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
   } else if (a.D == 64) {
     if (a.R <= 16)
-      hipLaunchKernelGGL((decode_mfma<64, 1>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<64, 1, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((decode_mfma<64, 2>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma<64, 2, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
+  if (a.R > 32) return hipErrorInvalidValue;
+  if (a.dtype == HW_BF16) return launch_mfma_elem<uint16_t>(a, grid, s);
+  if (a.dtype == HW_FP8) return launch_mfma_elem<uint8_t>(a, grid, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
@@ -1225,13 +1270,18 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
 }
 
 // Resident workgroups per CU of the kernel a launch would use (0 on error).
+template <typename E>
+int mfma_blocks_per_cu(int D, int rows) {
+  const int t = kMfmaThreads;
+  if (D == 128)
+    return rows <= 16 ? occupancy(decode_mfma<128, 1, E>, t) : occupancy(decode_mfma<128, 2, E>, t);
+  return rows <= 16 ? occupancy(decode_mfma<64, 1, E>, t) : occupancy(decode_mfma<64, 2, E>, t);
+}
+
 int decode_blocks_per_cu(int path, int dtype, int D, int rows) {
-  if (path == 2) {
-    const int t = kMfmaThreads;
-    if (D == 128)
-      return rows <= 16 ? occupancy(decode_mfma<128, 1>, t) : occupancy(decode_mfma<128, 2>, t);
-    return rows <= 16 ? occupancy(decode_mfma<64, 1>, t) : occupancy(decode_mfma<64, 2>, t);
-  }
+  if (path == 2)
+    return dtype == HW_FP8 ? mfma_blocks_per_cu<uint8_t>(D, rows)
+                           : mfma_blocks_per_cu<uint16_t>(D, rows);
   return dtype == HW_F32 ? occupancy(decode_valu<float, 128, 10>, kThreads)
                          : occupancy(decode_valu<uint16_t, 128, 10>, kThreads);
 }

@@ -40,7 +40,14 @@ struct alignas(16) DecodeTables {
   int32_t block_cap[HW_MAX_BLOCKS];
   double inv_freq[kMaxHalf];  // theta^(-2i/D), i < D/2
   uint64_t rope_frac[kMaxHalf];  // frac(theta^(-2i/D) / (2 pi)) * 2^64, i < D/2
+  float k_scale[HW_MAX_FP8_KV_HEADS];  // FP8 pools: this layer's scales per kv head
+  float v_scale[HW_MAX_FP8_KV_HEADS];
 };
+
+// Bytes per stored element of a pool type.
+__host__ __device__ inline int elem_bytes(int dtype) {
+  return dtype == HW_F32 ? 4 : (dtype == HW_BF16 ? 2 : 1);
+}
 
 // Kernel arguments of the fused decode kernels (passed by value).
 struct alignas(16) DecodeArgs {
@@ -59,7 +66,7 @@ struct alignas(16) DecodeArgs {
   int32_t plane_bytes;      // plane_elems * element size (< 2^31)
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
   int32_t nq;               // query tokens per worker (1: decode); rows are (w*nq + j)*G + h
-  int32_t dtype;            // HW_F32 / HW_BF16
+  int32_t dtype;            // HW_F32 / HW_BF16 / HW_FP8
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
   DecodeTables tab;
 };

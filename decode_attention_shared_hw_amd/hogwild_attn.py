@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libhogwild_attn.so")
 HW_OK, HW_EINVAL, HW_ERANGE, HW_ECAPACITY, HW_EUNSUPPORTED, HW_EWORKSPACE, HW_EHIP = range(7)
 HW_DEV_BAD_ENTRY, HW_DEV_BAD_LENGTH, HW_DEV_NO_TOKENS, HW_DEV_APPEND_OVERFLOW = 1, 2, 4, 8
 HW_DEV_WRITE_OVERFLOW = 16
-HW_F32, HW_BF16 = 0, 1
+HW_F32, HW_BF16, HW_FP8 = 0, 1, 2
 HW_TILE_TOKENS = 32
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 HW_LAYOUT_COMBINED, HW_LAYOUT_INTERLEAVED, HW_LAYOUT_CONTIGUOUS = 0, 1, 2
@@ -51,7 +51,17 @@ class hw_pool(ctypes.Structure):
         ("status", ctypes.c_void_p),
         ("block_start", ctypes.c_void_p),
         ("block_cap", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
+
+
+_HW_DTYPES = {torch.bfloat16: HW_BF16, torch.float32: HW_F32, torch.float8_e4m3fn: HW_FP8}
+
+
+def query_dtype(pool_dtype: torch.dtype) -> torch.dtype:
+    """dtype of q for a pool: fp32 for fp32 pools, bf16 for bf16 and FP8 pools."""
+    return torch.float32 if pool_dtype == torch.float32 else torch.bfloat16
 
 
 EXPORTED = [
@@ -126,10 +136,12 @@ class Pool:
     k, v: device tensors [num_layers, num_kv_heads, num_slots, head_dim] in the
     library's tile layout (see `layout`); block_len / status: device int32.
     block b owns slots [block_start[b], block_start[b] + block_cap[b]).
+    FP8 pools (dtype torch.float8_e4m3fn) hold E4M3 codes; k_scale / v_scale
+    [num_layers][num_kv_heads] (host) give value = code * scale.
     """
 
     def __init__(self, num_layers, num_kv_heads, head_dim, block_caps, dtype=torch.bfloat16,
-                 device="cuda", fill=None):
+                 device="cuda", fill=None, k_scale=None, v_scale=None):
         caps = [int(c) for c in block_caps]
         if any(c % HW_TILE_TOKENS for c in caps):
             raise ValueError("block capacities must be multiples of 32")
@@ -140,7 +152,7 @@ class Pool:
         self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
         self.num_slots = max(s, HW_TILE_TOKENS)
         self.dtype = dtype
-        self.hw_dtype = {torch.bfloat16: HW_BF16, torch.float32: HW_F32}[dtype]
+        self.hw_dtype = _HW_DTYPES[dtype]
         shape = (num_layers, num_kv_heads, self.num_slots, head_dim)
         if fill is None:
             self.k = torch.zeros(shape, dtype=dtype, device=device)
@@ -154,25 +166,51 @@ class Pool:
         self._cap = (ctypes.c_int32 * len(caps))(*caps)
         self.block_start = starts
         self.block_cap = caps
+        self._ks = self._vs = None
+        if k_scale is not None or v_scale is not None:
+            n = num_layers * num_kv_heads
+            ks = [float(x) for x in torch.as_tensor(k_scale, dtype=torch.float32).reshape(-1)]
+            vs = [float(x) for x in torch.as_tensor(v_scale, dtype=torch.float32).reshape(-1)]
+            if len(ks) != n or len(vs) != n:
+                raise ValueError("k_scale and v_scale must hold num_layers * num_kv_heads values")
+            self._ks = (ctypes.c_float * n)(*ks)
+            self._vs = (ctypes.c_float * n)(*vs)
         self.desc = hw_pool(self.hw_dtype, num_layers, num_kv_heads, head_dim, len(caps), 0,
                             self.num_slots, self.k.data_ptr(), self.v.data_ptr(),
                             self.block_len.data_ptr(), self.status.data_ptr(),
                             ctypes.cast(self._start, ctypes.c_void_p),
-                            ctypes.cast(self._cap, ctypes.c_void_p))
+                            ctypes.cast(self._cap, ctypes.c_void_p),
+                            ctypes.cast(self._ks, ctypes.c_void_p) if self._ks else None,
+                            ctypes.cast(self._vs, ctypes.c_void_p) if self._vs else None)
+
+    def scales(self, layer):
+        """(k_scale, v_scale) lists of one layer's kv heads (FP8 pools)."""
+        H = self.num_kv_heads
+        return list(self._ks[layer * H:(layer + 1) * H]), list(self._vs[layer * H:(layer + 1) * H])
 
     @property
     def num_blocks(self):
         return len(self.block_cap)
 
     # -- layout marshalling (index permutations only) --
+    def _bits(self, t):
+        # FP8 codes are moved as bytes (index permutations only)
+        return t.view(torch.uint8) if self.hw_dtype == HW_FP8 else t
+
     def store_layer(self, layer, k_logical, v_logical):
         """Write logical [Hkv, num_slots, D] K/V (pool dtype) into `layer`."""
-        self.k[layer].copy_(layout.pack_keys(k_logical.to(self.k.device, self.dtype)))
-        self.v[layer].copy_(layout.pack_values(v_logical.to(self.v.device, self.dtype)))
+        k = k_logical.to(self.k.device, self.dtype)
+        v = v_logical.to(self.v.device, self.dtype)
+        self._bits(self.k[layer]).copy_(layout.pack_keys(self._bits(k)))
+        self._bits(self.v[layer]).copy_(layout.pack_values(self._bits(v)))
 
     def load_layer(self, layer):
         """Logical [Hkv, num_slots, D] copies of `layer`'s K/V."""
-        return layout.unpack_keys(self.k[layer]), layout.unpack_values(self.v[layer])
+        k = layout.unpack_keys(self._bits(self.k[layer]))
+        v = layout.unpack_values(self._bits(self.v[layer]))
+        if self.hw_dtype == HW_FP8:
+            return k.view(self.dtype), v.view(self.dtype)
+        return k, v
 
     def set_lengths(self, lens):
         self.block_len.copy_(torch.as_tensor(lens, dtype=torch.int32))
@@ -205,7 +243,8 @@ def alloc_workspace(pool: Pool, num_workers: int, num_q_heads: int) -> torch.Ten
 def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
                    num_entries: torch.Tensor, rope_theta: float, out: torch.Tensor,
                    workspace: torch.Tensor, stream=None):
-    """q [W][Hq][D] (pool dtype), tables int32 [W][E][2], num_entries int32 [W], out fp32 [W][Hq][D]."""
+    """q [W][Hq][D] (query_dtype(pool.dtype)), tables int32 [W][E][2], num_entries int32 [W],
+    out fp32 [W][Hq][D]."""
     W, Hq, _ = q.shape
     code = lib().hw_attn_decode(ctypes.byref(pool.desc), int(layer), _ptr(q), W, Hq, _ptr(tables),
                                 int(tables.shape[1]), _ptr(num_entries), float(rope_theta),
@@ -216,7 +255,7 @@ def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor
 def hw_attn_chunk(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
                   num_entries: torch.Tensor, rope_theta: float, out: torch.Tensor,
                   workspace: torch.Tensor, stream=None):
-    """q [W][n][Hq][D] (pool dtype): each worker's last n tokens as queries, causal over the
+    """q [W][n][Hq][D] (query_dtype(pool.dtype)): each worker's last n tokens as queries, causal over the
     view; out fp32 [W][n][Hq][D]; workspace sized for W * n workers."""
     W, n, Hq, _ = q.shape
     code = lib().hw_attn_chunk(ctypes.byref(pool.desc), int(layer), _ptr(q), W, n, Hq,

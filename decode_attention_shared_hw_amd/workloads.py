@@ -11,8 +11,12 @@ Shapes (QwQ-32B / Qwen3-8B attention shapes; the pages' throughput table uses
   qwq_step  64 layers, 4 workers, common 16384, worker blocks U[256,1024]
   sweep     4/2/1 workers, total view 1024/8192/16384 (85% common)
   qwen3_loop 36 layers, 32q/8kv, 4 workers, common from 32768, appends every 64 steps
+  *_fp8     the same shapes with an FP8 E4M3 K/V pool (bf16 queries)
 Values: q ~ N(0,1); K, V ~ N(0,1) + a fixed per-(layer, kv head, channel)
-offset ~ N(0, 0.5) for the bf16 shapes (separate offsets for K and V).
+offset ~ N(0, 0.5) for the bf16 shapes (separate offsets for K and V).  FP8
+pools hold the same draws as codes of x / scale, with one scale per (layer,
+kv head) for K and one for V, amax / 448 over the head's plane (a
+calibration choice of the input generator; the pages give none).
 """
 from __future__ import annotations
 
@@ -63,14 +67,21 @@ class Workload:
         """Unique visible tokens per layer (every worker sees every block)."""
         return int(sum(self.lens))
 
+    @property
+    def q_dtype(self):
+        """fp32 queries for fp32 pools, bf16 for bf16 and FP8 pools."""
+        return torch.float32 if self.dtype == torch.float32 else torch.bfloat16
+
+    @property
+    def fp8(self):
+        return self.dtype == torch.float8_e4m3fn
+
     def kv_bytes_per_layer(self):
-        es = 2 if self.dtype == torch.bfloat16 else 4
-        return self.tokens * self.Hkv * self.D * 2 * es
+        return self.tokens * self.Hkv * self.D * 2 * self.dtype.itemsize
 
     def algorithmic_bytes_per_layer(self):
         """Each visible K/V token read once + q read + out (fp32) written."""
-        es = 2 if self.dtype == torch.bfloat16 else 4
-        return self.kv_bytes_per_layer() + self.W * self.Hq * self.D * (es + 4)
+        return self.kv_bytes_per_layer() + self.W * self.Hq * self.D * (self.q_dtype.itemsize + 4)
 
 
 def tiny(seed: int = 1001) -> Workload:
@@ -138,20 +149,50 @@ def _gen(seed: int, layer: int, tag: int, device) -> torch.Generator:
     return g
 
 
+def with_fp8(wl: Workload) -> Workload:
+    """The same workload over an FP8 E4M3 pool (same draws, same seed)."""
+    return dataclasses.replace(wl, name=wl.name.replace("bf16", "fp8"), dtype=torch.float8_e4m3fn)
+
+
 def make_q(wl: Workload, layer: int, device="cpu") -> torch.Tensor:
-    """q [W][Hq][D] in the pool dtype, N(0,1)."""
+    """q [W][Hq][D] in the query dtype of the pool, N(0,1)."""
     g = _gen(wl.seed, layer, 1, device)
     q = torch.randn(wl.W, wl.Hq, wl.D, generator=g, device=device, dtype=torch.float32)
-    return q.to(wl.dtype)
+    return q.to(wl.q_dtype)
 
 
 def make_kv(wl: Workload, layer: int, num_slots: int, device="cpu", poison_unused: bool = False,
             block_start=None):
-    """Logical K, V [Hkv][num_slots][D] in the pool dtype.
+    """Logical K, V [Hkv][num_slots][D] in the pool dtype (FP8 pools: make_kv_fp8).
 
     poison_unused: slots outside every block's current length hold NaN (they
     must never reach a result).
     """
+    if wl.fp8:
+        raise ValueError("FP8 workloads: use make_kv_fp8 (codes and scales)")
+    K, V = _draw_kv(wl, layer, num_slots, device, poison_unused, block_start)
+    return K.to(wl.dtype), V.to(wl.dtype)
+
+
+def make_kv_fp8(wl: Workload, layer: int, num_slots: int, device="cpu",
+                poison_unused: bool = False, block_start=None):
+    """FP8 E4M3 pools: logical K, V codes [Hkv][num_slots][D] (torch.float8_e4m3fn)
+    of the same draws as make_kv, and per kv head scales k_scale, v_scale [Hkv]
+    (amax of the head's plane / 448, so that no code saturates).  The stored
+    value is code * scale."""
+    K, V = _draw_kv(wl, layer, num_slots, device, poison_unused, block_start)
+
+    def quant(X):
+        amax = torch.nan_to_num(X.abs(), nan=0.0).amax(dim=(1, 2))
+        scale = (amax / 448.0).clamp_min(2.0 ** -20)
+        return (X / scale[:, None, None]).to(torch.float8_e4m3fn), scale.float().cpu()
+
+    K8, ks = quant(K)
+    V8, vs = quant(V)
+    return K8, V8, ks, vs
+
+
+def _draw_kv(wl: Workload, layer: int, num_slots: int, device, poison_unused, block_start):
     gk = _gen(wl.seed, layer, 2, device)
     gv = _gen(wl.seed, layer, 3, device)
     shape = (wl.Hkv, num_slots, wl.D)
@@ -168,7 +209,7 @@ def make_kv(wl: Workload, layer: int, num_slots: int, device="cpu", poison_unuse
             used[int(starts[b]):int(starts[b]) + int(n)] = True
         K[:, ~used] = float("nan")
         V[:, ~used] = float("nan")
-    return K.to(wl.dtype), V.to(wl.dtype)
+    return K, V
 
 
 def summary(wl: Workload) -> dict:
@@ -176,9 +217,10 @@ def summary(wl: Workload) -> dict:
         "workload": wl.name, "workers": wl.W, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
         "head_dim": wl.D, "rope_theta": wl.theta, "layers": wl.layers,
         "block_lens": [int(x) for x in wl.lens], "tokens": wl.tokens,
-        "kv_dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "kv_dtype": {torch.bfloat16: "bf16", torch.float32: "f32",
+                     torch.float8_e4m3fn: "fp8_e4m3"}[wl.dtype],
     }
 
 
 __all__ = ["Workload", "tiny", "qwq_layer", "qwq_step", "sweep", "qwen3_loop", "loop_appends",
-           "make_q", "make_kv", "summary", "round_up"]
+           "with_fp8", "make_q", "make_kv", "make_kv_fp8", "summary", "round_up"]

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define HW_ABI_VERSION 1
+#define HW_ABI_VERSION 2
 
 /* Tokens per tile of the pool layout; block starts and capacities are multiples of it. */
 #define HW_TILE_TOKENS 32
@@ -60,6 +60,7 @@ extern "C" {
 #define HW_MAX_WORKERS 32  /* workers per decode call                  */
 #define HW_MAX_ROWS 64     /* num_workers * (num_q_heads / num_kv_heads) */
 #define HW_MAX_ENTRIES 64  /* entries per worker table                 */
+#define HW_MAX_FP8_KV_HEADS 64 /* kv heads of an HW_FP8 pool             */
 
 typedef int32_t hw_status;
 #define HW_OK 0
@@ -80,6 +81,15 @@ typedef int32_t hw_status;
 /* Storage types. */
 #define HW_F32 0
 #define HW_BF16 1
+/*
+ * HW_FP8: OCP FP8 E4M3 ("e4m3fn": bias 7, 3 mantissa bits, subnormals, no
+ * infinity, 0x7f/0xff NaN, largest finite 448), one byte per element, with a
+ * per-(layer, kv head) scale for keys and one for values: the stored value
+ * is code * scale.  This is the FP8 attention of the mixed-precision item of
+ * news 1114328 sec. 6; the pages give no format, so OCP E4M3, the FP8 format
+ * of the MI355X matrix cores, is used.  Queries stay bf16.
+ */
+#define HW_FP8 2
 
 /* One entry of a worker's view: block id and where the block starts in the view. */
 typedef struct {
@@ -104,7 +114,8 @@ typedef struct {
  *                                       + (t % 16) * 8 + d % 8
  *   value element (slot, d) at tile base + ((t % 16) / 4) * 8 * D + d * 8
  *                                       + (t / 16) * 4 + t % 4
- * The same layout is used for fp32 pools.
+ * The same layout is used for fp32 and FP8 pools (element offsets are equal;
+ * an FP8 fragment is 8 bytes).
  *
  * block_len is device memory and is changed by hw_block_append /
  * hw_block_reset; block_start and block_cap are host arrays and fixed for the
@@ -125,6 +136,10 @@ typedef struct {
   int32_t* status;      /* (device) sticky HW_DEV_* bits                   */
   const int64_t* block_start; /* (host) [num_blocks], multiples of 32      */
   const int32_t* block_cap;   /* (host) [num_blocks], multiples of 32      */
+  /* (host) [num_layers][num_kv_heads] positive finite scales of an HW_FP8
+   * pool (key and value); NULL for the other types.  Read at each call. */
+  const float* k_scale;
+  const float* v_scale;
 } hw_pool;
 
 /* Returns HW_ABI_VERSION. */
@@ -148,8 +163,9 @@ size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t
 /*
  * One layer of concurrent-attention decode (key design 1; news 1114328 sec. 3.2).
  *
- *   q            (device) [num_workers][num_q_heads][head_dim], pool dtype: the
- *                one current query token of each worker, before RoPE.
+ *   q            (device) [num_workers][num_q_heads][head_dim], fp32 for fp32
+ *                pools, bf16 for bf16 and FP8 pools: the one current query
+ *                token of each worker, before RoPE.
  *   tables       (device) [num_workers][max_entries] views; worker w uses its
  *                first num_entries[w] entries.  A block not listed is invisible
  *                to w; a block may be listed at most once per worker.
@@ -160,9 +176,12 @@ size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t
  * For each worker w and q-head h (kv head g = h / (Hq/Hkv)):
  *   out[w][h] = sum over entries (b, off) and j < len_b of
  *       softmax_j( rho(q[w][h], i_q[w] - off) . K_b[g][j] / sqrt(D) ) V_b[g][j].
+ * FP8 pools: K and V are code * scale of their (layer, kv head); the
+ * products run on the bf16 matrix cores with the codes widened exactly.
  * Host-checked errors: HW_EINVAL (null pointers, num_q_heads % num_kv_heads,
  * layer out of range, max_entries < 1), HW_ERANGE (limits above),
- * HW_EUNSUPPORTED (head_dim), HW_EWORKSPACE, HW_EHIP (launch failure).
+ * HW_EUNSUPPORTED (head_dim; FP8 pools with more than 32 stacked rows or the
+ * VALU path forced), HW_EWORKSPACE, HW_EHIP (launch failure).
  */
 hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
                          int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
@@ -175,7 +194,7 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
  * whose K/V are already stored).  Query j of worker w sits at view position
  * i_q[w] - (chunk - 1 - j) and sees the view's tokens at positions up to its
  * own (a causal mask over the view); chunk = 1 is hw_attn_decode.
- *   q    (device) [num_workers][chunk][num_q_heads][head_dim], pool dtype.
+ *   q    (device) [num_workers][chunk][num_q_heads][head_dim], dtype as for decode.
  *   out  (device) [num_workers][chunk][num_q_heads][head_dim] fp32.
  *   workspace: hw_attn_workspace_bytes(pool, num_workers * chunk, num_q_heads).
  * Other arguments, errors and limits as hw_attn_decode, with
@@ -195,7 +214,9 @@ hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32
  * j < n, dst token m + j receives the src key re-encoded at local position
  * m + j (rotated by m with fp64 intermediates, rounded to nearest-even in the
  * pool type) and the src value unchanged; then block_len[dst] = m + n and
- * block_len[src] = 0.  src data is left in place.
+ * block_len[src] = 0.  src data is left in place.  FP8 pools: src and dst
+ * share the plane's key scale, so the codes are rotated and rounded to the
+ * nearest E4M3 code (saturating at 448).
  * Host-checked: HW_EINVAL (ids, src == dst), HW_ECAPACITY (cap_src > cap_dst
  * is allowed; only the run-time lengths decide, see HW_DEV_APPEND_OVERFLOW).
  */
@@ -221,7 +242,8 @@ hw_status hw_block_advance(const hw_pool* pool, int32_t n, const int32_t* blocks
  * key design 1: a block holds its keys at positions 0..len-1): key slot p of
  * kv head h receives rho(k_new[i][h], p), computed with fp64 intermediates and
  * rounded to nearest even in the pool type; value slot p receives v_new[i][h]
- * rounded the same way.  Lengths are not changed.  A listed block of length 0
+ * rounded the same way (FP8 pools: the codes nearest to x / scale of the
+ * layer's kv head, saturating at 448).  Lengths are not changed.  A listed block of length 0
  * is skipped and sets HW_DEV_WRITE_OVERFLOW.
  *   blocks (host) [n], as for hw_block_advance.
  *   k_new, v_new (device) [n][num_kv_heads][head_dim] fp32.
@@ -273,7 +295,8 @@ hw_status hw_pool_status(const hw_pool* pool, int32_t* flags, int32_t clear);
 
 /*
  * Process-wide tuning (not thread-safe against concurrent decode calls).
- *   path:           0 auto, 1 VALU fp32 kernel, 2 MFMA bf16 kernel (bf16 pools).
+ *   path:           0 auto, 1 VALU fp32 kernel (fp32 and bf16 pools), 2 MFMA
+ *                   bf16 kernel (bf16 and FP8 pools).
  *   units_per_head: number of split-K work units per kv head; 0 = automatic.
  * Returns HW_EINVAL for values out of range.
  */

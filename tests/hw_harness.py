@@ -33,21 +33,42 @@ def assert_close(got, ref, dtype, what=""):
 
 
 class Setup:
-    """A device pool filled from a workload (layers [0, n_layers)) plus host copies."""
+    """A device pool filled from a workload (layers [0, n_layers)) plus host copies.
+
+    K, V: the stored values per layer (FP8 pools: code * scale in float64);
+    K8, V8, k_scale, v_scale: the FP8 codes and scales (FP8 pools only)."""
 
     def __init__(self, wl: workloads.Workload, n_layers: int = 1, poison_unused=False,
                  gen_device="cpu"):
         self.wl = wl
-        self.pool = hw.Pool(n_layers, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
-        self.pool.set_lengths(wl.lens)
-        self.K, self.V, self.q = [], [], []
+        slots = sum(wl.caps)
+        starts = list(np.cumsum([0] + list(wl.caps[:-1])))
+        draws = []
         for layer in range(n_layers):
-            K, V = workloads.make_kv(wl, layer, self.pool.num_slots, device=gen_device,
-                                     poison_unused=poison_unused,
-                                     block_start=self.pool.block_start)
+            if wl.fp8:
+                draws.append(workloads.make_kv_fp8(wl, layer, max(slots, 32), device=gen_device,
+                                                   poison_unused=poison_unused, block_start=starts))
+            else:
+                draws.append(workloads.make_kv(wl, layer, max(slots, 32), device=gen_device,
+                                               poison_unused=poison_unused, block_start=starts))
+        self.k_scale = torch.stack([d[2] for d in draws]) if wl.fp8 else None
+        self.v_scale = torch.stack([d[3] for d in draws]) if wl.fp8 else None
+        self.pool = hw.Pool(n_layers, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype,
+                            k_scale=self.k_scale, v_scale=self.v_scale)
+        assert self.pool.block_start == starts and self.pool.num_slots == max(slots, 32)
+        self.pool.set_lengths(wl.lens)
+        self.K, self.V, self.q, self.K8, self.V8 = [], [], [], [], []
+        for layer, d in enumerate(draws):
+            K, V = d[0], d[1]
             self.pool.store_layer(layer, K, V)
-            self.K.append(K.cpu())
-            self.V.append(V.cpu())
+            if wl.fp8:
+                self.K8.append(K.cpu())
+                self.V8.append(V.cpu())
+                self.K.append(K.cpu().double() * d[2].double()[:, None, None])
+                self.V.append(V.cpu().double() * d[3].double()[:, None, None])
+            else:
+                self.K.append(K.cpu())
+                self.V.append(V.cpu())
             self.q.append(workloads.make_q(wl, layer, device=gen_device).cpu())
         self.tables = torch.zeros(wl.W, wl.W + 1, 2, dtype=torch.int32, device="cuda")
         self.num_entries = torch.zeros(wl.W, dtype=torch.int32, device="cuda")

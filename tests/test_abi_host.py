@@ -37,30 +37,35 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert hw.hw_abi_version() == 1
+    assert hw.hw_abi_version() == 2
     assert hw.hw_status_str(hw.HW_OK) == "ok"
     assert "workspace" in hw.hw_status_str(hw.HW_EWORKSPACE)
 
 
 def test_struct_layout_matches_header(lib):
     assert ctypes.sizeof(hw.hw_entry) == 8
-    # 6 int32 + int64 + 6 pointers
-    assert ctypes.sizeof(hw.hw_pool) == 6 * 4 + 8 + 6 * 8
+    # 6 int32 + int64 + 8 pointers
+    assert ctypes.sizeof(hw.hw_pool) == 6 * 4 + 8 + 8 * 8
     assert hw.hw_pool.num_slots.offset == 24 and hw.hw_pool.k.offset == 32
+    assert hw.hw_pool.k_scale.offset == 80 and hw.hw_pool.v_scale.offset == 88
 
 
 class FakePool:
     """A pool descriptor whose device pointers are never dereferenced (host checks only)."""
 
     def __init__(self, dtype=hw.HW_BF16, D=128, caps=(64, 32, 32), starts=None, Hkv=2, layers=1,
-                 slots=None):
+                 slots=None, k_scale=None, v_scale=None):
         starts = starts if starts is not None else list(np.cumsum([0] + list(caps[:-1])))
         self._s = (ctypes.c_int64 * len(caps))(*starts)
         self._c = (ctypes.c_int32 * len(caps))(*caps)
         slots = slots if slots is not None else int(sum(caps))
+        self._ks = (ctypes.c_float * len(k_scale))(*k_scale) if k_scale is not None else None
+        self._vs = (ctypes.c_float * len(v_scale))(*v_scale) if v_scale is not None else None
         self.desc = hw.hw_pool(dtype, layers, Hkv, D, len(caps), 0, slots, 0x1000, 0x2000,
                                0x3000, 0x4000, ctypes.cast(self._s, ctypes.c_void_p),
-                               ctypes.cast(self._c, ctypes.c_void_p))
+                               ctypes.cast(self._c, ctypes.c_void_p),
+                               ctypes.cast(self._ks, ctypes.c_void_p) if self._ks else None,
+                               ctypes.cast(self._vs, ctypes.c_void_p) if self._vs else None)
 
 
 def decode_rc(lib, pool, layer=0, W=2, Hq=4, E=3, theta=1e4, ws_bytes=1 << 30, ptr=0x5000):
@@ -187,3 +192,25 @@ def test_chunk_host_validation(lib):
     assert call(2, 16, 3) == hw.HW_EINVAL         # Hq % Hkv
     assert lib.hw_attn_workspace_bytes(P, 64, 2) > 0      # 64 stacked rows (chunk of 64, G = 1)
     assert lib.hw_attn_workspace_bytes(P, 65, 2) == 0
+
+
+def test_fp8_pool_host_validation(lib):
+    """FP8 pools need positive finite scales for every (layer, kv head), at most
+    HW_MAX_FP8_KV_HEADS kv heads, and run on the MFMA kernel only (<= 32 rows)."""
+    good = [0.5, 0.25]
+    assert decode_rc(lib, FakePool(dtype=hw.HW_FP8)) == hw.HW_EINVAL                # no scales
+    assert decode_rc(lib, FakePool(dtype=hw.HW_FP8, k_scale=good)) == hw.HW_EINVAL  # no v scales
+    for bad in ([0.5, 0.0], [0.5, -1.0], [float("nan"), 1.0], [float("inf"), 1.0]):
+        assert decode_rc(lib, FakePool(dtype=hw.HW_FP8, k_scale=bad, v_scale=good)) == hw.HW_EINVAL
+        assert decode_rc(lib, FakePool(dtype=hw.HW_FP8, k_scale=good, v_scale=bad)) == hw.HW_EINVAL
+    many = [1.0] * 65
+    assert decode_rc(lib, FakePool(dtype=hw.HW_FP8, Hkv=65, k_scale=many, v_scale=many),
+                     Hq=65) == hw.HW_ERANGE
+    fp8 = FakePool(dtype=hw.HW_FP8, k_scale=good, v_scale=good)
+    assert decode_rc(lib, fp8, W=17, Hq=4) == hw.HW_EUNSUPPORTED   # 34 rows > 32
+    try:
+        hw.hw_set_tuning(hw.PATH_VALU, 0)
+        assert decode_rc(lib, fp8) == hw.HW_EUNSUPPORTED
+    finally:
+        hw.hw_set_tuning(hw.PATH_AUTO, 0)
+    assert lib.hw_attn_workspace_bytes(ctypes.byref(fp8.desc), 2, 4) > 0

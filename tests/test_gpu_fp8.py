@@ -1,0 +1,226 @@
+"""GPU parity of FP8 E4M3 pools (the mixed-precision item of news 1114328 sec. 6)
+against the CPU oracle, through the C ABI.
+
+Attention: the oracle attends over the stored values (code * scale, exact in
+fp64) with the same bf16 queries; the GPU must stay within the bf16 bar
+(5e-3 max-abs, 1e-2 relative L2).  Append and token write: the stored codes
+are bit-exact against the oracle's nearest-even E4M3 rounding.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_shared_hw_amd import hogwild_attn as hw
+from decode_attention_shared_hw_amd import workloads
+from hw_harness import Setup, assert_close, errors
+
+pytestmark = pytest.mark.gpu
+
+FP8 = torch.float8_e4m3fn
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _tuning(request):
+    _say(f"[case] {request.node.name}")
+    yield
+    hw.hw_set_tuning(hw.PATH_AUTO, 0)
+
+
+def _custom(W, Hq, Hkv, D, lens, theta=1e6, caps=None, sigma=0.5, seed=7, layers=1):
+    caps = caps or [workloads.round_up(max(x, 1)) for x in lens]
+    return workloads.Workload(f"custom_fp8_W{W}_G{Hq // Hkv}_D{D}", W, Hq, Hkv, D, theta, FP8,
+                              layers, list(lens), list(caps), sigma, seed)
+
+
+def test_fp8_qwq_layer_matches_oracle():
+    s = Setup(workloads.with_fp8(workloads.qwq_layer()))
+    ref, rc = s.oracle_decode()
+    assert rc == 0
+    got = s.decode()
+    ma, rl = assert_close(got, ref, FP8, "qwq layer fp8")
+    # informational: the distance to attention over the unquantized bf16 pool
+    sb = Setup(workloads.qwq_layer())
+    refb, _ = sb.oracle_decode()
+    qa, ql = errors(got, refb)
+    _say(f"  fp8 vs oracle: max_abs {ma:.2e} rel_l2 {rl:.2e}; vs bf16 pool: {qa:.2e} / {ql:.2e}")
+
+
+@pytest.mark.parametrize("case", [
+    # (W, Hq, Hkv, D, lens)
+    (1, 1, 1, 64, [1, 0]),
+    (1, 8, 1, 128, [31, 0, 5]),
+    (3, 6, 2, 64, [100, 1, 0, 45]),
+    (2, 16, 2, 128, [300, 7, 33]),       # 16 rows
+    (8, 32, 8, 128, [5000] + [17] * 8),  # 32 rows
+    (4, 40, 8, 128, [2047, 511, 2, 64, 96]),
+])
+def test_fp8_ragged_shapes_match_oracle(case):
+    W, Hq, Hkv, D, lens = case
+    s = Setup(_custom(W, Hq, Hkv, D, lens), poison_unused=True)
+    ref, rc = s.oracle_decode()
+    assert rc == 0
+    got = s.decode()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, FP8, f"fp8 {case}")
+    assert hw.hw_pool_status(s.pool) == 0
+
+
+def test_fp8_single_visible_token_returns_its_value():
+    s = Setup(_custom(2, 4, 2, 128, [1, 0, 0]))
+    got = s.decode()
+    V = s.V[0]
+    for w in range(2):
+        for h in range(4):
+            # one visible token: its value (code * scale) up to the fp32 scale product
+            np.testing.assert_allclose(got[w, h], V[h // 2, 0].numpy(), rtol=1e-6, atol=0)
+
+
+def test_fp8_chunk_matches_oracle():
+    W, n, Hq, Hkv, D, lens = 2, 3, 40, 8, 128, [4000, 333, 517]
+    wl = _custom(W, Hq, Hkv, D, lens)
+    s = Setup(wl, poison_unused=True)
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn(W, n, Hq, D, generator=g).to(torch.bfloat16)
+    out = torch.full((W, n, Hq, D), float("nan"), device="cuda")
+    ws = hw.alloc_workspace(s.pool, W * n, Hq)
+    hw.hw_attn_chunk(s.pool, 0, q.cuda(), s.tables, s.num_entries, wl.theta, out, ws)
+    torch.cuda.synchronize()
+    tb, to, ne = s.oracle_tables()
+    ref, rc = oracle.attn_chunk(oracle.FORM_METHOD, q.double().numpy(), s.K[0].numpy(),
+                                s.V[0].numpy(), tb, to, ne, np.array(lens, np.int32),
+                                np.asarray(s.pool.block_start, np.int64), wl.theta)
+    assert rc == 0
+    assert_close(out.cpu().numpy(), ref, FP8, "fp8 chunk")
+
+
+def test_fp8_unit_count_does_not_change_the_result():
+    s = Setup(_custom(4, 40, 8, 128, [3000, 100, 200, 64, 5]))
+    ref, _ = s.oracle_decode()
+    for units in (1, 3, 16, 64):
+        hw.hw_set_tuning(hw.PATH_AUTO, units)
+        got = s.decode()
+        assert_close(got, ref, FP8, f"units {units}")
+
+
+def test_fp8_append_matches_oracle_bit_exact():
+    theta = 1e6
+    lens = [1000, 333, 17, 64]
+    wl = workloads.Workload("append_fp8", 3, 6, 2, 128, theta, FP8, 2, lens,
+                            [2048, 352, 32, 64], 0.5, 11)
+    s = Setup(wl, n_layers=2)
+    src, dst = 1, 0
+    Ko = np.stack([k.numpy() for k in s.K])
+    Vo = np.stack([v.numpy() for v in s.V])
+    lo = np.array(lens, np.int32)
+    rc = oracle.block_append(Ko, Vo, s.pool.block_start, s.pool.block_cap, lo, src, dst, theta,
+                             oracle.HWO_FP8, k_scale=s.k_scale.double().numpy())
+    assert rc == 0
+    hw.hw_block_append(s.pool, src, dst, theta)
+    torch.cuda.synchronize()
+    assert s.pool.block_len.cpu().tolist() == lo.tolist()
+    for layer in range(2):
+        K8, V8 = s.pool.load_layer(layer)
+        Kg = K8.cpu().double().numpy() * s.k_scale[layer].double().numpy()[:, None, None]
+        Vg = V8.cpu().double().numpy() * s.v_scale[layer].double().numpy()[:, None, None]
+        assert np.array_equal(Vg, Vo[layer])
+        assert np.array_equal(Kg, Ko[layer]), int((Kg != Ko[layer]).sum())
+
+
+def test_fp8_append_then_review_attention_is_nearly_unchanged():
+    """src right after common in worker 0's view: the append re-rounds keys to the
+    E4M3 grid, so attention moves by no more than that rounding allows."""
+    wl = _custom(2, 8, 2, 128, [700, 45, 300], caps=[1024, 64, 320])
+    s = Setup(wl)
+    before = s.decode()
+    hw.hw_block_append(s.pool, 2, 0, wl.theta)
+    hw.hw_build_combined_tables(s.pool, wl.W, 0, wl.worker_block, s.tables, s.num_entries)
+    after = s.decode()
+    assert s.pool.block_len.cpu().tolist() == [1000, 45, 0]
+    assert np.abs(after[0] - before[0]).max() < 3e-2
+
+
+def test_fp8_token_write_matches_oracle_bit_exact():
+    theta = 1e6
+    lens = [300, 31, 64, 0]
+    wl = workloads.Workload("write_fp8", 3, 6, 2, 128, theta, FP8, 2, lens, [512, 64, 96, 32], 0.5,
+                            13)
+    s = Setup(wl, n_layers=2)
+    blocks = [1, 2, 3]
+    g = torch.Generator().manual_seed(5)
+    kn = [torch.randn(3, wl.Hkv, wl.D, generator=g) * 3.0 for _ in range(2)]
+    vn = [torch.randn(3, wl.Hkv, wl.D, generator=g) for _ in range(2)]
+    hw.hw_block_advance(s.pool, blocks)
+    for layer in range(2):
+        hw.hw_block_write(s.pool, layer, blocks, kn[layer].cuda(), vn[layer].cuda(), theta)
+    torch.cuda.synchronize()
+    lo = np.array(lens, np.int32)
+    lo[blocks] += 1
+    assert s.pool.block_len.cpu().tolist() == lo.tolist()
+    assert hw.hw_pool_status(s.pool) == 0
+    for layer in range(2):
+        ks = s.k_scale[layer].double().numpy()
+        vs = s.v_scale[layer].double().numpy()
+        Ko, Vo = s.K[layer].numpy().copy(), s.V[layer].numpy().copy()
+        rc = oracle.block_write(Ko, Vo, s.pool.block_start, lo, blocks, kn[layer].double().numpy(),
+                                vn[layer].double().numpy(), theta, oracle.HWO_FP8, k_scale=ks,
+                                v_scale=vs)
+        assert rc == 0
+        K8, V8 = s.pool.load_layer(layer)
+        Kg = K8.cpu().double().numpy() * ks[:, None, None]
+        Vg = V8.cpu().double().numpy() * vs[:, None, None]
+        assert np.array_equal(Vg, Vo) and np.array_equal(Kg, Ko)
+
+
+def test_fp8_step_full_size_sampled():
+    """64-layer FP8 pool of the 16K / 4-worker step, outputs sampled against the oracle."""
+    wl = workloads.with_fp8(workloads.qwq_step())
+    pool_slots = sum(wl.caps)
+    starts = list(np.cumsum([0] + list(wl.caps[:-1])))
+    sample_layers = [0, 63]
+    draws, host = [], {}
+    ks_all, vs_all = [], []
+    for layer in range(wl.layers):
+        K8, V8, ks, vs = workloads.make_kv_fp8(wl, layer, pool_slots, device="cuda",
+                                               block_start=starts)
+        ks_all.append(ks)
+        vs_all.append(vs)
+        draws.append((K8, V8))
+        if layer in sample_layers:
+            host[layer] = (K8.cpu().double() * ks.double()[:, None, None],
+                           V8.cpu().double() * vs.double()[:, None, None],
+                           workloads.make_q(wl, layer, device="cuda").cpu())
+    pool = hw.Pool(wl.layers, wl.Hkv, wl.D, wl.caps, dtype=FP8, k_scale=torch.stack(ks_all),
+                   v_scale=torch.stack(vs_all))
+    pool.set_lengths(wl.lens)
+    for layer, (K8, V8) in enumerate(draws):
+        pool.store_layer(layer, K8, V8)
+    del draws
+    tables = torch.zeros(wl.W, wl.W + 1, 2, dtype=torch.int32, device="cuda")
+    ne = torch.zeros(wl.W, dtype=torch.int32, device="cuda")
+    hw.hw_build_combined_tables(pool, wl.W, 0, wl.worker_block, tables, ne)
+    ws = hw.alloc_workspace(pool, wl.W, wl.Hq)
+    tb, to, one = oracle.build_combined_tables(0, wl.worker_block, wl.lens)
+    rng = np.random.default_rng(0)
+    for layer in sample_layers:
+        K, V, q = host[layer]
+        out = torch.empty(wl.W, wl.Hq, wl.D, device="cuda")
+        hw.hw_attn_decode(pool, layer, q.cuda(), tables, ne, wl.theta, out, ws)
+        got = out.cpu().numpy()
+        for _ in range(4):
+            w, h = int(rng.integers(wl.W)), int(rng.integers(wl.Hq))
+            g = h // wl.G
+            ref, rc = oracle.attn_one(oracle.FORM_METHOD, q[w, h].double().numpy(), K[g].numpy(),
+                                      V[g].numpy(), tb[w], to[w], np.asarray(wl.lens, np.int32),
+                                      np.asarray(pool.block_start, np.int64), wl.theta)
+            assert rc == 0
+            ma, rl = errors(got[w, h], ref)
+            assert ma <= 5e-3 and rl <= 1e-2, (layer, w, h, ma, rl)
+    assert hw.hw_pool_status(pool) == 0
