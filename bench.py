@@ -82,6 +82,8 @@ def parse():
                          "grid, per-layer time on both paths; loop: 36-layer generation loop "
                          "with appends")
     ap.add_argument("--loop-steps", type=int, default=2048)
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 E4M3 pool variant of the step (reported as fp8_step)")
     return ap.parse_args()
 
 
@@ -288,49 +290,52 @@ def cpu_baseline(wl, pool_block_start, K, V, q, pairs):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(multi-GPU sharding is design-only, see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
-
+def make_step_pool(hw, torch, workloads, wl, keep_layer0):
+    """Device pool of every layer of `wl` (bf16 or FP8 codes with scales), its
+    queries, output and tables; the host copy of layer 0 when asked."""
     import numpy as np
-    import torch
 
-    from decode_attention_shared_hw_amd import hogwild_attn as hw
-    from decode_attention_shared_hw_amd import workloads
-
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    hw.lib()  # fail loudly if the library is missing
-    if args.config == "sweep":
-        return run_sweep(args)
-    if args.config == "loop":
-        return run_loop(args)
-    path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
-    hw.hw_set_tuning(path, args.units)
-
-    wl = workloads.qwq_step(layers=args.layers)
-    L, W = wl.layers, wl.W
-    pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
-    pool.set_lengths(wl.lens)
-    saved_lens = pool.block_len.clone()
+    L = wl.layers
     host_layer0 = None
+    draws, ks_all, vs_all = [], [], []
+    slots = sum(wl.caps)
+    starts = [int(x) for x in np.cumsum([0] + list(wl.caps[:-1]))]
+    pool = None
+    if not wl.fp8:
+        pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
     for layer in range(L):
-        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
-        pool.store_layer(layer, K, V)
-        if layer == 0 and not args.no_cpu_baseline:
-            host_layer0 = (K.cpu(), V.cpu())
-        del K, V
+        if wl.fp8:
+            K, V, ks, vs = workloads.make_kv_fp8(wl, layer, slots, device="cuda", block_start=starts)
+            draws.append((K, V))
+            ks_all.append(ks)
+            vs_all.append(vs)
+        else:
+            K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+            pool.store_layer(layer, K, V)
+            if layer == 0 and keep_layer0:
+                host_layer0 = (K.cpu(), V.cpu())
+            del K, V
+    if wl.fp8:
+        pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype, k_scale=torch.stack(ks_all),
+                       v_scale=torch.stack(vs_all))
+        for layer, (K, V) in enumerate(draws):
+            pool.store_layer(layer, K, V)
+        del draws
+    pool.set_lengths(wl.lens)
     q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
+    return pool, q, host_layer0
+
+
+def time_step(args, hw, torch, np, wl, pool, q):
+    """Graph (or eager) replay of the step, then per-launch HIP-event durations of
+    the decode calls and the append in an eager replay behind a GPU spin."""
+    L, W = wl.layers, wl.W
+    saved_lens = pool.block_len.clone()
     out = torch.zeros(L, W, wl.Hq, wl.D, dtype=torch.float32, device="cuda")
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
     ws = hw.alloc_workspace(pool, W, wl.Hq)
     torch.cuda.synchronize()
-
     stream = torch.cuda.Stream()
     counter = [0]
 
@@ -397,7 +402,38 @@ def main():
             dec_us += [a.elapsed_time(b) * 1e3 for a, b in evs["dec"]]
             app_us.append(evs["app"][0].elapsed_time(evs["app"][1]) * 1e3)
     torch.cuda.synchronize()
-    flags = hw.hw_pool_status(pool)
+    return {"ms_per_step": gpu_ms / args.steps, "dec_us": dec_us, "app_us": app_us, "wall": wall,
+            "flags": hw.hw_pool_status(pool), "graph": use_graph}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(multi-GPU sharding is design-only, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_shared_hw_amd import hogwild_attn as hw
+    from decode_attention_shared_hw_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    hw.lib()  # fail loudly if the library is missing
+    if args.config == "sweep":
+        return run_sweep(args)
+    if args.config == "loop":
+        return run_loop(args)
+    path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
+    hw.hw_set_tuning(path, args.units)
+
+    wl = workloads.qwq_step(layers=args.layers)
+    L, W = wl.layers, wl.W
+    pool, q, host_layer0 = make_step_pool(hw, torch, workloads, wl, not args.no_cpu_baseline)
+    t = time_step(args, hw, torch, np, wl, pool, q)
     if args.calibrate_copy > 0:
         # one plain copy of a known size: HBM counters of this dispatch scale
         # the decode kernel's counters (bytes read = bytes written = MIB MiB)
@@ -409,12 +445,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ms_per_step = gpu_ms / args.steps
+    ms_per_step = t["ms_per_step"]
     step_s = ms_per_step / 1e3
     value = W * L / step_s  # worker-tokens/s per layer
+    dec_us = t["dec_us"]
     dec_avg = float(np.mean(dec_us))
     bytes_per_launch = wl.algorithmic_bytes_per_layer()
     achieved = bytes_per_launch / (dec_avg * 1e-6) / 1e9
+    use_graph = t["graph"]
     result = {
         "metric": "worker-tokens/s per layer + achieved HBM GB/s (% of peak), 4 workers, 16K",
         "value": value,
@@ -443,15 +481,34 @@ def main():
             "p90_us": float(np.percentile(dec_us, 90)),
         },
         "us_per_layer": ms_per_step * 1e3 / L,
-        "append_us": float(np.mean(app_us)),
-        "wall_s": wall,
-        "device_status": flags,
+        "append_us": float(np.mean(t["app_us"])),
+        "wall_s": t["wall"],
+        "device_status": t["flags"],
     }
     if not args.no_cpu_baseline:
         K0, V0 = host_layer0
         result["cpu_baseline"] = cpu_baseline(wl, pool.block_start, K0, V0, q[0].cpu(),
                                               args.cpu_pairs)
         result["cpu_baseline"]["host"] = platform.processor() or platform.machine()
+    if not args.no_fp8 and path != hw.PATH_VALU:
+        # the same step over an FP8 E4M3 pool (half the K/V bytes; a separate
+        # numerics contract: bf16 queries, codes widened exactly)
+        del pool, q
+        torch.cuda.empty_cache()
+        wl8 = workloads.with_fp8(wl)
+        pool8, q8, _ = make_step_pool(hw, torch, workloads, wl8, False)
+        t8 = time_step(args, hw, torch, np, wl8, pool8, q8)
+        d8 = float(np.mean(t8["dec_us"]))
+        b8 = wl8.algorithmic_bytes_per_layer()
+        result["fp8_step"] = {
+            "workload": wl8.name, "kv_dtype": "fp8_e4m3 (per-(layer, kv head) scales)",
+            "value": W * L / (t8["ms_per_step"] / 1e3), "unit": "worker-tokens/s per layer",
+            "ms_per_step": t8["ms_per_step"], "us_per_layer": t8["ms_per_step"] * 1e3 / L,
+            "decode_avg_launch_us": d8, "bytes_per_launch": b8,
+            "achieved_gbs": b8 / (d8 * 1e-6) / 1e9,
+            "frac_of_peak": b8 / (d8 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "append_us": float(np.mean(t8["app_us"])), "device_status": t8["flags"],
+        }
     print(json.dumps(result), flush=True)
 
 

@@ -155,9 +155,14 @@ __device__ __forceinline__ void plan_entry(const DecodeArgs& a, Plan& p, int i, 
 // prologue is kept short and rolled: block-level work runs on wave 0 with one
 // lane per block, table entries on one thread each.
 // issue(): the kernel's own loads, issued with the plan's; commit(): their
-// LDS stores, run once they have arrived.
-template <int NTHR, typename Issue, typename Commit>
-__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
+// LDS stores, run once they have arrived.  NTHR threads (the first NTHR of
+// the workgroup) take part; sync() is their barrier.
+struct WorkgroupBarrier {
+  __device__ void operator()() const { __syncthreads(); }
+};
+
+template <int NTHR, typename Issue, typename Commit, typename Sync>
+__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit, Sync& sync) {
   const int tid = threadIdx.x;
   const int WE = a.W * a.E;
   // ---- loads: per block (lanes of wave 0) length, capacity and first slot;
@@ -199,7 +204,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
     p.bad_workers = 0u;
     plan_head_unit(a, &p.head, &p.unit);
   }
-  __syncthreads();
+  sync();
   // ---- visibility and view offsets from the tables
   commit();
   if (tid < WE) plan_entry(a, p, tid, ent, ne);
@@ -210,13 +215,16 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
     p.rope_frac[tid] = frac;
   }
   if (tid < a.NB) p.start[tid] = start;
-  __syncthreads();
+  sync();
   // ---- wave 0, lane b = block b: checked length, visibility without the
   // bad workers, the tile prefix over the visible blocks, and each worker's
   // query position (the last position of any block it sees)
   if (tid < 64) {
     const int b = tid;
     int v = 0;
+    // (opaque until here: otherwise the compiler compares right after the
+    // loads and waits for them before the rest of the plan's loads are issued)
+    asm volatile("" : "+v"(len), "+v"(cap));
     if (b < a.NB) {
       if (len < 0 || len > cap) {
         atomicOr(&p.flags, HW_DEV_BAD_LENGTH);
@@ -246,7 +254,41 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
       if (p.bad_workers) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
     }
   }
-  __syncthreads();
+  sync();
+}
+
+template <int NTHR, typename Issue, typename Commit>
+__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
+  WorkgroupBarrier sync;
+  build_plan<NTHR>(a, p, issue, commit, sync);
+}
+
+// Waves of one workgroup that synchronize through a counter in LDS instead of
+// s_barrier, so that the other waves of the workgroup never have to join:
+// each wave's LDS writes complete (release fence on LDS), lane 0 adds one,
+// and the wave waits until the counter reaches count * phase.  The counter
+// only grows; it must be zero before the first phase.  Every wave of the
+// group reaches every phase (no early exits), so every wait ends.
+struct LdsWaveBarrier {
+  uint32_t* ctr;
+  uint32_t count;
+  uint32_t phase;
+  __device__ void operator()() {
+    ++phase;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if ((threadIdx.x & 63) == 0)
+      __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count * phase)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
+};
+
+// Waits until an LDS counter that other waves advance reaches `target`.
+__device__ __forceinline__ void lds_wait_at_least(uint32_t* ctr, uint32_t target) {
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Block holding global tile j of the plan (cursor walks forward).
@@ -489,14 +531,28 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;
   const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  // this head's query rows, loaded with the plan's loads and staged in LDS so
-  // the main loop issues no vector memory operations other than the K/V stream
+  // The waves split for the prologue.
+  //  front (waves < kFront): load the tables, lengths and this head's query
+  //    rows, build the plan and the first group's rotated queries, and
+  //    synchronize among themselves through an LDS counter;
+  //  back: once the front waves' loads are back, request their speculative
+  //    first tile (the tile each started with in the previous call with this
+  //    workspace: within a decode step every layer's call has the same plan),
+  //    then wait for the rotated queries and keep the tile if the plan
+  //    confirms it.
+  // A wave whose tile requests stall on a full memory queue (a CU accepts
+  // about 64 KB before issue blocks) thus never holds a barrier the plan
+  // needs.  The front waves request their first tiles after the rotation.
+  constexpr int kFront = 4;
+  constexpr int NF = kFront * 64;
+  const bool front = wave < kFront;
+  __shared__ uint32_t sync_ctr[3];  // front barrier, front loads issued, rotation done
+  if (tid < 3) sync_ctr[tid] = 0u;
+  __syncthreads();
+  // this head's query rows, staged in LDS so that the main loop issues no
+  // vector memory operations other than the K/V stream
   constexpr int kQVec = RP * D / 8;
-  constexpr int kQRegs = (kQVec + NTHR - 1) / NTHR;
-  u32x4 qv[kQRegs];
-  // Speculative first tile: within a decode step every layer's call has the
-  // same plan, so each wave's first tile of the last call (hint) is requested
-  // before the plan is built, and kept if the plan confirms it.
+  constexpr int kQRegs = (kQVec + NF - 1) / NF;
   int h0, u0;
   plan_head_unit(a, &h0, &u0);
   const uint32_t koff = (q4 * 128 + li * 8) * EB;
@@ -513,11 +569,13 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   uint32_t* hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
   const uint32_t spec = *hint;  // uniform: a scalar load
   Frag kf[2][KS], vf[MT];
-  {
+  LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u};
+  if (front) {
+    u32x4 qv[kQRegs];
     auto issue = [&] {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * NTHR;
+        const int x = tid + k * NF;
         const int r = (8 * x) / D, d = (8 * x) - r * D;
         qv[k] = u32x4{0u, 0u, 0u, 0u};
         if (x < kQVec && r < a.R) {
@@ -530,16 +588,19 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     auto commit = [&] {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * NTHR;
+        const int x = tid + k * NF;
         if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
       }
-      // the speculative tile once the plan's own loads are back, so that its
-      // traffic does not queue ahead of them
-      __builtin_amdgcn_sched_barrier(0);
-      load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
-      __builtin_amdgcn_sched_barrier(0);
+      // the plan's loads are back: the back waves' tiles may now fill the
+      // memory queues (issued earlier, they delay these small loads by the
+      // whole chip's burst)
+      if (lane == 0) __hip_atomic_fetch_add(&sync_ctr[1], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_WORKGROUP);
     };
-    build_plan<NTHR>(a, plan, issue, commit);
+    build_plan<NF>(a, plan, issue, commit, front_sync);
+  } else {
+    lds_wait_at_least(&sync_ctr[1], kFront);
+    load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
   }
   bool rowvis[NT];
   f32x4 acc[MT][NT];
@@ -557,12 +618,13 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // block the stacked rows of head g rotated by i_q - view_offset of their
   // worker, scaled, rounded to bf16 and laid out as MFMA B fragments
   // (row 16t+li, dims 8*(4s+q4)..+8 at qfs[((blk*NT + t)*KS + s)*64 + lane]).
-  // Rows past R or of workers that do not see the block are zero.
+  // Rows past R or of workers that do not see the block are zero.  nthr: the
+  // threads taking part.
   bf16x8* qfs = reinterpret_cast<bf16x8*>(ubuf);
-  auto rotate_blocks = [&](int gb, int ge) {
+  auto rotate_blocks = [&](int gb, int ge, int nthr) {
     const int items = (ge - gb) * NT * (KS / 2) * 64;
 #pragma unroll 1
-    for (int x = tid; x < items; x += NTHR) {
+    for (int x = tid; x < items; x += nthr) {
       const int ln = x & 63;
       const int y = x >> 6;
       const int sh = y % (KS / 2);
@@ -600,9 +662,23 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // pipeline runs over this wave's tiles j, j + NWAVE, ...: the next tile's
   // keys are loaded into the key registers as soon as the current scores are
   // formed, its values into the value registers right after the P.V products,
-  // so every wave keeps a tile in flight while it computes.  The group's
-  // first tile is requested before the rotation.
+  // so every wave keeps a tile in flight while it computes.  A later group's
+  // first tile is requested before its rotation; in the first group the back
+  // waves keep their speculative tile when the plan confirms it.
   uint32_t first = 0xffffffffu;  // this wave's first tile (byte offset), none: all ones
+  // the first group's rotation (front waves), published to the back waves
+  if (front) {
+    if (plan.lo < plan.hi) {
+      const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
+      const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
+      rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NF);
+    }
+    front_sync();
+    if (lane == 0)
+      __hip_atomic_fetch_add(&sync_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    lds_wait_at_least(&sync_ctr[2], kFront);
+  }
   if (plan.lo < plan.hi) {
     const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
     const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
@@ -617,14 +693,16 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         rt = tile_ref<D>(plan, a.NB, j, bcur);
         const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * EB));
         if (gb == b_first) first = tile;
-        if (gb != b_first || tile != spec) {
+        if (gb != b_first || front || tile != spec) {
           load_keys<D, E>(krs, tile, koff, kf);
           load_values<D, E>(vrs, tile, voff, vf);
         }
       }
-      if (gb != b_first) __syncthreads();  // the previous group's fragments are consumed
-      rotate_blocks(gb, ge);
-      __syncthreads();
+      if (gb != b_first) {
+        __syncthreads();  // the previous group's fragments are consumed
+        rotate_blocks(gb, ge, NTHR);
+        __syncthreads();
+      }
       if (j < t_hi) {
         int qb = -1;
         int rowend[NT];
