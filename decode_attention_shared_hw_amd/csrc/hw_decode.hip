@@ -245,12 +245,25 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
     const int incl = wave_inclusive_scan(v);
     const int nt = __builtin_amdgcn_readlane(incl, 63);
     if (b < a.NB) p.tile0[b] = incl - v;
+    // The units split the tiles by cost: a tile costs 1 and every visible
+    // block after the first kBlockCost more (a unit that reaches another
+    // block rotates its queries before its front waves stream, measured at
+    // about five tiles' time).  Cost position x maps to tile
+    // sum_b clamp(x - cs_b, 0, tiles_b), cs_b being the cost position of
+    // block b's first tile.  C * (unit + 1) < 2^31: a plane holds under 2^31
+    // bytes, so under 2^18 tiles, and there are at most kMaxUnits units.
+    const int cv = v + ((v > 0 && incl > v) ? kBlockCost : 0);
+    const int cincl = wave_inclusive_scan(cv);
+    const uint32_t C = static_cast<uint32_t>(__builtin_amdgcn_readlane(cincl, 63));
+    const int cs = cincl - v;
+    const int xlo = static_cast<int>(C * p.unit / static_cast<uint32_t>(a.P));
+    const int xhi = static_cast<int>(C * (p.unit + 1) / static_cast<uint32_t>(a.P));
+    const int lo = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xlo - cs, 0), v)), 63);
+    const int hi = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xhi - cs, 0), v)), 63);
     if (b == 0) {
       p.tile0[a.NB] = nt;
-      // n * (unit + 1) < 2^31: a plane holds under 2^31 bytes, so under 2^18
-      // tiles, and there are at most kMaxUnits units
-      p.lo = static_cast<int>(static_cast<uint32_t>(nt * p.unit) / static_cast<uint32_t>(a.P));
-      p.hi = static_cast<int>(static_cast<uint32_t>(nt * (p.unit + 1)) / static_cast<uint32_t>(a.P));
+      p.lo = lo;
+      p.hi = hi;
       if (p.bad_workers) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
     }
   }

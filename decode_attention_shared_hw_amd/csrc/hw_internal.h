@@ -16,6 +16,7 @@ constexpr int kMfmaWaves = kMfmaThreads / 64;
 constexpr int kQfBlocks = 8;           // blocks whose rotated queries are held in LDS at once
 constexpr int kMaxHalf = 64;           // head_dim / 2 upper bound
 constexpr int kMaxUnits = 256;         // split-K work units per kv head
+constexpr int kBlockCost = 5;          // extra cost, in tiles, of each visible block after the first
 
 // Element offset of key (slot, d) inside one (layer, kv head) plane.  Tiles of
 // 32 slots; inside a tile: [half t/16][chunk d/8][token t%16][d%8].
