@@ -212,15 +212,18 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   const WsLayout wl = ws_layout(pool->num_kv_heads, P_ws, rows, pool->head_dim);
   if (!workspace || workspace_bytes < wl.total) return HW_EWORKSPACE;
 
-  DeviceInfo* di = nullptr;
-  st = device_info(&di);
-  if (st != HW_OK) return st;
   // units per head: the setting, bounded by the tiles the blocks can hold
   int64_t max_tiles = 0;
   for (int b = 0; b < pool->num_blocks; ++b) max_tiles += pool->block_cap[b] / HW_TILE_TOKENS;
   int64_t P = P_ws;
   if (P > max_tiles) P = max_tiles;
   if (P < 1) P = 1;
+  // workgroup indices stay below 2^16 (fast_div's range)
+  if (P * pool->num_kv_heads >= 65536) return HW_ERANGE;
+
+  DeviceInfo* di = nullptr;
+  st = device_info(&di);
+  if (st != HW_OK) return st;
 
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
@@ -253,6 +256,10 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   a.P = static_cast<int32_t>(P);
   a.D = pool->head_dim;
   a.dtype = pool->dtype;
+  a.mP = div_magic(static_cast<uint32_t>(a.P));
+  a.mE = div_magic(static_cast<uint32_t>(a.E));
+  a.mG = div_magic(static_cast<uint32_t>(a.G));
+  a.mGnq = div_magic(static_cast<uint32_t>(a.G * a.nq));
   const int64_t grid = P * pool->num_kv_heads;
   a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
   for (int b = 0; b < pool->num_blocks; ++b) {

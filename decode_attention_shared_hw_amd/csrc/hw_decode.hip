@@ -125,7 +125,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 // Workgroup -> (kv head, work unit): the units of a head are consecutive
 // workgroups.
 __device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, int* unit) {
-  *head = blockIdx.x / a.P;
+  *head = fast_div(blockIdx.x, a.mP);
   *unit = blockIdx.x - *head * a.P;
 }
 
@@ -134,7 +134,7 @@ __device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, i
 // range, block id out of range, a block listed twice) marks its worker bad.
 __device__ __forceinline__ void plan_entry(const DecodeArgs& a, Plan& p, int i, hw_entry e,
                                            int ne) {
-  const int w = i / a.E, slot = i - w * a.E;
+  const int w = fast_div(i, a.mE), slot = i - w * a.E;
   const uint32_t bit = 1u << w;
   if (ne < 0 || ne > a.E) {
     atomicOr(&p.bad_workers, bit);
@@ -187,7 +187,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   int ne = 0;
   if (tid < WE) {
     ent = a.tables[tid];
-    ne = a.num_entries[tid / a.E];
+    ne = a.num_entries[fast_div(tid, a.mE)];
   }
   issue();
   // ---- state that needs none of the loads
@@ -195,8 +195,9 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   if (tid < a.W) p.iq[tid] = -1;
   if (tid < HW_MAX_ROWS) {
     const bool row = tid < a.R;
-    p.row_w[tid] = row ? tid / (a.G * a.nq) : 0;
-    p.row_lag[tid] = row ? a.nq - 1 - (tid / a.G) % a.nq : 0;
+    const int w = fast_div(tid, a.mGnq);
+    p.row_w[tid] = row ? w : 0;
+    p.row_lag[tid] = row ? a.nq - 1 - (fast_div(tid, a.mG) - w * a.nq) : 0;
   }
   for (int i = tid; i < a.W * a.NB; i += NTHR) p.off[i] = 0;
   if (tid == 0) {
@@ -209,7 +210,8 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   commit();
   if (tid < WE) plan_entry(a, p, tid, ent, ne);
 #pragma unroll 1
-  for (int i = tid + NTHR; i < WE; i += NTHR) plan_entry(a, p, i, a.tables[i], a.num_entries[i / a.E]);
+  for (int i = tid + NTHR; i < WE; i += NTHR)
+    plan_entry(a, p, i, a.tables[i], a.num_entries[fast_div(i, a.mE)]);
   if (tid < a.D / 2) {
     p.invf[tid] = invf;
     p.rope_frac[tid] = frac;
@@ -540,6 +542,12 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // afterwards: the waves' softmax states
   __shared__ __attribute__((aligned(16))) float ubuf[kUnionFloats];
 
+  // every scalar argument of the prologue, requested at entry in one round
+  // trip (otherwise each use site waits for its own kernel-argument load)
+  asm volatile("" ::"s"(a.q), "s"(a.k), "s"(a.v), "s"(a.block_len), "s"(a.tables),
+               "s"(a.num_entries), "s"(a.ws_hint), "s"(a.plane_elems), "s"(a.plane_bytes),
+               "s"(a.W), "s"(a.Hq), "s"(a.G), "s"(a.R), "s"(a.E), "s"(a.NB), "s"(a.P), "s"(a.D), "s"(a.nq),
+               "s"(a.qscale), "s"(a.mP), "s"(a.mE), "s"(a.mG), "s"(a.mGnq));
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;
@@ -580,7 +588,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
                                                      offsetof(DecodeTables, k_scale))[h0];
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t* hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
-  const uint32_t spec = *hint;  // uniform: a scalar load
+  uint32_t spec = 0xffffffffu;  // back waves: the hinted first tile
   Frag kf[2][KS], vf[MT];
   LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u};
   if (front) {
@@ -592,7 +600,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         const int r = (8 * x) / D, d = (8 * x) - r * D;
         qv[k] = u32x4{0u, 0u, 0u, 0u};
         if (x < kQVec && r < a.R) {
-          const int w = r / a.G, h = h0 * a.G + (r - w * a.G);
+          const int w = fast_div(r, a.mG), h = h0 * a.G + (r - w * a.G);
           qv[k] =
               *reinterpret_cast<const u32x4*>(qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d);
         }
@@ -612,6 +620,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     };
     build_plan<NF>(a, plan, issue, commit, front_sync);
   } else {
+    spec = __builtin_amdgcn_readfirstlane(*hint);  // (loaded by the back waves only)
     lds_wait_at_least(&sync_ctr[1], kFront);
     load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
   }
@@ -939,7 +948,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
         const int r = (4 * x) / D, d = 4 * x - r * D;
         qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (x < kQVec && r < a.R) {
-          const int w = r / a.G, h = h0 * a.G + (r - w * a.G);
+          const int w = fast_div(r, a.mG), h = h0 * a.G + (r - w * a.G);
           const T* src = qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d;
           qv[k] = make_float4(load_elem(src, 0), load_elem(src, 1), load_elem(src, 2),
                               load_elem(src, 3));

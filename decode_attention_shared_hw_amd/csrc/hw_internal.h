@@ -45,6 +45,14 @@ struct alignas(16) DecodeTables {
   float v_scale[HW_MAX_FP8_KV_HEADS];
 };
 
+// x / d for 0 <= x < 2^16 and 1 <= d <= 256 with one multiply: the host
+// passes m = div_magic(d) = ceil(2^24 / d), and (x * 2^8 * m) >> 32 equals
+// floor(x / d) over that whole range (checked exhaustively).
+inline uint32_t div_magic(uint32_t d) { return ((1u << 24) + d - 1u) / d; }
+__device__ __forceinline__ int fast_div(int x, uint32_t m) {
+  return static_cast<int>(__umulhi(static_cast<uint32_t>(x) << 8, m));
+}
+
 // Bytes per stored element of a pool type.
 __host__ __device__ inline int elem_bytes(int dtype) {
   return dtype == HW_F32 ? 4 : (dtype == HW_BF16 ? 2 : 1);
@@ -67,6 +75,7 @@ struct alignas(16) DecodeArgs {
   int32_t plane_bytes;      // plane_elems * element size (< 2^31)
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
   int32_t nq;               // query tokens per worker (1: decode); rows are (w*nq + j)*G + h
+  uint32_t mP, mE, mG, mGnq;  // div_magic of P, E, G and G * nq (indices < 2^16)
   int32_t dtype;            // HW_F32 / HW_BF16 / HW_FP8
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
   DecodeTables tab;

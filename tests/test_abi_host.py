@@ -92,6 +92,13 @@ def test_decode_host_validation(lib):
     assert decode_rc(lib, FakePool(caps=(64, 32), starts=[0, 32])) == hw.HW_EINVAL  # overlap
     assert decode_rc(lib, FakePool(caps=(64,), slots=32)) == hw.HW_EINVAL    # beyond slots
     assert decode_rc(lib, FakePool(caps=tuple([32] * 65))) == hw.HW_ERANGE   # too many blocks
+    # kv heads x split units must stay below 2^16 workgroups
+    hw.hw_set_tuning(hw.PATH_AUTO, 256)
+    try:
+        big = FakePool(caps=(256 * 32,), Hkv=256)
+        assert decode_rc(lib, big, Hq=256) == hw.HW_ERANGE
+    finally:
+        hw.hw_set_tuning(hw.PATH_AUTO, 0)
 
 
 def test_workspace_bytes(lib):
