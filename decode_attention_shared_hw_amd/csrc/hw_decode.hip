@@ -535,12 +535,14 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int kState1 = RC1 * ACC_STRIDE + 2 * RC1;
   constexpr int kState2 = RP * ACC_STRIDE + 2 * RP;
   constexpr int kQfFloats = kQfBlocks * NT * KS * 64 * 4;  // rotated-query fragments
-  constexpr int kUnionFloats = cmax(cmax(NWAVE * kState1, NSTATE * kState2), kQfFloats);
+  constexpr int kEpiFloats = cmax(NWAVE * kState1, NSTATE * kState2);
   __shared__ Plan plan;
   __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
-  // main loop: the rotated-query fragments of up to kQfBlocks blocks;
-  // afterwards: the waves' softmax states
-  __shared__ __attribute__((aligned(16))) float ubuf[kUnionFloats];
+  // the rotated-query fragments of up to kQfBlocks blocks (main loop)
+  __shared__ __attribute__((aligned(16))) float qbuf[kQfFloats];
+  // the waves' softmax states (epilogue); apart from qbuf, so that a wave
+  // done with its tiles deposits its state while the others still stream
+  __shared__ __attribute__((aligned(16))) float ebuf[kEpiFloats];
 
   // every scalar argument of the prologue, requested at entry in one round
   // trip (otherwise each use site waits for its own kernel-argument load)
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // (row 16t+li, dims 8*(4s+q4)..+8 at qfs[((blk*NT + t)*KS + s)*64 + lane]).
   // Rows past R or of workers that do not see the block are zero.  nthr: the
   // threads taking part.
-  bf16x8* qfs = reinterpret_cast<bf16x8*>(ubuf);
+  bf16x8* qfs = reinterpret_cast<bf16x8*>(qbuf);
   auto rotate_blocks = [&](int gb, int ge, int nthr) {
     const int items = (ge - gb) * NT * (KS / 2) * 64;
 #pragma unroll 1
@@ -771,8 +773,6 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     }
   }
 
-  if (lane == 0) *hint = first;
-
   // full row sums (the four lanes of a row hold partial sums)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -780,11 +780,12 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     l_run[t] += __shfl_xor(l_run[t], 32);
   }
   // Combine the waves' softmax states (O^T rows below R, m, l) in LDS.  When
-  // every wave's state fits (R <= RC1 rows), all waves deposit at once;
-  // otherwise half of them at a time: the upper waves deposit, each lower
-  // wave folds in its partner (same fragment positions, so lane-local), and
-  // the lower waves deposit.  Then every thread combines its share of the
-  // unit's R*D outputs over the deposited states and stores the partial.
+  // every wave's state fits (R <= RC1 rows), each wave deposits its state in
+  // its own slot as soon as its tiles are done; otherwise, after a barrier,
+  // half of them at a time: the upper waves deposit, each lower wave folds in
+  // its partner (same fragment positions, so lane-local), and the lower
+  // waves deposit.  Then every thread combines its share of the unit's R*D
+  // outputs over the deposited states and stores the partial.
   auto deposit = [&](float* buf, int rc) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -808,7 +809,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       float M = -INFINITY;
 #pragma unroll
       for (int wv = 0; wv < NS; ++wv) {
-        mw[wv] = ubuf[wv * state + rc * ACC_STRIDE + r];
+        mw[wv] = ebuf[wv * state + rc * ACC_STRIDE + r];
         M = fmaxf(M, mw[wv]);
       }
       float L = 0.f;
@@ -816,7 +817,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       if (M != -INFINITY) {
 #pragma unroll
         for (int wv = 0; wv < NS; ++wv) {
-          const float* src = ubuf + wv * state;
+          const float* src = ebuf + wv * state;
           const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
           L += src[rc * ACC_STRIDE + rc + r] * sc;
           O += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d4) * sc;
@@ -826,16 +827,16 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
     }
   };
-  __syncthreads();  // every wave is done with the query fragments
   if (a.R <= RC1) {
-    deposit(ubuf + wave * kState1, RC1);
+    deposit(ebuf + wave * kState1, RC1);
     __syncthreads();
     combine_store(std::integral_constant<int, NWAVE>{}, kState1, RC1);
   } else {
-    if (wave >= NSTATE) deposit(ubuf + (wave - NSTATE) * kState2, RP);
+    __syncthreads();
+    if (wave >= NSTATE) deposit(ebuf + (wave - NSTATE) * kState2, RP);
     __syncthreads();
     if (wave < NSTATE) {
-      const float* src = ubuf + wave * kState2;
+      const float* src = ebuf + wave * kState2;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int r = 16 * t + li;
@@ -854,10 +855,11 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
       }
     }
     __syncthreads();
-    if (wave < NSTATE) deposit(ubuf + wave * kState2, RP);
+    if (wave < NSTATE) deposit(ebuf + wave * kState2, RP);
     __syncthreads();
     combine_store(std::integral_constant<int, NSTATE>{}, kState2, RP);
   }
+  if (lane == 0) *hint = first;
   if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
 }
 

@@ -13,7 +13,7 @@ constexpr int kThreads = 256;          // threads per decode workgroup (4 waves)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMfmaThreads = 512;      // threads per MFMA decode workgroup (8 waves)
 constexpr int kMfmaWaves = kMfmaThreads / 64;
-constexpr int kQfBlocks = 8;           // blocks whose rotated queries are held in LDS at once
+constexpr int kQfBlocks = 4;           // blocks whose rotated queries are held in LDS at once
 constexpr int kMaxHalf = 64;           // head_dim / 2 upper bound
 constexpr int kMaxUnits = 256;         // split-K work units per kv head
 constexpr int kBlockCost = 5;          // extra cost, in tiles, of each visible block after the first
