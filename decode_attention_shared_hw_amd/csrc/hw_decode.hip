@@ -645,39 +645,49 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // Rows past R or of workers that do not see the block are zero.  nthr: the
   // threads taking part.
   bf16x8* qfs = reinterpret_cast<bf16x8*>(qbuf);
+  // A thread's item (row, dims) is the same in every block (nthr is a
+  // multiple of IPB): its query values, frequencies, worker and i_q - lag are
+  // read from LDS once; per block only the view offset and visibility.
+  constexpr int IPB = NT * (KS / 2) * 64;  // items per block
   auto rotate_blocks = [&](int gb, int ge, int nthr) {
-    const int items = (ge - gb) * NT * (KS / 2) * 64;
+    const int slot = tid & (IPB - 1);
+    const int ln = slot & 63;
+    const int y = slot >> 6;
+    const int sh = y % (KS / 2);
+    const int t = y / (KS / 2);
+    const int r = 16 * t + (ln & 15);
+    const int w = plan.row_w[r];
+    const long long iq_lag = plan.iq[w] - plan.row_lag[r];
+    const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner dims are d0 + HALF
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
+    uint32_t xw[4], yw[4];
+    uint64_t fr[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      xw[e2] = qw[e2];
+      yw[e2] = qw[e2 + HALF / 2];
+      fr[2 * e2] = plan.rope_frac[d0 + 2 * e2];
+      fr[2 * e2 + 1] = plan.rope_frac[d0 + 2 * e2 + 1];
+    }
 #pragma unroll 1
-    for (int x = tid; x < items; x += nthr) {
-      const int ln = x & 63;
-      const int y = x >> 6;
-      const int sh = y % (KS / 2);
-      const int t = (y / (KS / 2)) % NT;
-      const int bi = y / ((KS / 2) * NT);
+    for (int bi = tid / IPB; bi < ge - gb; bi += nthr / IPB) {
       const int b = gb + bi;
-      const int r = 16 * t + (ln & 15);
-      const int w = plan.row_w[r];
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
-      const int wc = vis ? w : 0;
-      const int64_t delta = plan.iq[wc] - plan.row_lag[r] - plan.off[wc * a.NB + b];
+      const int64_t delta = iq_lag - plan.off[w * a.NB + b];
       const float sc = vis ? qsc : 0.f;
-      const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner block is d0 + HALF
-      // two dims per step: bf16 pairs (x, x+1) of the first half and their
-      // partners in the second half, rotated and stored as one 32-bit word each
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
-      uint32_t* lo = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh) * 64 + ln);
-      uint32_t* hi = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh + KS / 2) * 64 + ln);
-#pragma unroll 1
+      u32x4 lo, hi;
+#pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t xw = qw[e2], yw = qw[e2 + HALF / 2];
-        const float x0 = __uint_as_float(xw << 16), x1 = __uint_as_float(xw & 0xffff0000u);
-        const float y0 = __uint_as_float(yw << 16), y1 = __uint_as_float(yw & 0xffff0000u);
+        const float x0 = __uint_as_float(xw[e2] << 16), x1 = __uint_as_float(xw[e2] & 0xffff0000u);
+        const float y0 = __uint_as_float(yw[e2] << 16), y1 = __uint_as_float(yw[e2] & 0xffff0000u);
         float c0, s0, c1, s1;
-        rope_cos_sin_fx(delta, plan.rope_frac[d0 + 2 * e2], &c0, &s0);
-        rope_cos_sin_fx(delta, plan.rope_frac[d0 + 2 * e2 + 1], &c1, &s1);
+        rope_cos_sin_fx(delta, fr[2 * e2], &c0, &s0);
+        rope_cos_sin_fx(delta, fr[2 * e2 + 1], &c1, &s1);
         lo[e2] = pack_bf16x2((x0 * c0 - y0 * s0) * sc, (x1 * c1 - y1 * s1) * sc);
         hi[e2] = pack_bf16x2((y0 * c0 + x0 * s0) * sc, (y1 * c1 + x1 * s1) * sc);
       }
+      *reinterpret_cast<u32x4*>(qfs + ((bi * NT + t) * KS + sh) * 64 + ln) = lo;
+      *reinterpret_cast<u32x4*>(qfs + ((bi * NT + t) * KS + sh + KS / 2) * 64 + ln) = hi;
     }
   };
 
