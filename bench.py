@@ -16,9 +16,9 @@ workload (the appended tokens sit past the restored common length).
 The step is captured once in a HIP graph and replayed.
 
 Metric: worker-tokens/s per layer = W * layers / step time.  The roofline
-object reports the decode kernel's algorithmic HBM bytes per launch divided
-by its average duration (HIP events around each launch, eager replay of the
-same step) against MI355X's 8 TB/s.
+object reports the decode call's algorithmic HBM bytes divided by its average
+duration (HIP events on the launch stream around the 64 back-to-back calls of
+a step, eager replay) against MI355X's 8 TB/s.
 """
 from __future__ import annotations
 
@@ -343,12 +343,12 @@ def time_step(args, hw, torch, np, wl, pool, q):
         k = counter[0]
         counter[0] += 1
         hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, stream)
+        if events is not None:
+            events["dec"][0].record(stream)
         for layer in range(L):
-            if events is not None:
-                events["dec"][layer][0].record(stream)
             hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, stream)
-            if events is not None:
-                events["dec"][layer][1].record(stream)
+        if events is not None:
+            events["dec"][1].record(stream)
         src = wl.worker_block[k % W]
         if events is not None:
             events["app"][0].record(stream)
@@ -388,18 +388,20 @@ def time_step(args, hw, torch, np, wl, pool, q):
         wall = time.perf_counter() - t0
         gpu_ms = ev0.elapsed_time(ev1)
 
-        # ---- per-launch kernel durations (HIP events around each launch on
-        # the launch stream; a GPU spin first lets the host enqueue ahead)
+        # ---- per-launch durations: HIP events on the launch stream around the
+        # step's L back-to-back decode calls (per call: the span / L, so the
+        # events do not sit between the launches they time) and around the
+        # append; a GPU spin first lets the host enqueue ahead
         dec_us, app_us = [], []
         for _ in range(args.kernel_timing_steps):
-            evs = {"dec": [(torch.cuda.Event(enable_timing=True),
-                            torch.cuda.Event(enable_timing=True)) for _ in range(L)],
+            evs = {"dec": (torch.cuda.Event(enable_timing=True),
+                           torch.cuda.Event(enable_timing=True)),
                    "app": (torch.cuda.Event(enable_timing=True),
                            torch.cuda.Event(enable_timing=True))}
             torch.cuda._sleep(20_000_000)
             step(evs)
             stream.synchronize()
-            dec_us += [a.elapsed_time(b) * 1e3 for a, b in evs["dec"]]
+            dec_us.append(evs["dec"][0].elapsed_time(evs["dec"][1]) * 1e3 / L)
             app_us.append(evs["app"][0].elapsed_time(evs["app"][1]) * 1e3)
     torch.cuda.synchronize()
     return {"ms_per_step": gpu_ms / args.steps, "dec_us": dec_us, "app_us": app_us, "wall": wall,
