@@ -260,6 +260,7 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   a.mE = div_magic(static_cast<uint32_t>(a.E));
   a.mG = div_magic(static_cast<uint32_t>(a.G));
   a.mGnq = div_magic(static_cast<uint32_t>(a.G * a.nq));
+  a.mR = div_magic(static_cast<uint32_t>(a.R));
   const int64_t grid = P * pool->num_kv_heads;
   a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
   for (int b = 0; b < pool->num_blocks; ++b) {

@@ -1275,21 +1275,41 @@ __device__ __forceinline__ float readlane_f32(float x, int k) {
 }
 
 __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
+  // every scalar argument, requested at entry in one round trip
+  asm volatile("" ::"s"(a.ws_ml), "s"(a.ws_acc), "s"(a.out), "s"(a.status), "s"(a.R), "s"(a.P),
+               "s"(a.D), "s"(a.G), "s"(a.Hq), "s"(a.dtype), "s"(a.mR), "s"(a.mG));
   const int tid = threadIdx.x;  // output dim
   const int lane = tid & 63;
-  const int g = blockIdx.x / a.R;
+  const int g = fast_div(blockIdx.x, a.mR);
   const int r = blockIdx.x - g * a.R;
   const int P = a.P, D = a.D;
-  const float2* ml = a.ws_ml + static_cast<int64_t>(g) * P * a.R + r;
-  const float* accp = a.ws_acc + (static_cast<int64_t>(g) * P * a.R + r) * D + tid;
-  const int64_t ustride = static_cast<int64_t>(a.R) * D;
+  // FP8 pools: values are code * scale of the kv head (requested early)
+  const float vsc = a.dtype == HW_FP8
+                        ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
+                                                         offsetof(DecodeTables, v_scale))[g]
+                        : 1.f;
+  // this (kv head, row)'s partials as buffers: unit u's accumulators at byte
+  // u * R * D * 4, its (m, l) at byte u * R * 8; a unit index past the last
+  // is clamped to it (its weight is zero)
+  const uint32_t ustride = static_cast<uint32_t>(a.R * D) * 4u;
+  const int64_t row0 = static_cast<int64_t>(g) * P * a.R + r;
+  const __amdgpu_buffer_rsrc_t accrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws_acc + row0 * D, static_cast<short>(0), static_cast<int>(P * ustride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t mlrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws_ml + row0, static_cast<short>(0), P * a.R * 8, 0x00020000);
   float M = -INFINITY, L = 0.f, s = 0.f;
   for (int u0 = 0; u0 < P; u0 += kMergeChunk) {
     const int uk = u0 + (lane & (kMergeChunk - 1));
-    const float2 mv = ml[static_cast<int64_t>(min(uk, P - 1)) * a.R];
+    const float2 mv = __builtin_bit_cast(
+        float2, __builtin_amdgcn_raw_buffer_load_b64(
+                    mlrs, static_cast<uint32_t>(min(uk, P - 1) * a.R) * 8u, 0, 0));
     float av[kMergeChunk];
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) av[k] = accp[min(u0 + k, P - 1) * ustride];
+    for (int k = 0; k < kMergeChunk; ++k)
+      av[k] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(
+                     accrs, static_cast<uint32_t>(tid) * 4u,
+                     static_cast<uint32_t>(min(u0 + k, P - 1)) * ustride, 0));
     const float mk = uk < P ? mv.x : -INFINITY;
     float Mc = M;
 #pragma unroll
@@ -1308,11 +1328,8 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
     }
     M = Mc;
   }
-  const int w = r / a.G, h = g * a.G + (r - w * a.G);
-  float o = L > 0.f ? s / L : 0.f;
-  if (a.dtype == HW_FP8)  // FP8 pools: values are code * scale of the kv head
-    o *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
-                                        offsetof(DecodeTables, v_scale))[g];
+  const int w = fast_div(r, a.mG), h = g * a.G + (r - w * a.G);
+  const float o = L > 0.f ? s / L * vsc : 0.f;
   a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = o;
   if (tid == 0 && !(L > 0.f)) atomicOr(a.status, HW_DEV_NO_TOKENS);
 }

@@ -75,7 +75,7 @@ struct alignas(16) DecodeArgs {
   int32_t plane_bytes;      // plane_elems * element size (< 2^31)
   int32_t W, Hq, Hkv, G, R, E, NB, P, D;
   int32_t nq;               // query tokens per worker (1: decode); rows are (w*nq + j)*G + h
-  uint32_t mP, mE, mG, mGnq;  // div_magic of P, E, G and G * nq (indices < 2^16)
+  uint32_t mP, mE, mG, mGnq, mR;  // div_magic of P, E, G, G * nq and R (indices < 2^16)
   int32_t dtype;            // HW_F32 / HW_BF16 / HW_FP8
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
   DecodeTables tab;
