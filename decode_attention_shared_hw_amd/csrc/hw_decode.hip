@@ -1311,21 +1311,17 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
                      accrs, static_cast<uint32_t>(tid) * 4u,
                      static_cast<uint32_t>(min(u0 + k, P - 1)) * ustride, 0));
     const float mk = uk < P ? mv.x : -INFINITY;
-    float Mc = M;
-#pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) Mc = fmaxf(Mc, readlane_f32(mk, k));
+    // (each 32-lane half of the wave holds the chunk's units: DPP reductions)
+    const float Mc = fmaxf(M, half_max(mk));
     // while no unit has tokens every weight is 0 and (L, sum) stay 0
     const float Mu = Mc == -INFINITY ? 0.f : Mc;
     const float wk = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - Mu);
     const float lk = uk < P ? mv.y * wk : 0.f;
     const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mu);
-    L *= sc;
+    L = L * sc + half_sum(lk);
     s *= sc;
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k) {
-      L += readlane_f32(lk, k);
-      s += av[k] * readlane_f32(wk, k);
-    }
+    for (int k = 0; k < kMergeChunk; ++k) s += av[k] * readlane_f32(wk, k);
     M = Mc;
   }
   const int w = fast_div(r, a.mG), h = g * a.G + (r - w * a.G);
