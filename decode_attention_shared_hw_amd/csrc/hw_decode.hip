@@ -813,8 +813,9 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   const int64_t pu = partial_index(a, plan);
   auto combine_store = [&](auto nstate_c, int state, int rc) {
     constexpr int NS = decltype(nstate_c)::value;
-    for (int x = tid; x < a.R * (D / 4); x += NTHR) {
-      const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
+    // 8 outputs per item: R * D / 8 items (320 at 20 rows), one per thread
+    for (int x = tid; x < a.R * (D / 8); x += NTHR) {
+      const int r = x / (D / 8), d8 = 8 * (x - r * (D / 8));
       float mw[NS];
       float M = -INFINITY;
 #pragma unroll
@@ -823,18 +824,20 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         M = fmaxf(M, mw[wv]);
       }
       float L = 0.f;
-      f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
       if (M != -INFINITY) {
 #pragma unroll
         for (int wv = 0; wv < NS; ++wv) {
           const float* src = ebuf + wv * state;
           const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
           L += src[rc * ACC_STRIDE + rc + r] * sc;
-          O += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d4) * sc;
+          O0 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8) * sc;
+          O1 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8 + 4) * sc;
         }
       }
-      *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d4) = O;
-      if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
+      *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d8) = O0;
+      *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d8 + 4) = O1;
+      if (d8 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
     }
   };
   if (a.R <= RC1) {
