@@ -318,9 +318,9 @@ __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan
 }
 
 // ------------------------------------------------------------- MFMA kernel
-// bf16 pools, rows R = W*G <= 16*NT.  Each wave owns every 4th tile of the
-// workgroup's range and keeps its own (m, l, O^T) for all rows; the four
-// waves are combined in LDS at the end.
+// bf16 and FP8 pools, rows R = W*G <= 16*NT.  Each of the eight waves owns
+// every 8th tile of the workgroup's range and keeps its own (m, l, O^T) for
+// all rows; the waves' states are combined in LDS at the end.
 //
 // Fragments (v_mfma_f32_16x16x32_bf16, lane l: i = l%16, q4 = l/16):
 //   S^T[tok][row] = K[tok][:] . Q~[row][:]
@@ -352,7 +352,7 @@ __device__ __forceinline__ TileRef tile_ref(const Plan& p, int nb, int j, int& b
 }
 
 constexpr int cmax(int x, int y) { return x > y ? x : y; }
-constexpr int kOneLevelRows = 24;  // rows up to which all waves' states fit in LDS together
+constexpr int kOneLevelRows = 24;  // rows up to which every wave's state has its own LDS slot
 
 // Raw buffer resource over one kv-head plane (gfx9 descriptor word 3).  The
 // lane offsets are range-checked against the plane; the tile offset (an SGPR
