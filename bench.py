@@ -411,8 +411,8 @@ def time_step(args, hw, torch, np, wl, pool, q):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(multi-GPU sharding is design-only, see DESIGN.md)", file=sys.stderr)
+        print("bench.py: the decode path runs on one GPU; --gpus must be 1 "
+              "(sharding the kv heads over several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
