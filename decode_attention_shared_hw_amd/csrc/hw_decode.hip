@@ -314,7 +314,7 @@ __device__ __forceinline__ int block_of_tile(const Plan& p, int nb, int j, int b
 
 // Per-unit partial: (m, l) per row and the unnormalised accumulator.
 __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan& p) {
-  return static_cast<int64_t>(p.head) * a.P + p.unit;
+  return static_cast<int64_t>(p.head) * a.R * a.P + p.unit;
 }
 
 // ------------------------------------------------------------- MFMA kernel
@@ -568,10 +568,17 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // needs.  The front waves request their first tiles after the rotation.
   constexpr int kFront = 4;
   constexpr int NF = kFront * 64;
-  const bool front = wave < kFront;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool front = wave_u < kFront;  // wave-uniform: one side of each branch per wave
   __shared__ uint32_t sync_ctr[3];  // front barrier, front loads issued, rotation done
   if (tid < 3) sync_ctr[tid] = 0u;
-  __syncthreads();
+  // publishes the zeroed counters; each wave passes it once, the front waves
+  // right after requesting the plan's loads, the back waves first
+  auto init_barrier = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
   // this head's query rows, staged in LDS so that the main loop issues no
   // vector memory operations other than the K/V stream
   constexpr int kQVec = RP * D / 8;
@@ -580,16 +587,22 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   plan_head_unit(a, &h0, &u0);
   const uint32_t koff = (q4 * 128 + li * 8) * EB;
   const uint32_t voff = (q4 * 8 * D + li * 8) * EB;
-  const __amdgpu_buffer_rsrc_t krs = plane_rsrc(
-      static_cast<const char*>(a.k) + static_cast<int64_t>(h0) * a.plane_elems * EB, a.plane_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = plane_rsrc(
-      static_cast<const char*>(a.v) + static_cast<int64_t>(h0) * a.plane_elems * EB, a.plane_bytes);
-  // FP8 pools: the key scale of this kv head is folded into the rotated queries
-  float qsc = a.qscale;
-  if (EB == 1) qsc *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
-                                                     offsetof(DecodeTables, k_scale))[h0];
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t* hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
+  // this head's K/V plane descriptors, the query scale (FP8 pools: times the
+  // key scale of the kv head) and this wave's hint slot; set up by the front
+  // waves while their plan loads are in flight, by the back waves first
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  float qsc;
+  uint32_t* hint;
+  auto kv_setup = [&] {
+    krs = plane_rsrc(static_cast<const char*>(a.k) + static_cast<int64_t>(h0) * a.plane_elems * EB,
+                     a.plane_bytes);
+    vrs = plane_rsrc(static_cast<const char*>(a.v) + static_cast<int64_t>(h0) * a.plane_elems * EB,
+                     a.plane_bytes);
+    qsc = a.qscale;
+    if (EB == 1) qsc *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
+                                                       offsetof(DecodeTables, k_scale))[h0];
+    hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
+  };
   uint32_t spec = 0xffffffffu;  // back waves: the hinted first tile
   Frag kf[2][KS], vf[MT];
   LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u};
@@ -607,6 +620,8 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
               *reinterpret_cast<const u32x4*>(qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d);
         }
       }
+      init_barrier();
+      kv_setup();
     };
     auto commit = [&] {
 #pragma unroll
@@ -622,7 +637,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     };
     build_plan<NF>(a, plan, issue, commit, front_sync);
   } else {
-    spec = __builtin_amdgcn_readfirstlane(*hint);  // (loaded by the back waves only)
+    kv_setup();
+    const uint32_t hv = *hint;  // (loaded by the back waves only)
+    init_barrier();
+    spec = __builtin_amdgcn_readfirstlane(hv);
     lds_wait_at_least(&sync_ctr[1], kFront);
     load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
   }
@@ -835,9 +853,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
           O1 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8 + 4) * sc;
         }
       }
-      *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d8) = O0;
-      *reinterpret_cast<f32x4*>(a.ws_acc + (pu * a.R + r) * D + d8 + 4) = O1;
-      if (d8 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
+      const int64_t pr = pu + static_cast<int64_t>(r) * a.P;
+      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + d8) = O0;
+      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + d8 + 4) = O1;
+      if (d8 == 0) a.ws_ml[pr] = make_float2(M, L);
     }
   };
   if (a.R <= RC1) {
@@ -1256,8 +1275,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
         O.w += v.w * sc;
       }
     }
-    *reinterpret_cast<float4*>(a.ws_acc + (pu * a.R + r) * D + d4) = O;
-    if (d4 == 0) a.ws_ml[pu * a.R + r] = make_float2(M, L);
+    const int64_t pr = pu + static_cast<int64_t>(r) * a.P;
+    *reinterpret_cast<float4*>(a.ws_acc + pr * D + d4) = O;
+    if (d4 == 0) a.ws_ml[pr] = make_float2(M, L);
   }
   if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
 }
@@ -1277,42 +1297,45 @@ __device__ __forceinline__ float readlane_f32(float x, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
 }
 
-__global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a) {
+template <int D>
+__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
   // every scalar argument, requested at entry in one round trip
   asm volatile("" ::"s"(a.ws_ml), "s"(a.ws_acc), "s"(a.out), "s"(a.status), "s"(a.R), "s"(a.P),
-               "s"(a.D), "s"(a.G), "s"(a.Hq), "s"(a.dtype), "s"(a.mR), "s"(a.mG));
+               "s"(a.G), "s"(a.Hq), "s"(a.dtype), "s"(a.mR), "s"(a.mG));
   const int tid = threadIdx.x;  // output dim
   const int lane = tid & 63;
   const int g = fast_div(blockIdx.x, a.mR);
   const int r = blockIdx.x - g * a.R;
-  const int P = a.P, D = a.D;
+  const int P = a.P;
   // FP8 pools: values are code * scale of the kv head (requested early)
   const float vsc = a.dtype == HW_FP8
                         ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
                                                          offsetof(DecodeTables, v_scale))[g]
                         : 1.f;
-  // this (kv head, row)'s partials as buffers: unit u's accumulators at byte
-  // u * R * D * 4, its (m, l) at byte u * R * 8; a unit index past the last
-  // is clamped to it (its weight is zero)
-  const uint32_t ustride = static_cast<uint32_t>(a.R * D) * 4u;
-  const int64_t row0 = static_cast<int64_t>(g) * P * a.R + r;
+  // this (kv head, row)'s partials as buffers over its P units: unit u's
+  // accumulators at byte u * D * 4, its (m, l) at byte u * 8.  Units past the
+  // last lie outside the buffers, read as zero and get zero weight.
+  const int64_t row0 = (static_cast<int64_t>(g) * a.R + r) * P;
   const __amdgpu_buffer_rsrc_t accrs = __builtin_amdgcn_make_buffer_rsrc(
-      a.ws_acc + row0 * D, static_cast<short>(0), static_cast<int>(P * ustride), 0x00020000);
+      a.ws_acc + row0 * D, static_cast<short>(0), P * D * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t mlrs = __builtin_amdgcn_make_buffer_rsrc(
-      a.ws_ml + row0, static_cast<short>(0), P * a.R * 8, 0x00020000);
+      a.ws_ml + row0, static_cast<short>(0), P * 8, 0x00020000);
   float M = -INFINITY, L = 0.f, s = 0.f;
   for (int u0 = 0; u0 < P; u0 += kMergeChunk) {
     const int uk = u0 + (lane & (kMergeChunk - 1));
     const float2 mv = __builtin_bit_cast(
-        float2, __builtin_amdgcn_raw_buffer_load_b64(
-                    mlrs, static_cast<uint32_t>(min(uk, P - 1) * a.R) * 8u, 0, 0));
+        float2, __builtin_amdgcn_raw_buffer_load_b64(mlrs, static_cast<uint32_t>(uk) * 8u, 0, 0));
     float av[kMergeChunk];
 #pragma unroll
-    for (int k = 0; k < kMergeChunk; ++k)
-      av[k] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(
-                     accrs, static_cast<uint32_t>(tid) * 4u,
-                     static_cast<uint32_t>(min(u0 + k, P - 1)) * ustride, 0));
+    for (int k8 = 0; k8 < kMergeChunk; k8 += 8) {
+      // eight units per base offset: the rest in the instructions' offset field
+      uint32_t vo = static_cast<uint32_t>(tid + (u0 + k8) * D) * 4u;
+      asm volatile("" : "+v"(vo));  // (keeps the unit offsets in the offset field)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        av[k8 + k] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(accrs, vo + k * D * 4, 0, 0));
+    }
     const float mk = uk < P ? mv.x : -INFINITY;
     // (each 32-lane half of the wave holds the chunk's units: DPP reductions)
     const float Mc = fmaxf(M, half_max(mk));
@@ -1392,8 +1415,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-  if (a.P > kMaxUnits || a.D > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.Hkv * a.R), dim3(a.D), 0, s, a);
+  if (a.P > kMaxUnits || (a.D != 64 && a.D != 128)) return hipErrorInvalidValue;
+  if (a.D == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(a.Hkv * a.R), dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(a.Hkv * a.R), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

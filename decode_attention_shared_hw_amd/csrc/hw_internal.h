@@ -68,8 +68,8 @@ struct alignas(16) DecodeArgs {
   const int32_t* num_entries;
   float* out;               // [W][Hq][D]
   int32_t* status;
-  float2* ws_ml;            // [Hkv][P][R] (m, l) partials
-  float* ws_acc;            // [Hkv][P][R][D] partial accumulators
+  float2* ws_ml;            // [Hkv][R][P] (m, l) partials
+  float* ws_acc;            // [Hkv][R][P][D] partial accumulators
   uint32_t* ws_hint;        // [Hkv][P][kMfmaWaves] first tile (byte offset) of the last call
   int64_t plane_elems;      // num_slots * D
   int32_t plane_bytes;      // plane_elems * element size (< 2^31)
