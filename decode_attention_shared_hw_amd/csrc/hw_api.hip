@@ -257,6 +257,7 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   a.D = pool->head_dim;
   a.dtype = pool->dtype;
   a.mP = div_magic(static_cast<uint32_t>(a.P));
+  a.rP = 1.0 / a.P;
   a.mE = div_magic(static_cast<uint32_t>(a.E));
   a.mG = div_magic(static_cast<uint32_t>(a.G));
   a.mGnq = div_magic(static_cast<uint32_t>(a.G * a.nq));

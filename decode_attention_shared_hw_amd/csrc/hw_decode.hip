@@ -172,10 +172,12 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   const char* tabp = reinterpret_cast<const char*>(&a.tab);
   int len = 0, cap = 0;
   int64_t start = 0;
-  if (tid < a.NB) {
-    len = a.block_len[tid];
-    cap = reinterpret_cast<const int32_t*>(tabp + offsetof(DecodeTables, block_cap))[tid];
-    start = reinterpret_cast<const int64_t*>(tabp + offsetof(DecodeTables, block_start))[tid];
+  // (lane b of waves 0 and 1: block b's length and capacity; wave 0 its start)
+  if (tid < 128 && (tid & 63) < a.NB) {
+    len = a.block_len[tid & 63];
+    cap = reinterpret_cast<const int32_t*>(tabp + offsetof(DecodeTables, block_cap))[tid & 63];
+    if (tid < 64)
+      start = reinterpret_cast<const int64_t*>(tabp + offsetof(DecodeTables, block_start))[tid];
   }
   double invf = 0.0;
   uint64_t frac = 0u;
@@ -219,8 +221,9 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   if (tid < a.NB) p.start[tid] = start;
   sync();
   // ---- wave 0, lane b = block b: checked length, visibility without the
-  // bad workers, the tile prefix over the visible blocks, and each worker's
-  // query position (the last position of any block it sees)
+  // bad workers and the tile prefix over the visible blocks; at the same
+  // time wave 1, lane b = block b: each worker's query position (the last
+  // position of any block it sees)
   if (tid < 64) {
     const int b = tid;
     int v = 0;
@@ -235,14 +238,7 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
       const uint32_t vis = p.vis[b] & ~p.bad_workers;
       p.vis[b] = vis;
       p.len[b] = len;
-      if (vis != 0u && len > 0) {
-        v = (len + kTile - 1) / kTile;
-#pragma unroll 1
-        for (uint32_t m = vis; m != 0u; m &= m - 1u) {
-          const int w = __builtin_ctz(m);
-          atomicMax(&p.iq[w], static_cast<long long>(p.off[w * a.NB + b]) + len - 1);
-        }
-      }
+      if (vis != 0u && len > 0) v = (len + kTile - 1) / kTile;
     }
     const int incl = wave_inclusive_scan(v);
     const int nt = __builtin_amdgcn_readlane(incl, 63);
@@ -258,8 +254,15 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
     const int cincl = wave_inclusive_scan(cv);
     const uint32_t C = static_cast<uint32_t>(__builtin_amdgcn_readlane(cincl, 63));
     const int cs = cincl - v;
-    const int xlo = static_cast<int>(C * p.unit / static_cast<uint32_t>(a.P));
-    const int xhi = static_cast<int>(C * (p.unit + 1) / static_cast<uint32_t>(a.P));
+    // x / P for x < 2^31: the fp64 product is within 2^-21 of the quotient,
+    // so its truncation is exact except when P divides x, where it may be
+    // one short (the correction)
+    auto div_p = [&](uint32_t x) {
+      const uint32_t q = static_cast<uint32_t>(static_cast<double>(x) * a.rP);
+      return static_cast<int>(q + ((q + 1u) * static_cast<uint32_t>(a.P) <= x ? 1u : 0u));
+    };
+    const int xlo = div_p(C * p.unit);
+    const int xhi = div_p(C * (p.unit + 1));
     const int lo = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xlo - cs, 0), v)), 63);
     const int hi = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xhi - cs, 0), v)), 63);
     if (b == 0) {
@@ -267,6 +270,19 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
       p.lo = lo;
       p.hi = hi;
       if (p.bad_workers) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
+    }
+  } else if (tid < 128) {
+    const int b = tid - 64;
+    asm volatile("" : "+v"(len), "+v"(cap));
+    // (the same checks as wave 0; the visibility read here is the raw or the
+    // already cleaned word, the same once the bad workers are masked out)
+    if (b < a.NB && len > 0 && len <= cap) {
+      const uint32_t vis = p.vis[b] & ~p.bad_workers;
+#pragma unroll 1
+      for (uint32_t m = vis; m != 0u; m &= m - 1u) {
+        const int w = __builtin_ctz(m);
+        atomicMax(&p.iq[w], static_cast<long long>(p.off[w * a.NB + b]) + len - 1);
+      }
     }
   }
   sync();
@@ -549,7 +565,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   asm volatile("" ::"s"(a.q), "s"(a.k), "s"(a.v), "s"(a.block_len), "s"(a.tables),
                "s"(a.num_entries), "s"(a.ws_hint), "s"(a.plane_elems), "s"(a.plane_bytes),
                "s"(a.W), "s"(a.Hq), "s"(a.G), "s"(a.R), "s"(a.E), "s"(a.NB), "s"(a.P), "s"(a.D), "s"(a.nq),
-               "s"(a.qscale), "s"(a.mP), "s"(a.mE), "s"(a.mG), "s"(a.mGnq));
+               "s"(a.qscale), "s"(a.mP), "s"(a.mE), "s"(a.mG), "s"(a.mGnq), "s"(a.rP));
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;

@@ -78,6 +78,7 @@ struct alignas(16) DecodeArgs {
   uint32_t mP, mE, mG, mGnq, mR;  // div_magic of P, E, G, G * nq and R (indices < 2^16)
   int32_t dtype;            // HW_F32 / HW_BF16 / HW_FP8
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
+  double rP;                // 1 / P (rounded)
   DecodeTables tab;
 };
 
