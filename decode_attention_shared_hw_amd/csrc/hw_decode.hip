@@ -77,10 +77,12 @@ __device__ __forceinline__ void rope_cos_sin(int64_t delta, double w, float* c, 
 // signed value, give the angle in [-1/2, 1/2) revolution.  The hardware
 // v_sin/v_cos take revolutions; the result carries ~1e-6 absolute error, far
 // below the bf16 rounding applied to the rotated query on the MFMA path.
-__device__ __forceinline__ void rope_cos_sin_fx(int64_t delta, uint64_t frac, float* c,
+__device__ __forceinline__ void rope_cos_sin_fx(uint32_t delta, uint64_t frac, float* c,
                                                 float* s) {
-  const uint64_t ph = static_cast<uint64_t>(delta) * frac;
-  const float fr = static_cast<float>(static_cast<int32_t>(ph >> 32)) * 0x1p-32f;
+  // bits 32..63 of delta * frac (mod 2^64), delta < 2^32
+  const uint32_t ph = __umulhi(delta, static_cast<uint32_t>(frac)) +
+                      delta * static_cast<uint32_t>(frac >> 32);
+  const float fr = static_cast<float>(static_cast<int32_t>(ph)) * 0x1p-32f;
   *s = __builtin_amdgcn_sinf(fr);
   *c = __builtin_amdgcn_cosf(fr);
 }
@@ -707,7 +709,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     for (int bi = tid / IPB; bi < ge - gb; bi += nthr / IPB) {
       const int b = gb + bi;
       const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
-      const int64_t delta = iq_lag - plan.off[w * a.NB + b];
+      const uint32_t delta = static_cast<uint32_t>(iq_lag - plan.off[w * a.NB + b]);
       const float sc = vis ? qsc : 0.f;
       u32x4 lo, hi;
 #pragma unroll
