@@ -108,6 +108,7 @@ struct Plan {
   uint32_t bad_workers;
   int32_t flags;
   int32_t head, unit, lo, hi;
+  int32_t b_first, b_last;  // blocks holding tiles lo and hi - 1
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
@@ -267,10 +268,17 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
     const int xhi = div_p(C * (p.unit + 1));
     const int lo = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xlo - cs, 0), v)), 63);
     const int hi = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xhi - cs, 0), v)), 63);
+    // block of tile j: the last b < NB with tile0[b] <= j (tile0 does not
+    // decrease, so these blocks are a prefix)
+    const int t0 = incl - v;
+    const int bf = __builtin_popcountll(__ballot(b < a.NB && t0 <= lo)) - 1;
+    const int bl = __builtin_popcountll(__ballot(b < a.NB && t0 <= hi - 1)) - 1;
     if (b == 0) {
       p.tile0[a.NB] = nt;
       p.lo = lo;
       p.hi = hi;
+      p.b_first = bf;
+      p.b_last = bl;
       if (p.bad_workers) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
     }
   } else if (tid < 128) {
@@ -739,8 +747,8 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // the first group's rotation (front waves), published to the back waves
   if (front) {
     if (plan.lo < plan.hi) {
-      const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
-      const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
+      const int b_first = plan.b_first;
+      const int b_last = plan.b_last;
       rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NF);
     }
     front_sync();
@@ -750,8 +758,8 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     lds_wait_at_least(&sync_ctr[2], kFront);
   }
   if (plan.lo < plan.hi) {
-    const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
-    const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
+    const int b_first = plan.b_first;
+    const int b_last = plan.b_last;
     for (int gb = b_first; gb <= b_last; gb += kQfBlocks) {
       const int ge = min(gb + kQfBlocks, b_last + 1);
       const int t_lo = max(plan.lo, plan.tile0[gb]);
@@ -1168,8 +1176,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
 
   if (plan.lo < plan.hi) {
     const int bq = kQfBlocks;
-    const int b_first = block_of_tile(plan, a.NB, plan.lo, 0);
-    const int b_last = block_of_tile(plan, a.NB, plan.hi - 1, b_first);
+    const int b_first = plan.b_first;
+    const int b_last = plan.b_last;
     for (int gb = b_first; gb <= b_last; gb += bq) {
       const int ge = min(gb + bq, b_last + 1);
       const int t_lo = max(plan.lo, plan.tile0[gb]);
