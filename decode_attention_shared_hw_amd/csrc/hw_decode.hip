@@ -87,6 +87,27 @@ __device__ __forceinline__ void rope_cos_sin_fx(uint32_t delta, uint64_t frac, f
   *c = __builtin_amdgcn_cosf(fr);
 }
 
+// Lane l and lane l ^ 16 (l ^ 32) exchange values through the permlane swap
+// instructions (no LDS round trip): the pair returned holds the lane's own
+// value and its partner's, so a symmetric operation on the pair gives the
+// same result in both lanes.
+__device__ __forceinline__ float max_x16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Stacked rows of kv head g: r = (w * nq + j) * G + (h - g * G) for worker w,
 // query token j < nq and q-head h.  Query j of worker w sits lag = nq - 1 - j
 // positions before the worker's query position i_q (n = 1: the decode query).
@@ -504,8 +525,7 @@ __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
     float mt = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = max_x32(max_x16(mt));
     const float mn = fmaxf(m_run[t], mt);
     const float mu = mn == -INFINITY ? 0.f : mn;
     const float al = __builtin_amdgcn_exp2f(m_run[t] - mu);
@@ -830,8 +850,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // full row sums (the four lanes of a row hold partial sums)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    l_run[t] += __shfl_xor(l_run[t], 16);
-    l_run[t] += __shfl_xor(l_run[t], 32);
+    l_run[t] = sum_x32(sum_x16(l_run[t]));
   }
   // Combine the waves' softmax states (O^T rows below R, m, l) in LDS.  When
   // every wave's state fits (R <= RC1 rows), each wave deposits its state in
@@ -960,14 +979,14 @@ __device__ __forceinline__ float half_max(float x) {
   x = fmaxf(x, dpp_mov<0x4e>(x));   // quad_perm [2,3,0,1]
   x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
   x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
-  return fmaxf(x, __shfl_xor(x, 16));
+  return max_x16(x);
 }
 __device__ __forceinline__ float half_sum(float x) {
   x += dpp_mov<0xb1>(x);
   x += dpp_mov<0x4e>(x);
   x += dpp_mov<0x141>(x);
   x += dpp_mov<0x140>(x);
-  return x + __shfl_xor(x, 16);
+  return sum_x16(x);
 }
 
 template <typename T, int D, int RG>
