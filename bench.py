@@ -93,9 +93,12 @@ def _graph_layers_us(hw, torch, pool, wl, q, reps=20):
     out = torch.zeros(L, W, wl.Hq, wl.D, device="cuda")
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
-    hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne)
     ws = hw.alloc_workspace(pool, W, wl.Hq)
+    # the inputs were written on the default stream: complete them before the
+    # side stream reads them, and build the tables on the side stream itself
+    torch.cuda.synchronize()
     st = torch.cuda.Stream()
+    hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
     with torch.cuda.stream(st):
         for layer in range(L):
             hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
