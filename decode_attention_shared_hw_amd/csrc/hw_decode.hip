@@ -176,8 +176,8 @@ __device__ __forceinline__ void plan_entry(const DecodeArgs& a, Plan& p, int i, 
 
 // The plan costs one memory round trip: every global load is issued before
 // the first wait.  A kernel's code is fetched cold at every launch, so the
-// prologue is kept short and rolled: block-level work runs on wave 0 with one
-// lane per block, table entries on one thread each.
+// prologue is kept short and rolled: block-level work runs on waves 0 and 1
+// with one lane per block, table entries on one thread each.
 // issue(): the kernel's own loads, issued with the plan's; commit(): their
 // LDS stores, run once they have arrived.  NTHR threads (the first NTHR of
 // the workgroup) take part; sync() is their barrier.
@@ -189,7 +189,8 @@ template <int NTHR, typename Issue, typename Commit, typename Sync>
 __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit, Sync& sync) {
   const int tid = threadIdx.x;
   const int WE = a.W * a.E;
-  // ---- loads: per block (lanes of wave 0) length, capacity and first slot;
+  // ---- loads: per block (lanes of waves 0 and 1) length and capacity, and
+  // (wave 0) first slot;
   // per frequency its two forms; one table entry per thread.  The per-call
   // arrays are read from the kernel-argument segment through a pointer
   // (indexing the argument itself would copy it to scratch).
