@@ -111,7 +111,7 @@ struct WsLayout {
   size_t ml_off, acc_off, hint_off, total;
 };
 
-// [Hkv][units][rows] (m, l) pairs, then [Hkv][units][rows][D] accumulators,
+// [Hkv][rows][units] (m, l) pairs, then [Hkv][rows][units][D] accumulators,
 // then [Hkv][units][kMfmaWaves] first-tile hints.
 WsLayout ws_layout(int hkv, int units, int rows, int D) {
   WsLayout w;
