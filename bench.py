@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--units", type=int, default=0, help="split-K units per kv head (0 = auto)")
+    ap.add_argument("--balance", action="store_true",
+                    help="balanced tile order (tiles after each wave's first from a per-head "
+                         "counter) instead of fixed tile ranges per work unit")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -94,19 +97,24 @@ def _graph_layers_us(hw, torch, pool, wl, q, reps=20):
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
     ws = hw.alloc_workspace(pool, W, wl.Hq)
+    plan = hw.alloc_plan(pool, W, wl.Hq)
     # the inputs were written on the default stream: complete them before the
     # side stream reads them, and build the tables on the side stream itself
     torch.cuda.synchronize()
     st = torch.cuda.Stream()
     hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
-    with torch.cuda.stream(st):
+
+    def body():
+        hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=st)
         for layer in range(L):
-            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+            hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, st)
+
+    with torch.cuda.stream(st):
+        body()
         st.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st):
-            for layer in range(L):
-                hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+            body()
         g.replay()
         st.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -193,14 +201,16 @@ def run_loop(args):
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
     ws = hw.alloc_workspace(pool, W, wl.Hq)
+    plan = hw.alloc_plan(pool, W, wl.Hq)
     st = torch.cuda.Stream()
 
     def step_body():
         hw.hw_block_advance(pool, wl.worker_block, st)
         hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
+        hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=st)
         for layer in range(L):
             hw.hw_block_write(pool, layer, wl.worker_block, k_new[layer], v_new[layer], wl.theta, st)
-            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+            hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, st)
 
     lens = np.array(wl.lens, np.int64)
     dec_bytes = 0
@@ -229,7 +239,7 @@ def run_loop(args):
     step_us = ms * 1e3 / steps
     res = {"config": "loop", "workload": wl.name, "steps": steps, "layers": L, "workers": W,
            "appends": len(sched), "common_tokens": [int(wl.lens[0]), int(lens[0])],
-           "step": "advance + tables + 36 x (token write + decode), HIP graph; appends between",
+           "step": "advance + tables + plan + 36 x (token write + decode), HIP graph; appends between",
            "us_per_step": step_us, "us_per_layer": step_us / L,
            "worker_tokens_per_s_per_layer": W * L / (step_us * 1e-6),
            "decode_achieved_gbs": dec_bytes / (ms * 1e-3) / 1e9,
@@ -338,6 +348,7 @@ def time_step(args, hw, torch, np, wl, pool, q):
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
     ws = hw.alloc_workspace(pool, W, wl.Hq)
+    plan = hw.alloc_plan(pool, W, wl.Hq)
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     counter = [0]
@@ -346,10 +357,11 @@ def time_step(args, hw, torch, np, wl, pool, q):
         k = counter[0]
         counter[0] += 1
         hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, stream)
+        hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=stream)
         if events is not None:
             events["dec"][0].record(stream)
         for layer in range(L):
-            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, stream)
+            hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, stream)
         if events is not None:
             events["dec"][1].record(stream)
         src = wl.worker_block[k % W]
@@ -433,7 +445,7 @@ def main():
     if args.config == "loop":
         return run_loop(args)
     path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
-    hw.hw_set_tuning(path, args.units)
+    hw.hw_set_tuning(path, args.units, 1 if args.balance else 0)
 
     wl = workloads.qwq_step(layers=args.layers)
     L, W = wl.layers, wl.W
@@ -472,14 +484,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q; K,V N(0,1) + per-channel N(0,0.5) offset)",
         "config": {**workloads.summary(wl), "parallelism": "single GPU",
-                   "step": "tables + 64 x decode + 1 block append (graph replay)"
-                   if use_graph else "tables + 64 x decode + 1 block append (eager)"},
+                   "step": "tables + plan + 64 x decode + 1 block append (graph replay)"
+                   if use_graph else "tables + plan + 64 x decode + 1 block append (eager)"},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic() if path != hw.PATH_VALU else None,
-            "kernel": ("decode call = split kernel decode_mfma<128,2> + merge_kernel"
-                       if path != hw.PATH_VALU else "decode call = decode_valu<bf16> + merge_kernel"),
+            "kernel": ("decode call = run_mfma<128,2,bf16> (one launch)"
+                       if path != hw.PATH_VALU else "decode call = run_valu<bf16,128,10> (one launch)"),
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": dec_avg,
             "p10_us": float(np.percentile(dec_us, 10)),

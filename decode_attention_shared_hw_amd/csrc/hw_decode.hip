@@ -1,31 +1,31 @@
-// hw_decode.hip — concurrent-attention decode kernels for gfx950.
+// hw_decode.hip — run kernels of a decode call: a split launch and, when a
+// kv head has several work units, a merge launch.
 //
-// One decode call = two launches on the caller's stream:
-//
-//  split kernel, one workgroup per work unit (kv head g, unit u); a unit owns
-//  a contiguous range of 32-token tiles in the concatenation of the blocks
-//  that some worker sees.  Each workgroup
-//   1. decodes the worker tables and the device block lengths into a plan
-//      (visibility, view offsets, i_q, tile prefix)                  [prologue]
-//   2. for every block its range touches, rotates the stacked W*G query rows
-//      of head g by i_q - view_offset: only the single current query token is
-//      rotated, never the cache (Hogwild! notes, key design 1)        [a2]
-//   3. streams its K/V tiles once for all rows with an online softmax in the
-//      exp2 domain (split-K / Flash-Decoding; news 1114328 sec. 3.2)   [a3]
-//   4. writes its partial (m, l, acc) with plain stores.
-//  merge kernel, one workgroup per (kv head, row): log-sum-exp merge of the
-//  units' partials in fixed unit order (deterministic) and the output row [a4].
-//
+// Split launch: one workgroup per work unit (kv head g, unit u).  Each
+// workgroup
+//  1. reads the step's plan (hw_plan.hip), its head's query rows and the
+//     rotation steps into LDS in one memory round trip;
+//  2. for every block it will read, rotates the stacked rows of head g by the
+//     plan's delta (i_q - view_offset - lag): only the current query tokens
+//     are rotated, never the cache (Hogwild! notes, key design 1)        [a2]
+//  3. streams K/V tiles once for all W*G rows with an online softmax in the
+//     exp2 domain (split-K / Flash-Decoding; news 1114328 sec. 3.2)       [a3]
+//     Tiles come either from the unit's contiguous range of the plan
+//     (static: the result is bitwise the same on every run), or, balanced,
+//     one per wave from that range and then one at a time from a per-head
+//     counter, so that units on CUs that HBM serves faster take more tiles;
+//  4. combines its waves' states and stores the unit's partial (m, l, acc),
+//     or, with one unit per head, the final rows.
+// Merge launch: one workgroup per (kv head, row): log-sum-exp merge of the
+// units' partials in fixed unit order and the output row               [a4].
 // The kernel boundary orders the partials' stores before their loads, so no
-// workgroup ever waits on another and no cache maintenance is needed inside
-// a kernel.
+// workgroup waits on another.
 //
-// Two split kernels share the prologue:
-//   decode_valu<T>    fp32 VALU arithmetic over LDS-staged tiles (fp32 and
-//                     bf16 pools, rows <= 64).
-//   decode_mfma<D,NT> bf16 MFMA 16x16x32: S^T = K Q~^T and O^T = V^T P^T with
-//                     tiles loaded straight into operand fragments (the pool
-//                     layout matches them), rows = W*G <= 16*NT <= 32.
+// Two split kernels share the prologue and the epilogue:
+//   run_valu<T>        fp32 VALU arithmetic (fp32 and bf16 pools, rows <= 64)
+//   run_mfma<D,NT,E>   bf16 MFMA 16x16x32: S^T = K Q~^T and O^T = V^T P^T with
+//                      tiles loaded straight into operand fragments (the pool
+//                      layout matches them), rows = W*G <= 16*NT <= 80.
 #include <math.h>
 
 #include <type_traits>
@@ -39,7 +39,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Two floats rounded to bf16 (nearest even), low half first.
@@ -50,15 +49,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-template <typename T>
-__device__ __forceinline__ float load_elem(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_bits_to_f32(p[i]);
 }
 
 // cos/sin of delta * w with the angle formed and reduced mod 2*pi in fp64,
@@ -108,267 +98,265 @@ __device__ __forceinline__ float sum_x32(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Stacked rows of kv head g: r = (w * nq + j) * G + (h - g * G) for worker w,
-// query token j < nq and q-head h.  Query j of worker w sits lag = nq - 1 - j
-// positions before the worker's query position i_q (n = 1: the decode query).
-// The plan holds each row's worker and lag (row_w, row_lag), so the kernels
-// divide by G and nq once.
+// DPP move inside rows of 16 lanes.  The four patterns quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror and row_mirror, applied in turn with a
+// symmetric combine, leave every lane with the combination of its 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRow16[4] = {0xb1, 0x4e, 0x141, 0x140};
 
-// ----------------------------------------------------------------- prologue
-struct Plan {
-  int32_t len[HW_MAX_BLOCKS];
-  uint32_t vis[HW_MAX_BLOCKS];        // bit w set: worker w sees block b
-  int32_t tile0[HW_MAX_BLOCKS + 1];   // tiles of visible blocks, prefix sums
-  long long iq[HW_MAX_WORKERS];       // query position per worker, -1: none
-  int32_t row_w[HW_MAX_ROWS];         // worker of each stacked row (0 past R)
-  int32_t row_lag[HW_MAX_ROWS];       // positions before i_q of each row's query
-  int32_t off[HW_MAX_WORKERS * HW_MAX_BLOCKS];
-  int64_t start[HW_MAX_BLOCKS];       // first slot of each block
-  double invf[kMaxHalf];              // theta^(-2i/D)
-  uint64_t rope_frac[kMaxHalf];       // theta^(-2i/D) / (2 pi) mod 1, 64-bit fixed point
-  uint32_t bad_workers;
-  int32_t flags;
-  int32_t head, unit, lo, hi;
-  int32_t b_first, b_last;  // blocks holding tiles lo and hi - 1
+// max / sum over the 32 lanes of each half of the wave (every lane gets it)
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_mov<0xb1>(x));
+  x = fmaxf(x, dpp_mov<0x4e>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  x = fmaxf(x, dpp_mov<0x140>(x));
+  return max_x16(x);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_mov<0xb1>(x);
+  x += dpp_mov<0x4e>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return sum_x16(x);
+}
+
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+
+// Raw buffer resource (gfx9 descriptor word 3): lane offsets are range-checked
+// against `bytes`, so an offset past the end reads zero and writes nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+
+// Cache policy bits of gfx950 buffer accesses.
+constexpr int kPolicySC0 = 1;   // past the CU's L1 (L2 of the XCD)
+constexpr int kPolicyNT = 2;    // non-temporal: data read once (the K/V stream)
+constexpr int kPolicySC1 = 16;  // device scope: coherent between all CUs of the GPU
+
+// Phase timestamps of an instrumented build (HW_STAMPS, never in the
+// library's own build): thread 0 of each workgroup (lane 0 of each wave for
+// the per-wave stamps) records the 100 MHz real-time clock at fixed points.
+#ifdef HW_STAMPS
+__device__ uint64_t g_stamps[4096 * 32];
+#define HW_STAMP(k) (g_stamps[blockIdx.x * 32 + (k)] = __builtin_amdgcn_s_memrealtime())
+#define HW_MSTAMP(k) (g_stamps[(1024 + blockIdx.x) * 32 + (k)] = __builtin_amdgcn_s_memrealtime())
+#else
+#define HW_STAMP(k) ((void)0)
+#define HW_MSTAMP(k) ((void)0)
+#endif
+
+// ------------------------------------------------------------- plan in LDS
+struct PlanLds {
+  int32_t w[kPlanLdsWords];  // header, visible blocks, lengths (plan words [0, 340))
+  int32_t flags;             // HW_DEV_* bits found by this workgroup
+  int32_t tiles;             // tiles the workgroup processed
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
-// 1, 2, 4 and 8 lanes inside each row of 16, then the last lane of row 0
-// (row 2) is added to row 1 (row 3), and the last lane of row 1 to rows 2
-// and 3.  Lanes shifted in from outside a row read 0.
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
-  return x;
+// Dynamic LDS: the plan's row ends [NB][qrows].
+extern __shared__ int32_t rows_lds[];
+
+// Workgroup -> (kv head, unit): consecutive workgroups take consecutive heads,
+// so a head's units are Hkv workgroups apart (with 8 kv heads and the 8-XCD
+// round-robin dispatch, every unit of a head runs on one XCD).
+__device__ __forceinline__ void head_unit(const RunArgs& a, int* g, int* u) {
+#ifdef HW_HEAD_MAJOR
+  *g = fast_div(blockIdx.x, a.mP);
+  *u = blockIdx.x - *g * a.P;
+#else
+  *u = fast_div(blockIdx.x, a.mHkv);
+  *g = blockIdx.x - *u * a.Hkv;
+#endif
 }
 
-// Workgroup -> (kv head, work unit): the units of a head are consecutive
-// workgroups.
-__device__ __forceinline__ void plan_head_unit(const DecodeArgs& a, int* head, int* unit) {
-  *head = fast_div(blockIdx.x, a.mP);
-  *unit = blockIdx.x - *head * a.P;
-}
-
-// Table entry i (worker i / E, slot i % E): marks its block visible to the
-// worker and records the view offset.  A malformed table (entry count out of
-// range, block id out of range, a block listed twice) marks its worker bad.
-__device__ __forceinline__ void plan_entry(const DecodeArgs& a, Plan& p, int i, hw_entry e,
-                                           int ne) {
-  const int w = fast_div(i, a.mE), slot = i - w * a.E;
-  const uint32_t bit = 1u << w;
-  if (ne < 0 || ne > a.E) {
-    atomicOr(&p.bad_workers, bit);
-    return;
-  }
-  if (slot >= ne) return;
-  const int b = e.block_id;
-  if (b < 0 || b >= a.NB) {
-    atomicOr(&p.bad_workers, bit);
-    return;
-  }
-  if (atomicOr(&p.vis[b], bit) & bit) atomicOr(&p.bad_workers, bit);
-  p.off[w * a.NB + b] = e.view_offset;
-}
-
-// The plan costs one memory round trip: every global load is issued before
-// the first wait.  A kernel's code is fetched cold at every launch, so the
-// prologue is kept short and rolled: block-level work runs on waves 0 and 1
-// with one lane per block, table entries on one thread each.
-// issue(): the kernel's own loads, issued with the plan's; commit(): their
-// LDS stores, run once they have arrived.  NTHR threads (the first NTHR of
-// the workgroup) take part; sync() is their barrier.
-struct WorkgroupBarrier {
-  __device__ void operator()() const { __syncthreads(); }
+// Loads issued at kernel entry: the plan words [0, 340) (85 x 16 bytes), the
+// row ends (one word per thread; larger plans load the rest at commit), every
+// block's current length (for the stale-plan check).
+struct PlanLoads {
+  int4 w;
+  int32_t row;
+  int32_t len;
+  int32_t lo, hi;  // this unit's tile range (uniform)
 };
-
-template <int NTHR, typename Issue, typename Commit, typename Sync>
-__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit, Sync& sync) {
+template <int NTHR>
+__device__ __forceinline__ PlanLoads issue_plan_loads(const RunArgs& a, int u) {
   const int tid = threadIdx.x;
-  const int WE = a.W * a.E;
-  // ---- loads: per block (lanes of waves 0 and 1) length and capacity, and
-  // (wave 0) first slot;
-  // per frequency its two forms; one table entry per thread.  The per-call
-  // arrays are read from the kernel-argument segment through a pointer
-  // (indexing the argument itself would copy it to scratch).
-  const char* tabp = reinterpret_cast<const char*>(&a.tab);
-  int len = 0, cap = 0;
-  int64_t start = 0;
-  // (lane b of waves 0 and 1: block b's length and capacity; wave 0 its start)
-  if (tid < 128 && (tid & 63) < a.NB) {
-    len = a.block_len[tid & 63];
-    cap = reinterpret_cast<const int32_t*>(tabp + offsetof(DecodeTables, block_cap))[tid & 63];
-    if (tid < 64)
-      start = reinterpret_cast<const int64_t*>(tabp + offsetof(DecodeTables, block_start))[tid];
-  }
-  double invf = 0.0;
-  uint64_t frac = 0u;
-  if (tid < a.D / 2) {
-    invf = reinterpret_cast<const double*>(tabp + offsetof(DecodeTables, inv_freq))[tid];
-    frac = reinterpret_cast<const uint64_t*>(tabp + offsetof(DecodeTables, rope_frac))[tid];
-  }
-  hw_entry ent = {-1, 0};
-  int ne = 0;
-  if (tid < WE) {
-    ent = a.tables[tid];
-    ne = a.num_entries[fast_div(tid, a.mE)];
-  }
-  issue();
-  // ---- state that needs none of the loads
-  if (tid < a.NB) p.vis[tid] = 0u;
-  if (tid < a.W) p.iq[tid] = -1;
-  if (tid < HW_MAX_ROWS) {
-    const bool row = tid < a.R;
-    const int w = fast_div(tid, a.mGnq);
-    p.row_w[tid] = row ? w : 0;
-    p.row_lag[tid] = row ? a.nq - 1 - (fast_div(tid, a.mG) - w * a.nq) : 0;
-  }
-  for (int i = tid; i < a.W * a.NB; i += NTHR) p.off[i] = 0;
+  PlanLoads l;
+  l.w = make_int4(0, 0, 0, 0);
+  l.row = -1;
+  l.len = 0;
+  l.lo = a.plan[kPlanUnit + u];
+  l.hi = a.plan[kPlanUnit + u + 1];
+  if (tid < kPlanLdsWords / 4) l.w = reinterpret_cast<const int4*>(a.plan)[tid];
+  if (tid < a.NB * a.qrows) l.row = a.plan[kPlanRows + tid];
+  if (tid < a.NB) l.len = a.block_len[tid];
+  return l;
+}
+template <int NTHR>
+__device__ __forceinline__ void commit_plan_loads(const RunArgs& a, PlanLds& pl,
+                                                  const PlanLoads& l) {
+  const int tid = threadIdx.x;
+  if (tid < kPlanLdsWords / 4) reinterpret_cast<int4*>(pl.w)[tid] = l.w;
+  const int nrow = a.NB * a.qrows;
+  if (tid < nrow) rows_lds[tid] = l.row;
+#pragma unroll 1
+  for (int i = tid + NTHR; i < nrow; i += NTHR) rows_lds[i] = a.plan[kPlanRows + i];
   if (tid == 0) {
-    p.flags = 0;
-    p.bad_workers = 0u;
-    plan_head_unit(a, &p.head, &p.unit);
+    pl.flags = 0;
+    pl.tiles = 0;
   }
-  sync();
-  // ---- visibility and view offsets from the tables
-  commit();
-  if (tid < WE) plan_entry(a, p, tid, ent, ne);
-#pragma unroll 1
-  for (int i = tid + NTHR; i < WE; i += NTHR)
-    plan_entry(a, p, i, a.tables[i], a.num_entries[fast_div(i, a.mE)]);
-  if (tid < a.D / 2) {
-    p.invf[tid] = invf;
-    p.rope_frac[tid] = frac;
-  }
-  if (tid < a.NB) p.start[tid] = start;
-  sync();
-  // ---- wave 0, lane b = block b: checked length, visibility without the
-  // bad workers and the tile prefix over the visible blocks; at the same
-  // time wave 1, lane b = block b: each worker's query position (the last
-  // position of any block it sees)
-  if (tid < 64) {
-    const int b = tid;
-    int v = 0;
-    // (opaque until here: otherwise the compiler compares right after the
-    // loads and waits for them before the rest of the plan's loads are issued)
-    asm volatile("" : "+v"(len), "+v"(cap));
-    if (b < a.NB) {
-      if (len < 0 || len > cap) {
-        atomicOr(&p.flags, HW_DEV_BAD_LENGTH);
-        len = 0;
-      }
-      const uint32_t vis = p.vis[b] & ~p.bad_workers;
-      p.vis[b] = vis;
-      p.len[b] = len;
-      if (vis != 0u && len > 0) v = (len + kTile - 1) / kTile;
-    }
-    const int incl = wave_inclusive_scan(v);
-    const int nt = __builtin_amdgcn_readlane(incl, 63);
-    if (b < a.NB) p.tile0[b] = incl - v;
-    // The units split the tiles by cost: a tile costs 1 and every visible
-    // block after the first kBlockCost more (a unit that reaches another
-    // block rotates its queries before its front waves stream, measured at
-    // about five tiles' time).  Cost position x maps to tile
-    // sum_b clamp(x - cs_b, 0, tiles_b), cs_b being the cost position of
-    // block b's first tile.  C * (unit + 1) < 2^31: a plane holds under 2^31
-    // bytes, so under 2^18 tiles, and there are at most kMaxUnits units.
-    const int cv = v + ((v > 0 && incl > v) ? kBlockCost : 0);
-    const int cincl = wave_inclusive_scan(cv);
-    const uint32_t C = static_cast<uint32_t>(__builtin_amdgcn_readlane(cincl, 63));
-    const int cs = cincl - v;
-    // x / P for x < 2^31: the fp64 product is within 2^-21 of the quotient,
-    // so its truncation is exact except when P divides x, where it may be
-    // one short (the correction)
-    auto div_p = [&](uint32_t x) {
-      const uint32_t q = static_cast<uint32_t>(static_cast<double>(x) * a.rP);
-      return static_cast<int>(q + ((q + 1u) * static_cast<uint32_t>(a.P) <= x ? 1u : 0u));
-    };
-    const int xlo = div_p(C * p.unit);
-    const int xhi = div_p(C * (p.unit + 1));
-    const int lo = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xlo - cs, 0), v)), 63);
-    const int hi = __builtin_amdgcn_readlane(wave_inclusive_scan(min(max(xhi - cs, 0), v)), 63);
-    // block of tile j: the last b < NB with tile0[b] <= j (tile0 does not
-    // decrease, so these blocks are a prefix)
-    const int t0 = incl - v;
-    const int bf = __builtin_popcountll(__ballot(b < a.NB && t0 <= lo)) - 1;
-    const int bl = __builtin_popcountll(__ballot(b < a.NB && t0 <= hi - 1)) - 1;
-    if (b == 0) {
-      p.tile0[a.NB] = nt;
-      p.lo = lo;
-      p.hi = hi;
-      p.b_first = bf;
-      p.b_last = bl;
-      if (p.bad_workers) atomicOr(&p.flags, HW_DEV_BAD_ENTRY);
-    }
-  } else if (tid < 128) {
-    const int b = tid - 64;
-    asm volatile("" : "+v"(len), "+v"(cap));
-    // (the same checks as wave 0; the visibility read here is the raw or the
-    // already cleaned word, the same once the bad workers are masked out)
-    if (b < a.NB && len > 0 && len <= cap) {
-      const uint32_t vis = p.vis[b] & ~p.bad_workers;
-#pragma unroll 1
-      for (uint32_t m = vis; m != 0u; m &= m - 1u) {
-        const int w = __builtin_ctz(m);
-        atomicMax(&p.iq[w], static_cast<long long>(p.off[w * a.NB + b]) + len - 1);
-      }
-    }
-  }
-  sync();
 }
 
-template <int NTHR, typename Issue, typename Commit>
-__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
-  WorkgroupBarrier sync;
-  build_plan<NTHR>(a, p, issue, commit, sync);
-}
-
-// Waves of one workgroup that synchronize through a counter in LDS instead of
-// s_barrier, so that the other waves of the workgroup never have to join:
-// each wave's LDS writes complete (release fence on LDS), lane 0 adds one,
-// and the wave waits until the counter reaches count * phase.  The counter
-// only grows; it must be zero before the first phase.  Every wave of the
-// group reaches every phase (no early exits), so every wait ends.
-struct LdsWaveBarrier {
-  uint32_t* ctr;
-  uint32_t count;
-  uint32_t phase;
-  __device__ void operator()() {
-    ++phase;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if ((threadIdx.x & 63) == 0)
-      __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count * phase)
-      __builtin_amdgcn_s_sleep(1);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+// After the barrier that publishes the plan: this unit's tile range, or an
+// empty one (and HW_DEV_STALE_PLAN) when the plan does not fit this call: made
+// for another shape, or with visible blocks whose tiles would leave the kv-head
+// plane or do not match their lengths (every wave checks, lane j block j, so
+// no tile offset used below can leave the plane).  A block whose length
+// changed since the plan was made also reports HW_DEV_STALE_PLAN.
+template <int D, int EB>
+__device__ __forceinline__ bool unit_range(const RunArgs& a, PlanLds& pl, const PlanLoads& pload,
+                                           int* lo, int* hi) {
+  const int32_t* w = pl.w;
+  const int lane = threadIdx.x & 63;
+  const int lens_loaded = pload.len;
+  int l = pload.lo;
+  int h = pload.hi;
+  const int nvb = w[kHdrNvb];
+  bool ok = w[kHdrMagic] == kPlanMagic && w[kHdrP] == a.P && w[kHdrQrows] == a.qrows &&
+            w[kHdrNB] == a.NB && w[kHdrR] == a.R && nvb >= 0 && nvb <= a.NB && 0 <= l &&
+            l <= h && h <= w[kHdrTiles] && w[kPlanVbTile0] == 0 &&
+            w[kPlanVbTile0 + nvb] == w[kHdrTiles];
+  bool bad = false;
+  if (ok && lane < nvb) {
+    const int64_t start = w[kPlanVbStart + lane], len = w[kPlanVbLen + lane];
+    const int64_t tiles = (len + kTile - 1) / kTile;
+    bad = start < 0 || len <= 0 || w[kPlanVbTile0 + lane + 1] - w[kPlanVbTile0 + lane] != tiles ||
+          (start + tiles * kTile) * D * EB > a.plane_bytes;
   }
-};
-
-// Waits until an LDS counter that other waves advance reaches `target`.
-__device__ __forceinline__ void lds_wait_at_least(uint32_t* ctr, uint32_t target) {
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
-    __builtin_amdgcn_s_sleep(1);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  ok = ok && __ballot(bad) == 0ull;
+  if (!ok) {
+    l = 0;
+    h = 0;
+    if (threadIdx.x == 0) {
+      atomicOr(&pl.flags, HW_DEV_STALE_PLAN);
+      atomicOr(&pl.tiles, 1 << 30);  // (no tile count check for this launch)
+    }
+  }
+  if (static_cast<int>(threadIdx.x) < a.NB && lens_loaded != w[kPlanLens + threadIdx.x])
+    atomicOr(&pl.flags, HW_DEV_STALE_PLAN);
+  *lo = l;
+  *hi = h;
+  return ok;
 }
 
-// Block holding global tile j of the plan (cursor walks forward).
-__device__ __forceinline__ int block_of_tile(const Plan& p, int nb, int j, int b) {
-  while (b + 1 < nb && p.tile0[b + 1] <= j) ++b;
+// Visible blocks holding tiles lo and hi - 1 (every wave, from LDS): lane j
+// tests the first tile of visible block j.
+__device__ __forceinline__ void block_range(const PlanLds& pl, int lo, int hi, int* bf, int* bl) {
+  const int lane = threadIdx.x & 63;
+  const int nvb = pl.w[kHdrNvb];
+  const int t0 = lane < nvb ? pl.w[kPlanVbTile0 + lane] : 0x7fffffff;
+  *bf = __builtin_popcountll(__ballot(t0 <= lo)) - 1;
+  *bl = __builtin_popcountll(__ballot(t0 <= hi - 1)) - 1;
+}
+
+// Visible block of tile j, the cursor walking forward.
+__device__ __forceinline__ int block_of_tile(const PlanLds& pl, int j, int b) {
+  const int nvb = pl.w[kHdrNvb];
+  while (b + 1 < nvb && pl.w[kPlanVbTile0 + b + 1] <= j) ++b;
   return b;
 }
 
-// Per-unit partial: (m, l) per row and the unnormalised accumulator.
-__device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan& p) {
-  return static_cast<int64_t>(p.head) * a.R * a.P + p.unit;
+struct TileRef {
+  int b;          // visible block
+  int valid;      // tokens of the tile inside the block's length
+  int first;      // local position of the tile's first token in its block
+  uint32_t byte;  // byte offset of the tile in the kv-head plane
+};
+
+template <int D, int EB>
+__device__ __forceinline__ TileRef tile_ref(const PlanLds& pl, int j, int& bcur) {
+  bcur = block_of_tile(pl, j, bcur);
+  const int tl = j - pl.w[kPlanVbTile0 + bcur];
+  TileRef r;
+  r.b = bcur;
+  r.valid = min(kTile, pl.w[kPlanVbLen + bcur] - tl * kTile);
+  r.first = tl * kTile;
+  r.byte = static_cast<uint32_t>((pl.w[kPlanVbStart + bcur] + tl * kTile) * D * EB);
+  return r;
+}
+
+// ------------------------------------------------------------ unit finish
+// Stacked rows of kv head g: r = i * G + (h - g * G) for query row i
+// (= w * nq + j) and q-head h; output row (i, h) of out [qrows][Hq][D].
+__device__ __forceinline__ int64_t out_row(const RunArgs& a, int g, int r) {
+  const int i = fast_div(r, a.mG);
+  return static_cast<int64_t>(i) * a.Hq + g * a.G + (r - i * a.G);
+}
+
+// Called by every thread once the waves' states are deposited in LDS: ns
+// states of stride sstride floats, each [rc rows][ACC_STRIDE] accumulators
+// then rc maxima and rc sums.  Combines them 8 outputs per item and stores
+// the unit's partial ([Hkv][R][P] (m, l) pairs, [Hkv][R][P][D]
+// accumulators), or, with one unit per head, the final rows out = O / L.
+template <int NTHR, int D>
+__device__ void emit_unit(const RunArgs& a, PlanLds& pl, int g, int u, const float* sbuf, int ns,
+                          int sstride, int rc) {
+  constexpr int ACC_STRIDE = D + 4;
+  constexpr int kMaxStates = 8;
+  const int tid = threadIdx.x;
+  const int R = a.R, P = a.P;
+  const float vsc = a.dtype == HW_FP8
+                        ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a) +
+                                                         offsetof(RunArgs, v_scale))[g]
+                        : 1.f;
+  for (int x = tid; x < R * (D / 8); x += NTHR) {
+    const int r = x / (D / 8), d8 = 8 * (x - r * (D / 8));
+    float mw[kMaxStates];
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < kMaxStates; ++wv) {
+      mw[wv] = wv < ns ? sbuf[wv * sstride + rc * ACC_STRIDE + r] : -INFINITY;
+      M = fmaxf(M, mw[wv]);
+    }
+    float L = 0.f;
+    f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < kMaxStates; ++wv) {
+        if (wv < ns) {
+          const float* src = sbuf + wv * sstride;
+          const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
+          L += src[rc * ACC_STRIDE + rc + r] * sc;
+          O0 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8) * sc;
+          O1 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8 + 4) * sc;
+        }
+      }
+    }
+    if (P == 1) {
+      const float inv = L > 0.f ? vsc / L : 0.f;
+      float* o = a.out + out_row(a, g, r) * D + d8;
+      *reinterpret_cast<f32x4*>(o) = O0 * inv;
+      *reinterpret_cast<f32x4*>(o + 4) = O1 * inv;
+      if (d8 == 0 && !(L > 0.f)) atomicOr(&pl.flags, HW_DEV_NO_TOKENS);
+    } else {
+      const int64_t pr = (static_cast<int64_t>(g) * R + r) * P + u;
+      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + d8) = O0;
+      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + d8 + 4) = O1;
+      if (d8 == 0) a.ws_ml[pr] = make_float2(M, L);
+    }
+  }
+  if (tid == 0) a.ws_cnt[g * P + u] = pl.tiles;
+  if (P == 1) __syncthreads();
+  if (tid == 0 && pl.flags) atomicOr(a.status, pl.flags);
 }
 
 // ------------------------------------------------------------- MFMA kernel
-// bf16 and FP8 pools, rows R = W*G <= 16*NT.  Each of the eight waves owns
-// every 8th tile of the workgroup's range and keeps its own (m, l, O^T) for
-// all rows; the waves' states are combined in LDS at the end.
+// bf16 and FP8 pools, rows R = W*G <= 16*NT.  Each of the NW waves owns every
+// NW-th tile of the workgroup's range and keeps its own (m, l, O^T) for all
+// rows; the waves' states are combined in LDS at the end.
 //
 // Fragments (v_mfma_f32_16x16x32_bf16, lane l: i = l%16, q4 = l/16):
 //   S^T[tok][row] = K[tok][:] . Q~[row][:]
@@ -380,46 +368,12 @@ __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan
 //     B (P^T): row 16t+i, the same 8 tokens = this lane's S^T outputs
 //     D:       dims 16m + 4*q4 + v, row 16t+i
 
-struct TileRef {
-  int b;          // block
-  int valid;      // tokens of the tile inside the block's length
-  int first;      // local position of the tile's first token in its block
-  int64_t base;   // element offset of the tile in the kv-head plane
-};
-
-template <int D>
-__device__ __forceinline__ TileRef tile_ref(const Plan& p, int nb, int j, int& bcur) {
-  bcur = block_of_tile(p, nb, j, bcur);
-  const int tl = j - p.tile0[bcur];
-  TileRef r;
-  r.b = bcur;
-  r.valid = min(kTile, p.len[bcur] - tl * kTile);
-  r.first = tl * kTile;
-  r.base = (p.start[bcur] + static_cast<int64_t>(tl) * kTile) * D;
-  return r;
-}
-
-constexpr int cmax(int x, int y) { return x > y ? x : y; }
-constexpr int kOneLevelRows = 24;  // rows up to which every wave's state has its own LDS slot
-
-// Raw buffer resource over one kv-head plane (gfx9 descriptor word 3).  The
-// lane offsets are range-checked against the plane; the tile offset (an SGPR
-// operand) is in range by construction: a tile lies inside its block's
-// capacity, whose slots the host checked against the plane.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* p, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes,
-                                           0x00020000);
-}
-
 // Stored K/V elements as MFMA A fragments (8 elements per lane): bf16 pools
 // load 16 bytes and use them as they are; FP8 E4M3 pools load 8 bytes, which
 // are widened to bf16 (exactly: every E4M3 value is a bf16 value) just before
 // the product that consumes them, so the registers of a tile in flight hold
-// the narrow codes.
-// K/V fragments are read exactly once per call: their loads carry the
-// non-temporal cache policy (aux bit 1, `nt`), which measured 1.5 us faster per
-// 76 MB call than the default policy.
-constexpr int kStreamLoad = 2;
+// the narrow codes.  Every K/V fragment is read exactly once per call: the
+// loads carry the non-temporal policy.
 template <typename E>
 struct KvFrag;
 template <>
@@ -427,7 +381,7 @@ struct KvFrag<uint16_t> {
   typedef u32x4 type;
   static constexpr int kBytes = 2;
   __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kStreamLoad);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kPolicyNT);
   }
   __device__ static u32x4 widen(const type& f) { return f; }
 };
@@ -436,7 +390,7 @@ struct KvFrag<uint8_t> {
   typedef u32x2 type;
   static constexpr int kBytes = 1;
   __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kStreamLoad);
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kPolicyNT);
   }
   template <bool HI>
   __device__ static uint32_t pair(uint32_t w) {
@@ -450,7 +404,10 @@ struct KvFrag<uint8_t> {
 // (a3) one buffer load per lane per fragment: every key load of a wave is one
 // contiguous run (1 KB bf16, 512 B FP8), every value load four contiguous
 // runs.  koff / voff: this lane's byte offsets inside a tile; tile: the tile's
-// byte offset in the plane (wave-uniform, kept in an SGPR).
+// byte offset in the plane (wave-uniform, an SGPR operand).  The plane's
+// resource range-checks the lane offsets; the tile offset is inside the plane
+// by construction (a tile lies inside its block's capacity, whose slots the
+// host checked against the plane).
 template <int D, typename E>
 __device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t tile, uint32_t koff,
                                           typename KvFrag<E>::type (&kf)[2][D / 32]) {
@@ -468,19 +425,6 @@ __device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t
   constexpr int B = KvFrag<E>::kBytes;
 #pragma unroll
   for (int m = 0; m < D / 16; ++m) vf[m] = KvFrag<E>::load(vrs, voff + 16 * m * 8 * B, tile);
-}
-
-// The same loads with the tile offset in the range-checked lane offset: a
-// tile offset past the plane reads zeros, so any value may be passed (used
-// for the speculative first tile, whose offset comes from the last call).
-template <int D, typename E>
-__device__ __forceinline__ void load_tile_checked(__amdgpu_buffer_rsrc_t krs,
-                                                  __amdgpu_buffer_rsrc_t vrs, uint32_t tile,
-                                                  uint32_t koff, uint32_t voff,
-                                                  typename KvFrag<E>::type (&kf)[2][D / 32],
-                                                  typename KvFrag<E>::type (&vf)[D / 16]) {
-  load_keys<D, E>(krs, 0, koff + tile, kf);
-  load_values<D, E>(vrs, 0, voff + tile, vf);
 }
 
 // S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
@@ -507,7 +451,9 @@ __device__ __forceinline__ void tile_scores(const typename KvFrag<E>::type (&kf)
 
 // Online softmax of one tile's scores and the P.V update of the running
 // (m, l, O^T).  Row t keeps the tile's tokens up to rowlim[t] (its causal
-// limit, below `valid`); values of tokens at or past `valid` are zeroed.
+// limit, below `valid`); values of tokens at or past `valid` are zeroed.  The
+// row sum adds the bf16-rounded weights the P.V product uses, so numerator
+// and denominator carry the same weights.
 template <int D, int NT, typename E>
 __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
                                             const typename KvFrag<E>::type (&vf)[D / 16],
@@ -538,9 +484,8 @@ __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
     bf16x8 f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pv = __builtin_amdgcn_exp2f(sv[e] - mu);
-      sum += pv;
-      f[e] = static_cast<__bf16>(pv);
+      f[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[e] - mu));
+      sum += static_cast<float>(f[e]);
     }
     pf[t] = f;
     l_run[t] = l_run[t] * al + sum;
@@ -568,133 +513,101 @@ __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
   }
 }
 
+// A group's first tile is requested after its rotated queries are published
+// (0), its keys before the rotation (1), keys and values before it (2), or
+// (3) keys and values before it by the upper half of the waves while the
+// lower half rotates.  A
+// CU takes about 64 KB of outstanding loads before a wave's next load blocks
+// at issue, so requesting 8 waves' 16 KB tiles first stalls the rotation and
+// the barrier behind it until the first tiles return.
+#ifndef HW_ISSUE_BEFORE_ROTATION
+#define HW_ISSUE_BEFORE_ROTATION 1
+#endif
+constexpr int kIssueBeforeRotation = HW_ISSUE_BEFORE_ROTATION;
+// Rows up to which every wave's state has its own LDS slot (one-level combine).
+constexpr int kOneLevelRows = 20;
+// Waves of the MFMA kernel: 8 (two per SIMD) up to 32 rows; above that the
+// accumulators of 48..80 rows need the register file of one wave per SIMD.
+constexpr int mfma_waves(int NT) { return NT <= 2 ? 8 : 4; }
+
 template <int D, int NT, typename E>
-__global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   typedef typename KvFrag<E>::type Frag;
   constexpr int EB = KvFrag<E>::kBytes;
-  constexpr int NTHR = kMfmaThreads;
-  constexpr int NWAVE = kMfmaWaves;
-  constexpr int NSTATE = NWAVE / 2;  // wave states held in LDS at once
-  constexpr int KS = D / 32;  // k-steps of the QK product
-  constexpr int MT = D / 16;  // 16-dim tiles of the output
-  constexpr int RP = 16 * NT; // padded rows
+  constexpr int NWAVE = mfma_waves(NT);
+  constexpr int NTHR = 64 * NWAVE;
+  constexpr int NSTATE = NWAVE / 2;  // wave states held in LDS at once (two-level combine)
+  constexpr int KS = D / 32;         // k-steps of the QK product
+  constexpr int MT = D / 16;         // 16-dim tiles of the output
+  constexpr int RP = 16 * NT;        // padded rows
   constexpr int HALF = D / 2;
   constexpr int ACC_STRIDE = D + 4;
-  // one wave's (O^T, m, l) with room for RC1 rows (all waves at once) or RP
-  // rows (half of the waves at a time)
+  constexpr int kQf = NT <= 2 ? 6 : 1;  // blocks whose rotated queries are in LDS at once
+  constexpr bool kOneLevelOk = NWAVE == 8;
   constexpr int RC1 = RP < kOneLevelRows ? RP : kOneLevelRows;
   constexpr int kState1 = RC1 * ACC_STRIDE + 2 * RC1;
   constexpr int kState2 = RP * ACC_STRIDE + 2 * RP;
-  constexpr int kQfFloats = kQfBlocks * NT * KS * 64 * 4;  // rotated-query fragments
-  constexpr int kEpiFloats = cmax(NWAVE * kState1, NSTATE * kState2);
-  __shared__ Plan plan;
+  constexpr int kEpiFloats = cmax(kOneLevelOk ? NWAVE * kState1 : 0, NSTATE * kState2);
+  constexpr int kQfFloats = kQf * NT * KS * 64 * 4;
+  __shared__ PlanLds pl;
+  __shared__ uint64_t fracs[HALF];
   __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
-  // the rotated-query fragments of up to kQfBlocks blocks (main loop)
   __shared__ __attribute__((aligned(16))) float qbuf[kQfFloats];
   // the waves' softmax states (epilogue); apart from qbuf, so that a wave
   // done with its tiles deposits its state while the others still stream
   __shared__ __attribute__((aligned(16))) float ebuf[kEpiFloats];
 
-  // every scalar argument of the prologue, requested at entry in one round
-  // trip (otherwise each use site waits for its own kernel-argument load)
-  asm volatile("" ::"s"(a.q), "s"(a.k), "s"(a.v), "s"(a.block_len), "s"(a.tables),
-               "s"(a.num_entries), "s"(a.ws_hint), "s"(a.plane_elems), "s"(a.plane_bytes),
-               "s"(a.W), "s"(a.Hq), "s"(a.G), "s"(a.R), "s"(a.E), "s"(a.NB), "s"(a.P), "s"(a.D), "s"(a.nq),
-               "s"(a.qscale), "s"(a.mP), "s"(a.mE), "s"(a.mG), "s"(a.mGnq), "s"(a.rP));
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  // The waves split for the prologue.
-  //  front (waves < kFront): load the tables, lengths and this head's query
-  //    rows, build the plan and the first group's rotated queries, and
-  //    synchronize among themselves through an LDS counter;
-  //  back: once the front waves' loads are back, request their speculative
-  //    first tile (the tile each started with in the previous call with this
-  //    workspace: within a decode step every layer's call has the same plan),
-  //    then wait for the rotated queries and keep the tile if the plan
-  //    confirms it.
-  // A wave whose tile requests stall on a full memory queue (a CU accepts
-  // about 64 KB before issue blocks) thus never holds a barrier the plan
-  // needs.  The front waves request their first tiles after the rotation.
-  constexpr int kFront = 4;
-  constexpr int NF = kFront * 64;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const bool front = wave_u < kFront;  // wave-uniform: one side of each branch per wave
-  __shared__ uint32_t sync_ctr[3];  // front barrier, front loads issued, rotation done
-  if (tid < 3) sync_ctr[tid] = 0u;
-  // publishes the zeroed counters; each wave passes it once, the front waves
-  // right after requesting the plan's loads, the back waves first
-  auto init_barrier = [] {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  };
-  // this head's query rows, staged in LDS so that the main loop issues no
-  // vector memory operations other than the K/V stream
+  if (tid == 0) HW_STAMP(0);
+  int g, u;
+  head_unit(a, &g, &u);
+
+  // ---- 1. one round trip: plan, lengths, rotation steps, this head's rows
   constexpr int kQVec = RP * D / 8;
-  constexpr int kQRegs = (kQVec + NF - 1) / NF;
-  int h0, u0;
-  plan_head_unit(a, &h0, &u0);
+  constexpr int kQRegs = (kQVec + NTHR - 1) / NTHR;
+  const PlanLoads pload = issue_plan_loads<NTHR>(a, u);
+  uint64_t frac = 0;
+  if (tid < HALF)
+    frac = reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(&a) +
+                                             offsetof(RunArgs, rope_frac))[tid];
+  u32x4 qv[kQRegs];
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int k = 0; k < kQRegs; ++k) {
+    const int x = tid + k * NTHR;
+    const int r = (8 * x) / D, d = (8 * x) - r * D;
+    qv[k] = u32x4{0u, 0u, 0u, 0u};
+    if (x < kQVec && r < a.R)
+      qv[k] = *reinterpret_cast<const u32x4*>(qg + out_row(a, g, r) * D + d);
+  }
+  // this head's K/V plane descriptors and the query scale (FP8 pools: times
+  // the key scale of the kv head)
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(
+      static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.plane_elems * EB, a.plane_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(
+      static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.plane_elems * EB, a.plane_bytes);
+  float qsc = a.qscale;
+  if (EB == 1)
+    qsc *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a) +
+                                          offsetof(RunArgs, k_scale))[g];
+  commit_plan_loads<NTHR>(a, pl, pload);
+  if (tid < HALF) fracs[tid] = frac;
+#pragma unroll
+  for (int k = 0; k < kQRegs; ++k) {
+    const int x = tid + k * NTHR;
+    if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
+  }
+  __syncthreads();
+  if (tid == 0) HW_STAMP(1);
+  int lo, hi, b_first, b_last;
+  const bool plan_ok = unit_range<D, EB>(a, pl, pload, &lo, &hi);
+  block_range(pl, lo, hi, &b_first, &b_last);
+
   const uint32_t koff = (q4 * 128 + li * 8) * EB;
   const uint32_t voff = (q4 * 8 * D + li * 8) * EB;
-  // this head's K/V plane descriptors, the query scale (FP8 pools: times the
-  // key scale of the kv head) and this wave's hint slot; set up by the front
-  // waves while their plan loads are in flight, by the back waves first
-  __amdgpu_buffer_rsrc_t krs, vrs;
-  float qsc;
-  uint32_t* hint;
-  auto kv_setup = [&] {
-    krs = plane_rsrc(static_cast<const char*>(a.k) + static_cast<int64_t>(h0) * a.plane_elems * EB,
-                     a.plane_bytes);
-    vrs = plane_rsrc(static_cast<const char*>(a.v) + static_cast<int64_t>(h0) * a.plane_elems * EB,
-                     a.plane_bytes);
-    qsc = a.qscale;
-    if (EB == 1) qsc *= reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
-                                                       offsetof(DecodeTables, k_scale))[h0];
-    hint = a.ws_hint + (static_cast<int64_t>(h0) * a.P + u0) * NWAVE + wave_u;
-  };
-  uint32_t spec = 0xffffffffu;  // back waves: the hinted first tile
   Frag kf[2][KS], vf[MT];
-  LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u};
-  if (front) {
-    u32x4 qv[kQRegs];
-    auto issue = [&] {
-#pragma unroll
-      for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * NF;
-        const int r = (8 * x) / D, d = (8 * x) - r * D;
-        qv[k] = u32x4{0u, 0u, 0u, 0u};
-        if (x < kQVec && r < a.R) {
-          const int w = fast_div(r, a.mG), h = h0 * a.G + (r - w * a.G);
-          qv[k] =
-              *reinterpret_cast<const u32x4*>(qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d);
-        }
-      }
-      init_barrier();
-      kv_setup();
-    };
-    auto commit = [&] {
-#pragma unroll
-      for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * NF;
-        if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
-      }
-      // the plan's loads are back: the back waves' tiles may now fill the
-      // memory queues (issued earlier, they delay these small loads by the
-      // whole chip's burst)
-      if (lane == 0) __hip_atomic_fetch_add(&sync_ctr[1], 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_WORKGROUP);
-    };
-    build_plan<NF>(a, plan, issue, commit, front_sync);
-  } else {
-    kv_setup();
-    const uint32_t hv = *hint;  // (loaded by the back waves only)
-    init_barrier();
-    spec = __builtin_amdgcn_readfirstlane(hv);
-    lds_wait_at_least(&sync_ctr[1], kFront);
-    load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
-  }
   bool rowvis[NT];
   f32x4 acc[MT][NT];
   float m_run[NT], l_run[NT];
@@ -707,144 +620,177 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     for (int m = 0; m < MT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // (a2) rotated queries of blocks gb..ge-1, shared by all waves: for each
-  // block the stacked rows of head g rotated by i_q - view_offset of their
-  // worker, scaled, rounded to bf16 and laid out as MFMA B fragments
-  // (row 16t+li, dims 8*(4s+q4)..+8 at qfs[((blk*NT + t)*KS + s)*64 + lane]).
-  // Rows past R or of workers that do not see the block are zero.  nthr: the
-  // threads taking part.
+  // (a2) rotated queries of visible blocks gb..ge-1, shared by all waves: for
+  // each block the stacked rows of head g rotated by their row end (the
+  // delta), scaled, rounded to bf16 and laid out as MFMA B fragments
+  // (row 16t+li, dims 8*(4s+q4)..+8 at qfs[((bi*NT + t)*KS + s)*64 + lane]).
+  // Rows past R or that see nothing of the block are zero.  Item (bi, t, sh,
+  // lane) rotates the 8 pairs (d0 + e, d0 + e + D/2), d0 = 8*(4*sh + q4).
   bf16x8* qfs = reinterpret_cast<bf16x8*>(qbuf);
-  // A thread's item (row, dims) is the same in every block (nthr is a
-  // multiple of IPB): its query values, frequencies, worker and i_q - lag are
-  // read from LDS once; per block only the view offset and visibility.
   constexpr int IPB = NT * (KS / 2) * 64;  // items per block
   auto rotate_blocks = [&](int gb, int ge, int nthr) {
-    const int slot = tid & (IPB - 1);
-    const int ln = slot & 63;
-    const int y = slot >> 6;
-    const int sh = y % (KS / 2);
-    const int t = y / (KS / 2);
-    const int r = 16 * t + (ln & 15);
-    const int w = plan.row_w[r];
-    const long long iq_lag = plan.iq[w] - plan.row_lag[r];
-    const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner dims are d0 + HALF
-    const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
-    uint32_t xw[4], yw[4];
-    uint64_t fr[8];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      xw[e2] = qw[e2];
-      yw[e2] = qw[e2 + HALF / 2];
-      fr[2 * e2] = plan.rope_frac[d0 + 2 * e2];
-      fr[2 * e2 + 1] = plan.rope_frac[d0 + 2 * e2 + 1];
-    }
+    for (int x = tid; x < (ge - gb) * IPB; x += nthr) {
+      const int bi = x / IPB;
+      const int slot = x - bi * IPB;
+      const int ln = slot & 63;
+      const int y = slot >> 6;
+      const int sh = y % (KS / 2);
+      const int t = y / (KS / 2);
+      const int r = 16 * t + (ln & 15);
+      const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner dims are d0 + HALF
+      int re = -1;
+      if (r < a.R) re = rows_lds[(gb + bi) * a.qrows + fast_div(r, a.mG)];
+      const float sc = re >= 0 ? qsc : 0.f;
+      const uint32_t delta = static_cast<uint32_t>(re >= 0 ? re : 0);
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
+      uint32_t* lo4 = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh) * 64 + ln);
+      uint32_t* hi4 = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh + KS / 2) * 64 + ln);
+      // (rolled: this code runs once per launch and is fetched cold)
 #pragma unroll 1
-    for (int bi = tid / IPB; bi < ge - gb; bi += nthr / IPB) {
-      const int b = gb + bi;
-      const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
-      const uint32_t delta = static_cast<uint32_t>(iq_lag - plan.off[w * a.NB + b]);
-      const float sc = vis ? qsc : 0.f;
-      u32x4 lo, hi;
-#pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float x0 = __uint_as_float(xw[e2] << 16), x1 = __uint_as_float(xw[e2] & 0xffff0000u);
-        const float y0 = __uint_as_float(yw[e2] << 16), y1 = __uint_as_float(yw[e2] & 0xffff0000u);
+        const uint32_t xw = qw[e2], yw = qw[e2 + HALF / 2];
+        const float x0 = __uint_as_float(xw << 16), x1 = __uint_as_float(xw & 0xffff0000u);
+        const float y0 = __uint_as_float(yw << 16), y1 = __uint_as_float(yw & 0xffff0000u);
         float c0, s0, c1, s1;
-        rope_cos_sin_fx(delta, fr[2 * e2], &c0, &s0);
-        rope_cos_sin_fx(delta, fr[2 * e2 + 1], &c1, &s1);
-        lo[e2] = pack_bf16x2((x0 * c0 - y0 * s0) * sc, (x1 * c1 - y1 * s1) * sc);
-        hi[e2] = pack_bf16x2((y0 * c0 + x0 * s0) * sc, (y1 * c1 + x1 * s1) * sc);
+        rope_cos_sin_fx(delta, fracs[d0 + 2 * e2], &c0, &s0);
+        rope_cos_sin_fx(delta, fracs[d0 + 2 * e2 + 1], &c1, &s1);
+        lo4[e2] = pack_bf16x2((x0 * c0 - y0 * s0) * sc, (x1 * c1 - y1 * s1) * sc);
+        hi4[e2] = pack_bf16x2((y0 * c0 + x0 * s0) * sc, (y1 * c1 + x1 * s1) * sc);
       }
-      *reinterpret_cast<u32x4*>(qfs + ((bi * NT + t) * KS + sh) * 64 + ln) = lo;
-      *reinterpret_cast<u32x4*>(qfs + ((bi * NT + t) * KS + sh + KS / 2) * 64 + ln) = hi;
     }
   };
 
-  // Blocks with tiles in [lo, hi) form the index range [b_first, b_last];
-  // they are rotated kQfBlocks at a time.  Within a group, a software
-  // pipeline runs over this wave's tiles j, j + NWAVE, ...: the next tile's
-  // keys are loaded into the key registers as soon as the current scores are
-  // formed, its values into the value registers right after the P.V products,
-  // so every wave keeps a tile in flight while it computes.  A later group's
-  // first tile is requested before its rotation; in the first group the back
-  // waves keep their speculative tile when the plan confirms it.
-  uint32_t first = 0xffffffffu;  // this wave's first tile (byte offset), none: all ones
-  // the first group's rotation (front waves), published to the back waves
-  if (front) {
-    if (plan.lo < plan.hi) {
-      const int b_first = plan.b_first;
-      const int b_last = plan.b_last;
-      rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NF);
+  // One tile of the loop: per-row limits from the plan when the tile's block
+  // changes, scores, then the next tile's keys requested into the key
+  // registers, the softmax and P.V update, the next tile's values requested.
+  // Every wave keeps a tile in flight while it computes.
+  int qb = -1;
+  int rowend[NT];
+  const bf16x8* qf = qfs;
+  // (`more` is a compile-time flag: with the next tile's loads conditional
+  // the compiler cannot count the loads in flight and waits for all of them
+  // before the scores, this tile's values included)
+  auto step = [&](const TileRef& rt, int gb, auto more_c, uint32_t tn) {
+    constexpr bool more = decltype(more_c)::value;
+    if (rt.b != qb) {
+      qb = rt.b;
+      qf = qfs + (qb - gb) * NT * KS * 64;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int r = 16 * t + li;
+        rowend[t] = r < a.R ? rows_lds[qb * a.qrows + fast_div(r, a.mG)] : -1;
+        rowvis[t] = rowend[t] >= 0;
+      }
     }
-    front_sync();
+    int rowlim[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) rowlim[t] = min(rt.valid - 1, rowend[t] - rt.first);
+    f32x4 sc[2][NT];
+    tile_scores<D, NT, E>(kf, qf, lane, sc);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (more) load_keys<D, E>(krs, tn, koff, kf);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_update<D, NT, E>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (more) load_values<D, E>(vrs, tn, voff, vf);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const std::true_type kMore;
+  const std::false_type kLast;
+
+  int done_tiles = 0;  // tiles this wave processed
+  const int nvb = pl.w[kHdrNvb];
+  if (a.balance && plan_ok && nvb <= kQf && a.P > 1) {
+    // Balanced: every visible block rotated at once; wave w of unit u takes
+    // tile u*NWAVE + w, then tiles from the head's counter (tickets start
+    // after the P*NWAVE first tiles; a wave without a first tile starts with
+    // a ticket).  Each wave's next ticket is requested one tile ahead, so its
+    // latency hides under the current tile (the first under the rotation).
+    const int T = pl.w[kHdrTiles];
+    const int base = a.P * NWAVE;
+    uint32_t* ctr = a.sync + static_cast<int64_t>(g) * kSyncStride;
+    int j = u * NWAVE + wave;
+    int bcur = 0;
+    TileRef rt = {0, 0, 0, 0u};
+    if (j < T) {
+      rt = tile_ref<D, EB>(pl, j, bcur);
+      const uint32_t t0 = __builtin_amdgcn_readfirstlane(rt.byte);
+      load_keys<D, E>(krs, t0, koff, kf);
+      load_values<D, E>(vrs, t0, voff, vf);
+    }
+    uint32_t ticket = 0;
     if (lane == 0)
-      __hip_atomic_fetch_add(&sync_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else {
-    lds_wait_at_least(&sync_ctr[2], kFront);
-  }
-  if (plan.lo < plan.hi) {
-    const int b_first = plan.b_first;
-    const int b_last = plan.b_last;
-    for (int gb = b_first; gb <= b_last; gb += kQfBlocks) {
-      const int ge = min(gb + kQfBlocks, b_last + 1);
-      const int t_lo = max(plan.lo, plan.tile0[gb]);
-      const int t_hi = min(plan.hi, plan.tile0[ge]);
+      ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    rotate_blocks(0, nvb, NTHR);
+    __syncthreads();
+    if (tid == 0) HW_STAMP(2);
+    if (j >= T) {
+      j = base + static_cast<int>(__builtin_amdgcn_readfirstlane(ticket));
+      if (j < T) {
+        if (lane == 0)
+          ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        rt = tile_ref<D, EB>(pl, j, bcur);
+        const uint32_t t0 = __builtin_amdgcn_readfirstlane(rt.byte);
+        load_keys<D, E>(krs, t0, koff, kf);
+        load_values<D, E>(vrs, t0, voff, vf);
+      }
+    }
+    while (j < T) {
+      const int jn = base + static_cast<int>(__builtin_amdgcn_readfirstlane(ticket));
+      ++done_tiles;
+      if (jn >= T) {
+        step(rt, 0, kLast, 0u);
+        break;
+      }
+      if (lane == 0)
+        ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const TileRef rn = tile_ref<D, EB>(pl, jn, bcur);
+      step(rt, 0, kMore, __builtin_amdgcn_readfirstlane(rn.byte));
+      j = jn;
+      rt = rn;
+    }
+  } else if (lo < hi) {
+    // Static: blocks with tiles in [lo, hi) form the index range [b_first,
+    // b_last], rotated kQf at a time; wave w takes tiles lo + w, lo + w +
+    // NWAVE, ... of each group.  A group's first tile is requested before
+    // its rotation (kIssueBeforeRotation).
+    for (int gb = b_first; gb <= b_last; gb += kQf) {
+      const int ge = min(gb + kQf, b_last + 1);
+      const int t_lo = max(lo, pl.w[kPlanVbTile0 + gb]);
+      const int t_hi = min(hi, pl.w[kPlanVbTile0 + ge]);
       int j = t_lo + wave;
       int bcur = gb;
-      TileRef rt = {0, 0, 0, 0};
+      TileRef rt = {0, 0, 0, 0u};
+      uint32_t tile0 = 0;
+      // mode 3: the upper half of the waves requests its first tiles at
+      // once while the lower half rotates (a CU holds ~64 KB of requests:
+      // half the waves' tiles), then requests its own
+      const bool early = kIssueBeforeRotation == 3 ? wave >= NWAVE / 2 : kIssueBeforeRotation >= 1;
+      const bool early_v = kIssueBeforeRotation == 3 ? early : kIssueBeforeRotation >= 2;
       if (j < t_hi) {
-        rt = tile_ref<D>(plan, a.NB, j, bcur);
-        const uint32_t tile = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * EB));
-        if (gb == b_first) first = tile;
-        if (gb != b_first || front || tile != spec) {
-          load_keys<D, E>(krs, tile, koff, kf);
-          load_values<D, E>(vrs, tile, voff, vf);
-        }
+        rt = tile_ref<D, EB>(pl, j, bcur);
+        tile0 = __builtin_amdgcn_readfirstlane(rt.byte);
+        if (early) load_keys<D, E>(krs, tile0, koff, kf);
+        if (early_v) load_values<D, E>(vrs, tile0, voff, vf);
       }
-      if (gb != b_first) {
-        __syncthreads();  // the previous group's fragments are consumed
-        rotate_blocks(gb, ge, NTHR);
-        __syncthreads();
-      }
+      if (gb != b_first) __syncthreads();  // the previous group's fragments are consumed
+      if (kIssueBeforeRotation != 3 || wave < NWAVE / 2)
+        rotate_blocks(gb, ge, kIssueBeforeRotation == 3 ? NTHR / 2 : NTHR);
+      __syncthreads();
+      if (tid == 0 && gb == b_first) HW_STAMP(2);
+      qb = -1;
       if (j < t_hi) {
-        int qb = -1;
-        int rowend[NT];
-        const bf16x8* qf = qfs;
+        if (!early) load_keys<D, E>(krs, tile0, koff, kf);
+        if (!early_v) load_values<D, E>(vrs, tile0, voff, vf);
         for (;;) {
-          if (rt.b != qb) {
-            qb = rt.b;
-            qf = qfs + (qb - gb) * NT * KS * 64;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const int r = 16 * t + li;
-              const int w = plan.row_w[r];
-              rowvis[t] = r < a.R && ((plan.vis[qb] >> w) & 1u);
-              // last local position row r may see in this block (causal limit)
-              rowend[t] = rowvis[t]
-                              ? static_cast<int>(plan.iq[w] - plan.row_lag[r] - plan.off[w * a.NB + qb])
-                              : -1;
-            }
-          }
-          int rowlim[NT];
-#pragma unroll
-          for (int t = 0; t < NT; ++t) rowlim[t] = min(rt.valid - 1, rowend[t] - rt.first);
-          f32x4 sc[2][NT];
           const int jn = j + NWAVE;
+          ++done_tiles;
           if (jn >= t_hi) {
-            tile_scores<D, NT, E>(kf, qf, lane, sc);
-            tile_update<D, NT, E>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
+            step(rt, gb, kLast, 0u);
             break;
           }
-          const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
-          const uint32_t tn = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * EB));
-          tile_scores<D, NT, E>(kf, qf, lane, sc);
-          __builtin_amdgcn_sched_barrier(0);
-          load_keys<D, E>(krs, tn, koff, kf);
-          __builtin_amdgcn_sched_barrier(0);
-          tile_update<D, NT, E>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
-          __builtin_amdgcn_sched_barrier(0);
-          load_values<D, E>(vrs, tn, voff, vf);
-          __builtin_amdgcn_sched_barrier(0);
+          const TileRef rn = tile_ref<D, EB>(pl, jn, bcur);
+          step(rt, gb, kMore, __builtin_amdgcn_readfirstlane(rn.byte));
           j = jn;
           rt = rn;
         }
@@ -852,18 +798,20 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     }
   }
 
+  if (lane == 0) {
+    HW_STAMP(3 + wave);
+    atomicAdd(&pl.tiles, done_tiles);
+  }
   // full row sums (the four lanes of a row hold partial sums)
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    l_run[t] = sum_x32(sum_x16(l_run[t]));
-  }
-  // Combine the waves' softmax states (O^T rows below R, m, l) in LDS.  When
-  // every wave's state fits (R <= RC1 rows), each wave deposits its state in
-  // its own slot as soon as its tiles are done; otherwise, after a barrier,
-  // half of them at a time: the upper waves deposit, each lower wave folds in
-  // its partner (same fragment positions, so lane-local), and the lower
-  // waves deposit.  Then every thread combines its share of the unit's R*D
-  // outputs over the deposited states and stores the partial.
+  for (int t = 0; t < NT; ++t) l_run[t] = sum_x32(sum_x16(l_run[t]));
+  // Combine the waves' states (O^T rows below R, m, l) in LDS.  When every
+  // wave's state fits (R <= RC1 rows, 8 waves), each wave deposits its state
+  // in its own slot as soon as its tiles are done; otherwise, after a
+  // barrier, half of them at a time: the upper waves deposit, each lower wave
+  // folds in its partner (same fragment positions, so lane-local), and the
+  // lower waves deposit.  Then every thread combines its share of the unit's
+  // R*D outputs over the deposited states.
   auto deposit = [&](float* buf, int rc) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -878,41 +826,12 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         *reinterpret_cast<f32x4*>(buf + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
     }
   };
-  const int64_t pu = partial_index(a, plan);
-  auto combine_store = [&](auto nstate_c, int state, int rc) {
-    constexpr int NS = decltype(nstate_c)::value;
-    // 8 outputs per item: R * D / 8 items (320 at 20 rows), one per thread
-    for (int x = tid; x < a.R * (D / 8); x += NTHR) {
-      const int r = x / (D / 8), d8 = 8 * (x - r * (D / 8));
-      float mw[NS];
-      float M = -INFINITY;
-#pragma unroll
-      for (int wv = 0; wv < NS; ++wv) {
-        mw[wv] = ebuf[wv * state + rc * ACC_STRIDE + r];
-        M = fmaxf(M, mw[wv]);
-      }
-      float L = 0.f;
-      f32x4 O0 = f32x4{0.f, 0.f, 0.f, 0.f}, O1 = O0;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int wv = 0; wv < NS; ++wv) {
-          const float* src = ebuf + wv * state;
-          const float sc = mw[wv] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[wv] - M);
-          L += src[rc * ACC_STRIDE + rc + r] * sc;
-          O0 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8) * sc;
-          O1 += *reinterpret_cast<const f32x4*>(src + r * ACC_STRIDE + d8 + 4) * sc;
-        }
-      }
-      const int64_t pr = pu + static_cast<int64_t>(r) * a.P;
-      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + d8) = O0;
-      *reinterpret_cast<f32x4*>(a.ws_acc + pr * D + d8 + 4) = O1;
-      if (d8 == 0) a.ws_ml[pr] = make_float2(M, L);
-    }
-  };
-  if (a.R <= RC1) {
+  int ns, sstride, rc;
+  if (kOneLevelOk && a.R <= RC1) {
     deposit(ebuf + wave * kState1, RC1);
-    __syncthreads();
-    combine_store(std::integral_constant<int, NWAVE>{}, kState1, RC1);
+    ns = NWAVE;
+    sstride = kState1;
+    rc = RC1;
   } else {
     __syncthreads();
     if (wave >= NSTATE) deposit(ebuf + (wave - NSTATE) * kState2, RP);
@@ -938,11 +857,14 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     }
     __syncthreads();
     if (wave < NSTATE) deposit(ebuf + wave * kState2, RP);
-    __syncthreads();
-    combine_store(std::integral_constant<int, NSTATE>{}, kState2, RP);
+    ns = NSTATE;
+    sstride = kState2;
+    rc = RP;
   }
-  if (lane == 0) *hint = first;
-  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
+  __syncthreads();
+  if (tid == 0) HW_STAMP(11);
+  emit_unit<NTHR, D>(a, pl, g, u, ebuf, ns, sstride, rc);
+  if (lane == 0) HW_STAMP(16 + wave);
 }
 
 // ------------------------------------------------------------- VALU kernel
@@ -964,6 +886,7 @@ template <>
 struct ValuTraits<float> {
   static constexpr int EPC = 4;  // elements per 16-byte chunk
   __device__ static float elem(const u32x4& c, int e) { return __uint_as_float(c[e]); }
+  __device__ static float load(const float* p) { return *p; }
 };
 template <>
 struct ValuTraits<uint16_t> {
@@ -972,44 +895,27 @@ struct ValuTraits<uint16_t> {
     const uint32_t w = c[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
   }
+  __device__ static float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 };
 
-// max / sum over the 32 lanes of each half of the wave (every lane gets it)
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float half_max(float x) {
-  x = fmaxf(x, dpp_mov<0xb1>(x));   // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_mov<0x4e>(x));   // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
-  x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
-  return max_x16(x);
-}
-__device__ __forceinline__ float half_sum(float x) {
-  x += dpp_mov<0xb1>(x);
-  x += dpp_mov<0x4e>(x);
-  x += dpp_mov<0x141>(x);
-  x += dpp_mov<0x140>(x);
-  return sum_x16(x);
-}
-
 template <typename T, int D, int RG>
-__global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void run_valu(RunArgs a) {
   constexpr int NTHR = kThreads, NWAVE = kWaves;
   constexpr int EPC = ValuTraits<T>::EPC;
   constexpr int KC = D / EPC;     // key chunks per token
   constexpr int DPL = D / 64;     // output dims per lane
   constexpr int RM = 2 * RG;      // rows held
+  constexpr int HALF = D / 2;
   constexpr int PS = 36;          // P row stride (floats), keeps float4 reads aligned
   constexpr int kPWave = RM * PS + RM;  // one wave's P and rescale factors
   constexpr int ACC_STRIDE = D + 4;
   constexpr int kState = RM * ACC_STRIDE + 2 * RM;
   constexpr int kQBlock = RM * D;      // rotated queries of one block (floats)
   constexpr int kQfFloats = 40960 / 4;  // 40 KB of rotated queries per group
-  constexpr int kQfBlocks = kQfFloats / kQBlock > 0 ? kQfFloats / kQBlock : 1;
-  constexpr int kUnion = cmax(kQfBlocks * kQBlock, 2 * kState);
-  __shared__ Plan plan;
+  constexpr int kQf = kQfFloats / kQBlock > 0 ? kQfFloats / kQBlock : 1;
+  constexpr int kUnion = cmax(kQf * kQBlock, 2 * kState);
+  __shared__ PlanLds pl;
+  __shared__ double invf[HALF];
   __shared__ __attribute__((aligned(16))) float qs[RM * D];  // raw query rows
   // rotated queries during the loop; the waves' softmax states at the end
   __shared__ __attribute__((aligned(16))) float ubuf[kUnion];
@@ -1018,41 +924,45 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int tl = lane & 31, rg = lane >> 5;
+  int g, u;
+  head_unit(a, &g, &u);
+  int lo, hi, b_first, b_last;
   {
-    int h0, u0;
-    plan_head_unit(a, &h0, &u0);
     constexpr int kQVec = RM * D / 4;  // float4 of staged query
     constexpr int kQRegs = (kQVec + NTHR - 1) / NTHR;
+    const PlanLoads pload = issue_plan_loads<NTHR>(a, u);
+    double w = 0.0;
+    if (tid < HALF)
+      w = reinterpret_cast<const double*>(reinterpret_cast<const char*>(&a) +
+                                          offsetof(RunArgs, inv_freq))[tid];
     float4 qv[kQRegs];
     const T* qg = static_cast<const T*>(a.q);
-    auto issue = [&] {
 #pragma unroll
-      for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * NTHR;
-        const int r = (4 * x) / D, d = 4 * x - r * D;
-        qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (x < kQVec && r < a.R) {
-          const int w = fast_div(r, a.mG), h = h0 * a.G + (r - w * a.G);
-          const T* src = qg + (static_cast<int64_t>(w) * a.Hq + h) * D + d;
-          qv[k] = make_float4(load_elem(src, 0), load_elem(src, 1), load_elem(src, 2),
-                              load_elem(src, 3));
-        }
+    for (int k = 0; k < kQRegs; ++k) {
+      const int x = tid + k * NTHR;
+      const int r = (4 * x) / D, d = 4 * x - r * D;
+      qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (x < kQVec && r < a.R) {
+        const T* src = qg + out_row(a, g, r) * D + d;
+        qv[k] = make_float4(ValuTraits<T>::load(src), ValuTraits<T>::load(src + 1),
+                            ValuTraits<T>::load(src + 2), ValuTraits<T>::load(src + 3));
       }
-    };
-    auto commit = [&] {
+    }
+    commit_plan_loads<NTHR>(a, pl, pload);
+    if (tid < HALF) invf[tid] = w;
 #pragma unroll
-      for (int k = 0; k < kQRegs; ++k) {
-        const int x = tid + k * NTHR;
-        if (x < kQVec) *reinterpret_cast<float4*>(qs + 4 * x) = qv[k];
-      }
-    };
-    build_plan<NTHR>(a, plan, issue, commit);
+    for (int k = 0; k < kQRegs; ++k) {
+      const int x = tid + k * NTHR;
+      if (x < kQVec) *reinterpret_cast<float4*>(qs + 4 * x) = qv[k];
+    }
+    __syncthreads();
+    (void)unit_range<D, static_cast<int>(sizeof(T))>(a, pl, pload, &lo, &hi);
   }
-  const int g = plan.head;
+  block_range(pl, lo, hi, &b_first, &b_last);
   const __amdgpu_buffer_rsrc_t krs =
-      plane_rsrc(static_cast<const T*>(a.k) + static_cast<int64_t>(g) * a.plane_elems, a.plane_bytes);
+      make_rsrc(static_cast<const T*>(a.k) + static_cast<int64_t>(g) * a.plane_elems, a.plane_bytes);
   const __amdgpu_buffer_rsrc_t vrs =
-      plane_rsrc(static_cast<const T*>(a.v) + static_cast<int64_t>(g) * a.plane_elems, a.plane_bytes);
+      make_rsrc(static_cast<const T*>(a.v) + static_cast<int64_t>(g) * a.plane_elems, a.plane_bytes);
   float* pbuf = pbuf_all + wave * kPWave;
 
   float acc[RM][DPL];
@@ -1067,23 +977,22 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
 #pragma unroll
     for (int dd = 0; dd < DPL; ++dd) acc[r][dd] = 0.f;
 
-  // (a2) rotated, scaled queries of blocks gb..ge-1: qr[(b-gb)*RM*D + r*D + d]
+  // (a2) rotated, scaled queries of visible blocks gb..ge-1:
+  // ubuf[(b-gb)*RM*D + r*D + d]; rows that see nothing of a block are zero
   auto rotate_blocks = [&](int gb, int ge) {
-    const int half = D / 2;
-    const int items = (ge - gb) * RM * half;
+    const int items = (ge - gb) * RM * HALF;
     for (int x = tid; x < items; x += NTHR) {
-      const int i = x % half;
-      const int r = (x / half) % RM;
-      const int bi = x / (half * RM);
-      const int b = gb + bi;
-      const int w = plan.row_w[r];
-      const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
+      const int i = x % HALF;
+      const int r = (x / HALF) % RM;
+      const int bi = x / (HALF * RM);
+      int re = -1;
+      if (r < a.R) re = rows_lds[(gb + bi) * a.qrows + fast_div(r, a.mG)];
       float c = 0.f, s = 0.f;
-      if (vis) rope_cos_sin(plan.iq[w] - plan.row_lag[r] - plan.off[w * a.NB + b], plan.invf[i], &c, &s);
-      const float x0 = qs[r * D + i], x1 = qs[r * D + i + half];
+      if (re >= 0) rope_cos_sin(re, invf[i], &c, &s);
+      const float x0 = qs[r * D + i], x1 = qs[r * D + i + HALF];
       float* dst = ubuf + bi * kQBlock + r * D;
-      dst[i] = vis ? (x0 * c - x1 * s) * a.qscale : 0.f;
-      dst[i + half] = vis ? (x1 * c + x0 * s) * a.qscale : 0.f;
+      dst[i] = re >= 0 ? (x0 * c - x1 * s) * a.qscale : 0.f;
+      dst[i + HALF] = re >= 0 ? (x1 * c + x0 * s) * a.qscale : 0.f;
     }
   };
 
@@ -1112,14 +1021,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
         }
   };
 
-  // last local position of block b that row rg*RG+i may see (-1: none)
+  // last local position of visible block b that row rg*RG+i may see (-1: none)
   auto row_ends = [&](int b, int (&rowend)[RG]) {
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       const int r = rg * RG + i;
-      const int w = plan.row_w[r];
-      const bool vis = r < a.R && ((plan.vis[b] >> w) & 1u);
-      rowend[i] = vis ? static_cast<int>(plan.iq[w] - plan.row_lag[r] - plan.off[w * a.NB + b]) : -1;
+      rowend[i] = r < a.R ? rows_lds[b * a.qrows + fast_div(r, a.mG)] : -1;
     }
   };
   auto compute = [&](const u32x4 (&kc)[KC], const u32x4 (&vc)[DPL][4][VC], const float* qblk,
@@ -1198,22 +1105,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
     }
   };
 
-  if (plan.lo < plan.hi) {
-    const int bq = kQfBlocks;
-    const int b_first = plan.b_first;
-    const int b_last = plan.b_last;
-    for (int gb = b_first; gb <= b_last; gb += bq) {
-      const int ge = min(gb + bq, b_last + 1);
-      const int t_lo = max(plan.lo, plan.tile0[gb]);
-      const int t_hi = min(plan.hi, plan.tile0[ge]);
+  int done_tiles = 0;  // tiles this wave processed
+  if (lo < hi) {
+    for (int gb = b_first; gb <= b_last; gb += kQf) {
+      const int ge = min(gb + kQf, b_last + 1);
+      const int t_lo = max(lo, pl.w[kPlanVbTile0 + gb]);
+      const int t_hi = min(hi, pl.w[kPlanVbTile0 + ge]);
       int j = t_lo + wave;
       int bcur = gb;
-      TileRef rt = {0, 0, 0, 0};
+      TileRef rt = {0, 0, 0, 0u};
       u32x4 kc[KC], vc[DPL][4][VC];
       if (j < t_hi) {
-        rt = tile_ref<D>(plan, a.NB, j, bcur);
-        const uint32_t tile =
-            __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rt.base * sizeof(T)));
+        rt = tile_ref<D, static_cast<int>(sizeof(T))>(pl, j, bcur);
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(rt.byte);
         load_k(tile, kc);
         load_v(tile, vc);
       }
@@ -1226,13 +1130,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
           int rowend[RG];
           row_ends(rt.b, rowend);
           const int jn = j + NWAVE;
+          ++done_tiles;
           if (jn >= t_hi) {
             compute(kc, vc, qblk, rowend, rt.valid, rt.first);
             break;
           }
-          const TileRef rn = tile_ref<D>(plan, a.NB, jn, bcur);
-          const uint32_t tn =
-              __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(rn.base * sizeof(T)));
+          const TileRef rn = tile_ref<D, static_cast<int>(sizeof(T))>(pl, jn, bcur);
+          const uint32_t tn = __builtin_amdgcn_readfirstlane(rn.byte);
           compute(kc, vc, qblk, rowend, rt.valid, rt.first);
           load_k(tn, kc);
           load_v(tn, vc);
@@ -1243,7 +1147,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
     }
   }
 
-  // ---- combine the waves' states (two at a time) and store the partial
+  // ---- combine the waves' states (two at a time) into the unit's partial
   // state of row r: acc on every lane (dims), (m, l) on the row group's lanes
   auto deposit = [&](float* buf) {
 #pragma unroll
@@ -1263,6 +1167,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       }
     }
   };
+  if (lane == 0) atomicAdd(&pl.tiles, done_tiles);
   __syncthreads();  // every wave is done with the queries and its P buffer
   if (wave >= 2) deposit(ubuf + (wave - 2) * kState);
   __syncthreads();
@@ -1273,16 +1178,16 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
     for (int r = 0; r < RM; ++r) {
       if (r >= a.R) continue;  // (uniform; keeps the trip count constant)
       // own (m, l) of row r: held by the lanes of row group r / RG
-      float mo = -INFINITY, lo = 0.f;
+      float mo = -INFINITY, lo2 = 0.f;
 #pragma unroll
       for (int k = 0; k < RG; ++k)
         if (k == r % RG) {
           mo = m_run[k];
-          lo = l_run[k];
+          lo2 = l_run[k];
         }
       // lanes of the other half hold another row: take row r's from lane (r/RG)*32
       mo = __shfl(mo, (r / RG) * 32);
-      lo = __shfl(lo, (r / RG) * 32);
+      lo2 = __shfl(lo2, (r / RG) * 32);
       const float m2 = src[RM * ACC_STRIDE + r];
       const float l2 = src[RM * ACC_STRIDE + RM + r];
       const float M = fmaxf(mo, m2);
@@ -1292,7 +1197,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
       for (int dd = 0; dd < DPL; ++dd)
         acc[r][dd] = acc[r][dd] * s1 + src[r * ACC_STRIDE + DPL * lane + dd] * s2;
       // the merged (m, l) go back to the row group's registers
-      const float lm = lo * s1 + l2 * s2;
+      const float lm = lo2 * s1 + l2 * s2;
 #pragma unroll
       for (int k = 0; k < RG; ++k)
         if (k == r % RG && rg == r / RG) {
@@ -1304,32 +1209,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
   __syncthreads();
   if (wave < 2) deposit(ubuf + wave * kState);
   __syncthreads();
-  const int64_t pu = partial_index(a, plan);
-  for (int x = tid; x < a.R * (D / 4); x += NTHR) {
-    const int r = x / (D / 4), d4 = 4 * (x - r * (D / 4));
-    const float m0 = ubuf[RM * ACC_STRIDE + r], m1 = ubuf[kState + RM * ACC_STRIDE + r];
-    const float M = fmaxf(m0, m1);
-    float L = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int wv = 0; wv < 2; ++wv) {
-        const float* src = ubuf + wv * kState;
-        const float mw = wv ? m1 : m0;
-        const float sc = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        L += src[RM * ACC_STRIDE + RM + r] * sc;
-        const float4 v = *reinterpret_cast<const float4*>(src + r * ACC_STRIDE + d4);
-        O.x += v.x * sc;
-        O.y += v.y * sc;
-        O.z += v.z * sc;
-        O.w += v.w * sc;
-      }
-    }
-    const int64_t pr = pu + static_cast<int64_t>(r) * a.P;
-    *reinterpret_cast<float4*>(a.ws_acc + pr * D + d4) = O;
-    if (d4 == 0) a.ws_ml[pr] = make_float2(M, L);
-  }
-  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
+  emit_unit<NTHR, D>(a, pl, g, u, ubuf, 2, kState, RM);
 }
 
 // ----------------------------------------------------------- merge kernel
@@ -1339,7 +1219,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeArgs a) {
 // kMergeChunk at a time: lane k of every wave loads unit u0+k's (m, l) and
 // forms its weight, which the lanes read back with readlane while summing
 // their accumulators, so the kernel has neither LDS nor barriers; the
-// running (M, L, sum) is rescaled when a later chunk raises M.
+// running (M, L, sum) is rescaled when a later chunk raises M.  The
+// workgroup of row 0 of each head also checks that the head's units
+// processed every tile of the plan once and resets the head's tile counter.
 constexpr int kMergeChunk = 32;  // units whose loads are in flight together
 
 // Lane k's value of x (the builtin moves 32-bit integers: pass the bits).
@@ -1348,28 +1230,27 @@ __device__ __forceinline__ float readlane_f32(float x, int k) {
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void merge_kernel(RunArgs a) {
   // every scalar argument, requested at entry in one round trip
   asm volatile("" ::"s"(a.ws_ml), "s"(a.ws_acc), "s"(a.out), "s"(a.status), "s"(a.R), "s"(a.P),
                "s"(a.G), "s"(a.Hq), "s"(a.dtype), "s"(a.mR), "s"(a.mG));
   const int tid = threadIdx.x;  // output dim
   const int lane = tid & 63;
+  if (tid == 0) HW_MSTAMP(0);
   const int g = fast_div(blockIdx.x, a.mR);
   const int r = blockIdx.x - g * a.R;
   const int P = a.P;
   // FP8 pools: values are code * scale of the kv head (requested early)
   const float vsc = a.dtype == HW_FP8
-                        ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a.tab) +
-                                                         offsetof(DecodeTables, v_scale))[g]
+                        ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a) +
+                                                         offsetof(RunArgs, v_scale))[g]
                         : 1.f;
   // this (kv head, row)'s partials as buffers over its P units: unit u's
   // accumulators at byte u * D * 4, its (m, l) at byte u * 8.  Units past the
   // last lie outside the buffers, read as zero and get zero weight.
   const int64_t row0 = (static_cast<int64_t>(g) * a.R + r) * P;
-  const __amdgpu_buffer_rsrc_t accrs = __builtin_amdgcn_make_buffer_rsrc(
-      a.ws_acc + row0 * D, static_cast<short>(0), P * D * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t mlrs = __builtin_amdgcn_make_buffer_rsrc(
-      a.ws_ml + row0, static_cast<short>(0), P * 8, 0x00020000);
+  const __amdgpu_buffer_rsrc_t accrs = make_rsrc(a.ws_acc + row0 * D, P * D * 4);
+  const __amdgpu_buffer_rsrc_t mlrs = make_rsrc(a.ws_ml + row0, P * 8);
   float M = -INFINITY, L = 0.f, s = 0.f;
   for (int u0 = 0; u0 < P; u0 += kMergeChunk) {
     const int uk = u0 + (lane & (kMergeChunk - 1));
@@ -1400,94 +1281,136 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
     for (int k = 0; k < kMergeChunk; ++k) s += av[k] * readlane_f32(wk, k);
     M = Mc;
   }
-  const int w = fast_div(r, a.mG), h = g * a.G + (r - w * a.G);
   const float o = L > 0.f ? s / L * vsc : 0.f;
-  a.out[(static_cast<int64_t>(w) * a.Hq + h) * D + tid] = o;
+  a.out[out_row(a, g, r) * D + tid] = o;
   if (tid == 0 && !(L > 0.f)) atomicOr(a.status, HW_DEV_NO_TOKENS);
+  if (a.balance && r == 0 && tid < 64) {
+    // balanced runs: every tile of the head taken exactly once (lane k sums
+    // units k, k + 64, ...), then the head's ticket counter back to zero
+    int n = 0;
+    for (int uu = tid; uu < P; uu += 64) n += a.ws_cnt[g * P + uu];
+    n = static_cast<int>(half_sum(static_cast<float>(n)));  // < 2^24: exact
+    n += __shfl_xor(n, 32);
+    if (tid == 0) {
+      if (n < (1 << 30) && n != a.plan[kHdrTiles]) atomicOr(a.status, HW_DEV_WORKSPACE);
+      __hip_atomic_store(a.sync + static_cast<int64_t>(g) * kSyncStride, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (lane == 0) HW_MSTAMP(1 + (tid >> 6));
 }
 
 template <typename K>
-int occupancy(K kernel, int threads) {
+int occupancy(K kernel, int threads, size_t dyn) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, dyn) != hipSuccess) return 0;
   return n;
 }
+
+// Dynamic LDS of a launch: the plan's row ends.
+size_t rows_bytes(const RunArgs& a) { return static_cast<size_t>(a.NB) * a.qrows * 4; }
 
 }  // namespace
 
 template <typename T, int D>
-hipError_t launch_valu_rows(const DecodeArgs& a, int grid, hipStream_t s) {
+hipError_t launch_valu_rows(const RunArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.Hkv * a.P));
+  const size_t dyn = rows_bytes(a);
   if (a.R <= 8)
-    hipLaunchKernelGGL((decode_valu<T, D, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((run_valu<T, D, 4>), grid, dim3(kThreads), dyn, s, a);
   else if (a.R <= 16)
-    hipLaunchKernelGGL((decode_valu<T, D, 8>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((run_valu<T, D, 8>), grid, dim3(kThreads), dyn, s, a);
   else if (a.R <= 20)
-    hipLaunchKernelGGL((decode_valu<T, D, 10>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((run_valu<T, D, 10>), grid, dim3(kThreads), dyn, s, a);
   else if (a.R <= 32)
-    hipLaunchKernelGGL((decode_valu<T, D, 16>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((run_valu<T, D, 16>), grid, dim3(kThreads), dyn, s, a);
   else
-    hipLaunchKernelGGL((decode_valu<T, D, 32>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((run_valu<T, D, 32>), grid, dim3(kThreads), dyn, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int grid, hipStream_t s) {
-  if ((a.D != 64 && a.D != 128) || a.R > HW_MAX_ROWS || a.dtype == HW_FP8)
+hipError_t launch_run_valu(const RunArgs& a, hipStream_t s) {
+  if ((a.D != 64 && a.D != 128) || a.R > kValuMaxRows || a.dtype == HW_FP8)
     return hipErrorInvalidValue;
   if (a.dtype == HW_F32)
-    return a.D == 128 ? launch_valu_rows<float, 128>(a, grid, s) : launch_valu_rows<float, 64>(a, grid, s);
-  return a.D == 128 ? launch_valu_rows<uint16_t, 128>(a, grid, s)
-                    : launch_valu_rows<uint16_t, 64>(a, grid, s);
+    return a.D == 128 ? launch_valu_rows<float, 128>(a, s) : launch_valu_rows<float, 64>(a, s);
+  return a.D == 128 ? launch_valu_rows<uint16_t, 128>(a, s) : launch_valu_rows<uint16_t, 64>(a, s);
 }
 
-template <typename E>
-hipError_t launch_mfma_elem(const DecodeArgs& a, int grid, hipStream_t s) {
-  if (a.D == 128) {
-    if (a.R <= 16)
-      hipLaunchKernelGGL((decode_mfma<128, 1, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_mfma<128, 2, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
-  } else if (a.D == 64) {
-    if (a.R <= 16)
-      hipLaunchKernelGGL((decode_mfma<64, 1, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_mfma<64, 2, E>), dim3(grid), dim3(kMfmaThreads), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+template <int D, typename E>
+hipError_t launch_mfma_d(const RunArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.Hkv * a.P));
+  const size_t dyn = rows_bytes(a);
+  if (a.R <= 16)
+    hipLaunchKernelGGL((run_mfma<D, 1, E>), grid, dim3(64 * mfma_waves(1)), dyn, s, a);
+  else if (a.R <= 32)
+    hipLaunchKernelGGL((run_mfma<D, 2, E>), grid, dim3(64 * mfma_waves(2)), dyn, s, a);
+  else if (a.R <= 48)
+    hipLaunchKernelGGL((run_mfma<D, 3, E>), grid, dim3(64 * mfma_waves(3)), dyn, s, a);
+  else if (a.R <= 64)
+    hipLaunchKernelGGL((run_mfma<D, 4, E>), grid, dim3(64 * mfma_waves(4)), dyn, s, a);
+  else
+    hipLaunchKernelGGL((run_mfma<D, 5, E>), grid, dim3(64 * mfma_waves(5)), dyn, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int grid, hipStream_t s) {
-  if (a.R > 32) return hipErrorInvalidValue;
-  if (a.dtype == HW_BF16) return launch_mfma_elem<uint16_t>(a, grid, s);
-  if (a.dtype == HW_FP8) return launch_mfma_elem<uint8_t>(a, grid, s);
+hipError_t launch_run_mfma(const RunArgs& a, hipStream_t s) {
+  if (a.R > kMfmaMaxRows) return hipErrorInvalidValue;
+  if (a.D == 128) {
+    if (a.dtype == HW_BF16) return launch_mfma_d<128, uint16_t>(a, s);
+    if (a.dtype == HW_FP8) return launch_mfma_d<128, uint8_t>(a, s);
+  } else if (a.D == 64) {
+    if (a.dtype == HW_BF16) return launch_mfma_d<64, uint16_t>(a, s);
+    if (a.dtype == HW_FP8) return launch_mfma_d<64, uint8_t>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
+// Resident workgroups per CU of the kernel a launch would use (0 on error),
+// with the dynamic LDS of the largest plan (64 blocks, the rows given).
+template <int D, typename E>
+int mfma_occ(int rows) {
+  const size_t dyn = static_cast<size_t>(HW_MAX_BLOCKS) * rows * 4;
+  if (rows <= 16) return occupancy(run_mfma<D, 1, E>, 64 * mfma_waves(1), dyn);
+  if (rows <= 32) return occupancy(run_mfma<D, 2, E>, 64 * mfma_waves(2), dyn);
+  if (rows <= 48) return occupancy(run_mfma<D, 3, E>, 64 * mfma_waves(3), dyn);
+  if (rows <= 64) return occupancy(run_mfma<D, 4, E>, 64 * mfma_waves(4), dyn);
+  return occupancy(run_mfma<D, 5, E>, 64 * mfma_waves(5), dyn);
+}
+template <typename T, int D>
+int valu_occ(int rows) {
+  const size_t dyn = static_cast<size_t>(HW_MAX_BLOCKS) * rows * 4;
+  if (rows <= 8) return occupancy(run_valu<T, D, 4>, kThreads, dyn);
+  if (rows <= 16) return occupancy(run_valu<T, D, 8>, kThreads, dyn);
+  if (rows <= 20) return occupancy(run_valu<T, D, 10>, kThreads, dyn);
+  if (rows <= 32) return occupancy(run_valu<T, D, 16>, kThreads, dyn);
+  return occupancy(run_valu<T, D, 32>, kThreads, dyn);
+}
+
+hipError_t launch_merge(const RunArgs& a, hipStream_t s) {
   if (a.P > kMaxUnits || (a.D != 64 && a.D != 128)) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.Hkv * a.R));
   if (a.D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(a.Hkv * a.R), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, s, a);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(a.Hkv * a.R), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
-// Resident workgroups per CU of the kernel a launch would use (0 on error).
-template <typename E>
-int mfma_blocks_per_cu(int D, int rows) {
-  const int t = kMfmaThreads;
-  if (D == 128)
-    return rows <= 16 ? occupancy(decode_mfma<128, 1, E>, t) : occupancy(decode_mfma<128, 2, E>, t);
-  return rows <= 16 ? occupancy(decode_mfma<64, 1, E>, t) : occupancy(decode_mfma<64, 2, E>, t);
-}
-
-int decode_blocks_per_cu(int path, int dtype, int D, int rows) {
-  if (path == 2)
-    return dtype == HW_FP8 ? mfma_blocks_per_cu<uint8_t>(D, rows)
-                           : mfma_blocks_per_cu<uint16_t>(D, rows);
-  return dtype == HW_F32 ? occupancy(decode_valu<float, 128, 10>, kThreads)
-                         : occupancy(decode_valu<uint16_t, 128, 10>, kThreads);
+int run_blocks_per_cu(int path, int dtype, int D, int rows) {
+  if (path == 2) {
+    if (D == 128) return dtype == HW_FP8 ? mfma_occ<128, uint8_t>(rows) : mfma_occ<128, uint16_t>(rows);
+    return dtype == HW_FP8 ? mfma_occ<64, uint8_t>(rows) : mfma_occ<64, uint16_t>(rows);
+  }
+  if (D == 128) return dtype == HW_F32 ? valu_occ<float, 128>(rows) : valu_occ<uint16_t, 128>(rows);
+  return dtype == HW_F32 ? valu_occ<float, 64>(rows) : valu_occ<uint16_t, 64>(rows);
 }
 
 }  // namespace hw
+
+#ifdef HW_STAMPS
+extern "C" int hw_debug_stamps(uint64_t* host, size_t n) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(hw::g_stamps), n * sizeof(uint64_t), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 1;
+}
+#endif

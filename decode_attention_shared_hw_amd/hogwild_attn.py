@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libhogwild_attn.so")
 
 HW_OK, HW_EINVAL, HW_ERANGE, HW_ECAPACITY, HW_EUNSUPPORTED, HW_EWORKSPACE, HW_EHIP = range(7)
 HW_DEV_BAD_ENTRY, HW_DEV_BAD_LENGTH, HW_DEV_NO_TOKENS, HW_DEV_APPEND_OVERFLOW = 1, 2, 4, 8
-HW_DEV_WRITE_OVERFLOW = 16
+HW_DEV_WRITE_OVERFLOW, HW_DEV_STALE_PLAN, HW_DEV_WORKSPACE = 16, 32, 64
 HW_F32, HW_BF16, HW_FP8 = 0, 1, 2
 HW_TILE_TOKENS = 32
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
@@ -65,7 +65,8 @@ def query_dtype(pool_dtype: torch.dtype) -> torch.dtype:
 
 
 EXPORTED = [
-    "hw_abi_version", "hw_status_str", "hw_attn_workspace_bytes", "hw_attn_decode", "hw_attn_chunk",
+    "hw_abi_version", "hw_status_str", "hw_attn_plan_bytes", "hw_attn_plan", "hw_attn_run",
+    "hw_attn_workspace_bytes", "hw_attn_decode", "hw_attn_chunk",
     "hw_block_append", "hw_block_reset", "hw_block_advance", "hw_block_write",
     "hw_build_combined_tables", "hw_build_view_tables", "hw_pool_status", "hw_set_tuning",
 ]
@@ -87,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.hw_abi_version.argtypes = []
         L.hw_status_str.restype = ctypes.c_char_p
         L.hw_status_str.argtypes = [i32]
+        L.hw_attn_plan_bytes.restype = sz
+        L.hw_attn_plan_bytes.argtypes = [PP, i32, i32, i32]
+        L.hw_attn_plan.restype = i32
+        L.hw_attn_plan.argtypes = [PP, i32, i32, i32, P, i32, P, P, sz, P]
+        L.hw_attn_run.restype = i32
+        L.hw_attn_run.argtypes = [PP, i32, P, i32, i32, i32, P, sz, d, P, P, sz, P]
         L.hw_attn_workspace_bytes.restype = sz
         L.hw_attn_workspace_bytes.argtypes = [PP, i32, i32]
         L.hw_attn_decode.restype = i32
@@ -106,9 +113,9 @@ def lib() -> ctypes.CDLL:
         L.hw_build_view_tables.restype = i32
         L.hw_build_view_tables.argtypes = [PP, i32, i32, i32, P, P, P, P]
         L.hw_pool_status.restype = i32
-        L.hw_pool_status.argtypes = [PP, P, i32]
+        L.hw_pool_status.argtypes = [PP, P, i32, P]
         L.hw_set_tuning.restype = i32
-        L.hw_set_tuning.argtypes = [i32, i32]
+        L.hw_set_tuning.argtypes = [i32, i32, i32]
         _lib = L
     return _lib
 
@@ -224,8 +231,51 @@ def hw_status_str(code: int) -> str:
     return lib().hw_status_str(int(code)).decode()
 
 
-def hw_set_tuning(path: int = PATH_AUTO, units_per_head: int = 0):
-    _check(lib().hw_set_tuning(int(path), int(units_per_head)), "hw_set_tuning")
+def hw_set_tuning(path: int = PATH_AUTO, units_per_head: int = 0, balance: int = 0):
+    _check(lib().hw_set_tuning(int(path), int(units_per_head), int(balance)), "hw_set_tuning")
+
+
+def _expect(t, name, dtype, shape, device):
+    """Raise ValueError unless `t` is a contiguous tensor of `dtype` and `shape` on `device`
+    (the library sees bare pointers and cannot check sizes itself)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the pool is on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _expect_bytes(t, name, nbytes, device):
+    """A contiguous device byte buffer of at least `nbytes`."""
+    if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor on {device}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _check_views(pool, tables, num_entries, W):
+    dev = pool.k.device
+    if not isinstance(tables, torch.Tensor) or tables.dim() != 3 or tables.shape[2] != 2:
+        raise ValueError("tables: expected int32 [W][E][2]")
+    _expect(tables, "tables", torch.int32, (W, tables.shape[1], 2), dev)
+    _expect(num_entries, "num_entries", torch.int32, (W,), dev)
+
+
+def hw_attn_plan_bytes(pool: Pool, num_workers: int, chunk: int, num_q_heads: int) -> int:
+    return int(lib().hw_attn_plan_bytes(ctypes.byref(pool.desc), num_workers, chunk, num_q_heads))
+
+
+def alloc_plan(pool: Pool, num_workers: int, num_q_heads: int, chunk: int = 1) -> torch.Tensor:
+    """Device buffer for hw_attn_plan (int32 words)."""
+    n = hw_attn_plan_bytes(pool, num_workers, chunk, num_q_heads)
+    if n == 0:
+        raise HWError(HW_EINVAL, "hw_attn_plan_bytes")
+    return torch.empty((n + 3) // 4, dtype=torch.int32, device=pool.k.device)
 
 
 def hw_attn_workspace_bytes(pool: Pool, num_workers: int, num_q_heads: int) -> int:
@@ -233,11 +283,47 @@ def hw_attn_workspace_bytes(pool: Pool, num_workers: int, num_q_heads: int) -> i
 
 
 def alloc_workspace(pool: Pool, num_workers: int, num_q_heads: int) -> torch.Tensor:
-    """Device workspace for hw_attn_decode (needs no initialisation)."""
+    """Device workspace for hw_attn_decode / hw_attn_chunk / hw_attn_run (zeroed: its merge
+    counters must start at zero; every call leaves them zero)."""
     n = hw_attn_workspace_bytes(pool, num_workers, num_q_heads)
     if n == 0:
         raise HWError(HW_EINVAL, "hw_attn_workspace_bytes")
-    return torch.empty(n, dtype=torch.uint8, device=pool.k.device)
+    return torch.zeros(n, dtype=torch.uint8, device=pool.k.device)
+
+
+def hw_attn_plan(pool: Pool, tables: torch.Tensor, num_entries: torch.Tensor, plan: torch.Tensor,
+                 num_q_heads: int, chunk: int = 1, stream=None):
+    """Plan of the decode (chunk = 1) or chunk calls over these views: tables int32 [W][E][2],
+    num_entries int32 [W], plan from alloc_plan."""
+    W = int(num_entries.shape[0]) if isinstance(num_entries, torch.Tensor) else 0
+    _check_views(pool, tables, num_entries, W)
+    nb = hw_attn_plan_bytes(pool, W, chunk, num_q_heads)
+    _expect_bytes(plan, "plan", nb, pool.k.device)
+    code = lib().hw_attn_plan(ctypes.byref(pool.desc), W, int(chunk), int(num_q_heads),
+                              _ptr(tables), int(tables.shape[1]), _ptr(num_entries), _ptr(plan),
+                              plan.numel() * plan.element_size(), _stream(stream))
+    _check(code, "hw_attn_plan")
+
+
+def hw_attn_run(pool: Pool, layer: int, q: torch.Tensor, plan: torch.Tensor, rope_theta: float,
+                out: torch.Tensor, workspace: torch.Tensor, stream=None):
+    """One layer from a plan.  q [W][Hq][D] (decode) or [W][n][Hq][D] (chunk),
+    query_dtype(pool.dtype); out fp32 of the same shape."""
+    dev = pool.k.device
+    if not isinstance(q, torch.Tensor) or q.dim() not in (3, 4):
+        raise ValueError("q: expected [W][Hq][D] or [W][n][Hq][D]")
+    W, n = int(q.shape[0]), (int(q.shape[1]) if q.dim() == 4 else 1)
+    Hq = int(q.shape[-2])
+    shape = (W, Hq, pool.head_dim) if q.dim() == 3 else (W, n, Hq, pool.head_dim)
+    _expect(q, "q", query_dtype(pool.dtype), shape, dev)
+    _expect(out, "out", torch.float32, shape, dev)
+    _expect_bytes(plan, "plan", hw_attn_plan_bytes(pool, W, n, Hq), dev)
+    _expect_bytes(workspace, "workspace", hw_attn_workspace_bytes(pool, W * n, Hq), dev)
+    code = lib().hw_attn_run(ctypes.byref(pool.desc), int(layer), _ptr(q), W, n, Hq, _ptr(plan),
+                             plan.numel() * plan.element_size(), float(rope_theta), _ptr(out),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _check(code, "hw_attn_run")
 
 
 def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
@@ -245,10 +331,18 @@ def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor
                    workspace: torch.Tensor, stream=None):
     """q [W][Hq][D] (query_dtype(pool.dtype)), tables int32 [W][E][2], num_entries int32 [W],
     out fp32 [W][Hq][D]."""
+    dev = pool.k.device
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q: expected [W][Hq][D]")
     W, Hq, _ = q.shape
+    _expect(q, "q", query_dtype(pool.dtype), (W, Hq, pool.head_dim), dev)
+    _expect(out, "out", torch.float32, (W, Hq, pool.head_dim), dev)
+    _check_views(pool, tables, num_entries, W)
+    _expect_bytes(workspace, "workspace", hw_attn_workspace_bytes(pool, W, Hq), dev)
     code = lib().hw_attn_decode(ctypes.byref(pool.desc), int(layer), _ptr(q), W, Hq, _ptr(tables),
                                 int(tables.shape[1]), _ptr(num_entries), float(rope_theta),
-                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+                                _ptr(out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "hw_attn_decode")
 
 
@@ -257,11 +351,18 @@ def hw_attn_chunk(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
                   workspace: torch.Tensor, stream=None):
     """q [W][n][Hq][D] (query_dtype(pool.dtype)): each worker's last n tokens as queries, causal over the
     view; out fp32 [W][n][Hq][D]; workspace sized for W * n workers."""
+    dev = pool.k.device
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q: expected [W][n][Hq][D]")
     W, n, Hq, _ = q.shape
+    _expect(q, "q", query_dtype(pool.dtype), (W, n, Hq, pool.head_dim), dev)
+    _expect(out, "out", torch.float32, (W, n, Hq, pool.head_dim), dev)
+    _check_views(pool, tables, num_entries, W)
+    _expect_bytes(workspace, "workspace", hw_attn_workspace_bytes(pool, W * n, Hq), dev)
     code = lib().hw_attn_chunk(ctypes.byref(pool.desc), int(layer), _ptr(q), W, n, Hq,
                                _ptr(tables), int(tables.shape[1]), _ptr(num_entries),
-                               float(rope_theta), _ptr(out), _ptr(workspace), workspace.numel(),
-                               _stream(stream))
+                               float(rope_theta), _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "hw_attn_chunk")
 
 
@@ -292,6 +393,9 @@ def hw_block_write(pool: Pool, layer: int, blocks, k_new: torch.Tensor, v_new: t
     """Store each listed block's new token of `layer` in slot block_len - 1.
     k_new, v_new: device fp32 [len(blocks)][num_kv_heads][head_dim]."""
     n, p, keep = _blocks(blocks)
+    shape = (n, pool.num_kv_heads, pool.head_dim)
+    _expect(k_new, "k_new", torch.float32, shape, pool.k.device)
+    _expect(v_new, "v_new", torch.float32, shape, pool.k.device)
     _check(lib().hw_block_write(ctypes.byref(pool.desc), int(layer), n, p, _ptr(k_new),
                                 _ptr(v_new), float(rope_theta), _stream(stream)),
            "hw_block_write")
@@ -300,6 +404,8 @@ def hw_block_write(pool: Pool, layer: int, blocks, k_new: torch.Tensor, v_new: t
 def hw_build_combined_tables(pool: Pool, num_workers: int, common_block: int, worker_block,
                              tables: torch.Tensor, num_entries: torch.Tensor, stream=None):
     """tables: device int32 [W][W+1][2]; num_entries: device int32 [W]."""
+    _expect(tables, "tables", torch.int32, (num_workers, num_workers + 1, 2), pool.k.device)
+    _expect(num_entries, "num_entries", torch.int32, (num_workers,), pool.k.device)
     wb = (ctypes.c_int32 * num_workers)(*[int(b) for b in worker_block])
     _check(lib().hw_build_combined_tables(ctypes.byref(pool.desc), int(num_workers),
                                           int(common_block), ctypes.cast(wb, ctypes.c_void_p),
@@ -311,6 +417,8 @@ def hw_build_view_tables(pool: Pool, layout: int, num_workers: int, common_block
                          worker_block, tables: torch.Tensor, num_entries: torch.Tensor,
                          stream=None):
     """View tables of one of the HW_LAYOUT_* layouts; shapes as hw_build_combined_tables."""
+    _expect(tables, "tables", torch.int32, (num_workers, num_workers + 1, 2), pool.k.device)
+    _expect(num_entries, "num_entries", torch.int32, (num_workers,), pool.k.device)
     wb = (ctypes.c_int32 * num_workers)(*[int(b) for b in worker_block])
     _check(lib().hw_build_view_tables(ctypes.byref(pool.desc), int(layout), int(num_workers),
                                       int(common_block), ctypes.cast(wb, ctypes.c_void_p),
@@ -318,8 +426,9 @@ def hw_build_view_tables(pool: Pool, layout: int, num_workers: int, common_block
            "hw_build_view_tables")
 
 
-def hw_pool_status(pool: Pool, clear: bool = False) -> int:
+def hw_pool_status(pool: Pool, clear: bool = False, stream=None) -> int:
+    """The pool's sticky HW_DEV_* bits once `stream`'s work so far is done (synchronizes it)."""
     flags = ctypes.c_int32(0)
-    _check(lib().hw_pool_status(ctypes.byref(pool.desc), ctypes.byref(flags), int(bool(clear))),
-           "hw_pool_status")
+    _check(lib().hw_pool_status(ctypes.byref(pool.desc), ctypes.byref(flags), int(bool(clear)),
+                                _stream(stream)), "hw_pool_status")
     return int(flags.value)

@@ -31,9 +31,10 @@
  *
  * Memory: every pointer marked (device) is device memory on the current HIP
  * device; (host) is host memory read during the call.  The caller owns every
- * buffer.  No call allocates, frees or synchronizes, except hw_pool_status().
- * All device work is enqueued on `stream` (a hipStream_t; NULL = default
- * stream) and calls return after enqueueing.
+ * buffer.  q, out, plans and workspaces are 16-byte aligned (HW_EINVAL
+ * otherwise).  No call allocates, frees or synchronizes, except hw_pool_status()
+ * (which synchronizes its stream).  All device work is enqueued on `stream`
+ * (a hipStream_t; NULL = default stream) and calls return after enqueueing.
  *
  * Errors: problems visible on the host are reported by the return code and
  * then nothing is enqueued.  Problems only visible on the device (lengths
@@ -52,13 +53,14 @@
 extern "C" {
 #endif
 
-#define HW_ABI_VERSION 2
+#define HW_ABI_VERSION 3
 
 /* Tokens per tile of the pool layout; block starts and capacities are multiples of it. */
 #define HW_TILE_TOKENS 32
 #define HW_MAX_BLOCKS 64   /* blocks per pool                          */
 #define HW_MAX_WORKERS 32  /* workers per decode call                  */
-#define HW_MAX_ROWS 64     /* num_workers * (num_q_heads / num_kv_heads) */
+#define HW_MAX_ROWS 80     /* num_workers * chunk * (num_q_heads / num_kv_heads);
+                              64 for fp32 pools and the VALU path      */
 #define HW_MAX_ENTRIES 64  /* entries per worker table                 */
 #define HW_MAX_FP8_KV_HEADS 64 /* kv heads of an HW_FP8 pool             */
 
@@ -66,17 +68,23 @@ typedef int32_t hw_status;
 #define HW_OK 0
 #define HW_EINVAL 1        /* null pointer, bad shape, bad id, src == dst      */
 #define HW_ERANGE 2        /* a value outside the supported limits above       */
-#define HW_ECAPACITY 3     /* append cannot fit by the host-known capacities   */
-#define HW_EUNSUPPORTED 4  /* dtype / head_dim combination not built           */
-#define HW_EWORKSPACE 5    /* workspace missing or smaller than required       */
+#define HW_ECAPACITY 3     /* (reserved; capacities are checked on the device) */
+#define HW_EUNSUPPORTED 4  /* dtype / head_dim / path combination not built    */
+#define HW_EWORKSPACE 5    /* workspace or plan missing or smaller than required */
 #define HW_EHIP 6          /* a HIP runtime call failed                        */
 
 /* Device-detected conditions (sticky bits of the pool status word). */
-#define HW_DEV_BAD_ENTRY 1       /* table entry with block id out of range, or a block listed twice */
+#define HW_DEV_BAD_ENTRY 1       /* table entry with block id out of range, a block listed twice,
+                                    or a view whose positions i_q - view_offset reach 2^31  */
 #define HW_DEV_BAD_LENGTH 2      /* block_len < 0 or > capacity                                      */
 #define HW_DEV_NO_TOKENS 4       /* a worker sees no token; its rows are written as zeros            */
 #define HW_DEV_APPEND_OVERFLOW 8 /* len_dst + len_src > cap_dst at run time; nothing was moved        */
 #define HW_DEV_WRITE_OVERFLOW 16 /* advance past a block's capacity, or a token write into an empty block */
+#define HW_DEV_STALE_PLAN 32     /* hw_attn_run: the plan was made for another call shape or pool
+                                    (its units are skipped and their rows written as zeros), or a
+                                    block length changed since the plan was made                   */
+#define HW_DEV_WORKSPACE 64      /* a run's work units did not cover every tile exactly once: the
+                                    workspace's counters were not zero when the call started       */
 
 /* Storage types. */
 #define HW_F32 0
@@ -118,14 +126,14 @@ typedef struct {
  * an FP8 fragment is 8 bytes).
  *
  * block_len is device memory and is changed by hw_block_append /
- * hw_block_reset; block_start and block_cap are host arrays and fixed for the
- * pool's lifetime.  status is a device int32 holding the sticky HW_DEV_* bits;
- * the caller zeroes it once.
+ * hw_block_reset / hw_block_advance; block_start and block_cap are host
+ * arrays and fixed for the pool's lifetime.  status is a device int32 holding
+ * the sticky HW_DEV_* bits; the caller zeroes it once.
  */
 typedef struct {
-  int32_t dtype;        /* HW_F32 or HW_BF16                               */
+  int32_t dtype;        /* HW_F32, HW_BF16 or HW_FP8                       */
   int32_t num_layers;   /* >= 1                                            */
-  int32_t num_kv_heads; /* >= 1                                            */
+  int32_t num_kv_heads; /* >= 1 (FP8 pools: <= HW_MAX_FP8_KV_HEADS)       */
   int32_t head_dim;     /* 64 or 128                                       */
   int32_t num_blocks;   /* 1 .. HW_MAX_BLOCKS                              */
   int32_t reserved;     /* must be 0                                       */
@@ -137,7 +145,8 @@ typedef struct {
   const int64_t* block_start; /* (host) [num_blocks], multiples of 32      */
   const int32_t* block_cap;   /* (host) [num_blocks], multiples of 32      */
   /* (host) [num_layers][num_kv_heads] positive finite scales of an HW_FP8
-   * pool (key and value); NULL for the other types.  Read at each call. */
+   * pool (key and value); NULL for the other types.  A call reads the
+   * scales of the layer it works on. */
   const float* k_scale;
   const float* v_scale;
 } hw_pool;
@@ -149,39 +158,94 @@ int32_t hw_abi_version(void);
 const char* hw_status_str(hw_status status);
 
 /*
- * Bytes of device workspace hw_attn_decode needs for this pool and call
- * shape under the current tuning: split partials for the log-sum-exp merge
- * and per-wave first-tile hints (the tiles the previous call started with,
- * requested before the plan is known and verified against it).  For
- * hw_attn_chunk pass num_workers * chunk.  Returns 0 if the shape is invalid
- * (more than HW_MAX_ROWS stacked rows).  The workspace needs no
- * initialisation, and one workspace serves any sequence of calls on one
- * stream; calls that may overlap need distinct workspaces.
+ * Decode in two parts (key design 1 and 2: within one decode step every
+ * layer sees the same views, so everything that depends on the views and
+ * the block lengths but not on the layer is built once per step):
+ *
+ *   hw_attn_plan   reads the worker tables and the device block lengths and
+ *                  writes a plan: which blocks are visible, how their tiles
+ *                  are split into work units, and for every visible block
+ *                  and query row the row's rotation delta
+ *                  i_q - lag - view_offset.  One small launch.
+ *   hw_attn_run    one layer's attention from a plan: one launch.
+ *
+ * hw_attn_decode / hw_attn_chunk do both on every call.  A plan stays valid
+ * while the tables, entry counts and block lengths it was made from are
+ * unchanged (token writes into already reserved slots do not change them);
+ * a run whose plan does not fit its call, or whose pool's lengths changed,
+ * reports HW_DEV_STALE_PLAN.
  */
-size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t num_q_heads);
+
+/* Bytes of a plan for `num_workers` workers with `chunk` query tokens each
+ * (chunk = 1: decode).  0 if the shape is invalid. */
+size_t hw_attn_plan_bytes(const hw_pool* pool, int32_t num_workers, int32_t chunk,
+                          int32_t num_q_heads);
 
 /*
- * One layer of concurrent-attention decode (key design 1; news 1114328 sec. 3.2).
- *
- *   q            (device) [num_workers][num_q_heads][head_dim], fp32 for fp32
- *                pools, bf16 for bf16 and FP8 pools: the one current query
- *                token of each worker, before RoPE.
  *   tables       (device) [num_workers][max_entries] views; worker w uses its
  *                first num_entries[w] entries.  A block not listed is invisible
  *                to w; a block may be listed at most once per worker.
  *   num_entries  (device) [num_workers].
+ *   plan         (device) >= hw_attn_plan_bytes(...) bytes, written.
+ * Host-checked errors: HW_EINVAL (null pointers, num_q_heads % num_kv_heads,
+ * max_entries < 1), HW_ERANGE (limits above, chunk < 1), HW_EUNSUPPORTED,
+ * HW_EWORKSPACE (plan too small), HW_EHIP (launch failure).  Malformed tables
+ * and lengths set HW_DEV_BAD_ENTRY / HW_DEV_BAD_LENGTH when the plan is built.
+ */
+hw_status hw_attn_plan(const hw_pool* pool, int32_t num_workers, int32_t chunk,
+                       int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
+                       const int32_t* num_entries, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * Bytes of device workspace a call needs for this pool and call shape under
+ * the current tuning and device (for chunks pass num_workers * chunk): the
+ * per-kv-head tile counters, a plan (used by hw_attn_decode / hw_attn_chunk)
+ * and the work units' partial states.  Returns 0 if the shape is invalid.
+ * The first 16 KB (the tile counters) must be zero before the workspace's
+ * first use; every call leaves them zero, so one workspace serves any
+ * sequence of calls on one stream (a call that finds them otherwise reports
+ * HW_DEV_WORKSPACE).  Calls that may overlap need distinct workspaces.
+ */
+size_t hw_attn_workspace_bytes(const hw_pool* pool, int32_t num_workers, int32_t num_q_heads);
+
+/*
+ * One layer of attention from a plan made by hw_attn_plan with the same
+ * pool, num_workers, chunk and num_q_heads.
+ *   q    (device) [num_workers][chunk][num_q_heads][head_dim], fp32 for fp32
+ *        pools, bf16 for bf16 and FP8 pools: the current query tokens of each
+ *        worker, before RoPE.
+ *   out  (device) [num_workers][chunk][num_q_heads][head_dim] fp32.
+ *   workspace (device) >= hw_attn_workspace_bytes(pool, num_workers * chunk,
+ *        num_q_heads) bytes.
+ * For each worker w, query token j and q-head h (kv head g = h / (Hq/Hkv)),
+ * with query j at view position i_q[w] - (chunk - 1 - j):
+ *   out[w][j][h] = sum over entries (b, off) and positions p < len_b with
+ *       off + p <= i_q[w] - (chunk - 1 - j) of
+ *       softmax_p( rho(q[w][j][h], i_q[w] - (chunk - 1 - j) - off) . K_b[g][p] / sqrt(D) ) V_b[g][p]
+ * (chunk = 1: every listed token, no mask).  FP8 pools: K and V are
+ * code * scale of their (layer, kv head); the products run on the bf16
+ * matrix cores with the codes widened exactly.  Rows that see no token are
+ * written as zeros and set HW_DEV_NO_TOKENS.
+ * A call is one launch of work units (split-K over the visible tiles) and,
+ * with several units per kv head, one launch merging their partials.
+ * Host-checked errors: HW_EINVAL (null pointers, num_q_heads % num_kv_heads,
+ * layer out of range, theta), HW_ERANGE (limits above), HW_EUNSUPPORTED
+ * (head_dim; FP8 pools with the VALU path forced; fp32 pools with the MFMA
+ * path forced or more than 64 rows), HW_EWORKSPACE, HW_EHIP.
+ */
+hw_status hw_attn_run(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
+                      int32_t chunk, int32_t num_q_heads, const void* plan, size_t plan_bytes,
+                      double rope_theta, float* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * One layer of concurrent-attention decode (key design 1; news 1114328 sec.
+ * 3.2): hw_attn_plan into the workspace, then hw_attn_run with chunk = 1.
+ *   q            (device) [num_workers][num_q_heads][head_dim].
+ *   tables, num_entries as hw_attn_plan.
  *   out          (device) [num_workers][num_q_heads][head_dim] fp32.
  *   workspace    (device) >= hw_attn_workspace_bytes(pool, W, Hq) bytes.
- *
- * For each worker w and q-head h (kv head g = h / (Hq/Hkv)):
- *   out[w][h] = sum over entries (b, off) and j < len_b of
- *       softmax_j( rho(q[w][h], i_q[w] - off) . K_b[g][j] / sqrt(D) ) V_b[g][j].
- * FP8 pools: K and V are code * scale of their (layer, kv head); the
- * products run on the bf16 matrix cores with the codes widened exactly.
- * Host-checked errors: HW_EINVAL (null pointers, num_q_heads % num_kv_heads,
- * layer out of range, max_entries < 1), HW_ERANGE (limits above),
- * HW_EUNSUPPORTED (head_dim; FP8 pools with more than 32 stacked rows or the
- * VALU path forced), HW_EWORKSPACE, HW_EHIP (launch failure).
+ * Errors as hw_attn_plan and hw_attn_run.
  */
 hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
                          int32_t num_q_heads, const hw_entry* tables, int32_t max_entries,
@@ -191,16 +255,11 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
 /*
  * Multi-token query chunk: every worker attends with its last `chunk` tokens
  * at once (a prompt injected into, or a header prefilled in, its own block,
- * whose K/V are already stored).  Query j of worker w sits at view position
- * i_q[w] - (chunk - 1 - j) and sees the view's tokens at positions up to its
- * own (a causal mask over the view); chunk = 1 is hw_attn_decode.
+ * whose K/V are already stored; key design 2's "\n\n + worker" header, key
+ * design 3's periodic self-check prompt).  hw_attn_plan then hw_attn_run.
  *   q    (device) [num_workers][chunk][num_q_heads][head_dim], dtype as for decode.
  *   out  (device) [num_workers][chunk][num_q_heads][head_dim] fp32.
  *   workspace: hw_attn_workspace_bytes(pool, num_workers * chunk, num_q_heads).
- * Other arguments, errors and limits as hw_attn_decode, with
- * num_workers * chunk * (num_q_heads / num_kv_heads) <= HW_MAX_ROWS
- * (HW_ERANGE otherwise, or for chunk < 1).  Rows that see no token are zero
- * and set HW_DEV_NO_TOKENS.
  */
 hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
                         int32_t chunk, int32_t num_q_heads, const hw_entry* tables,
@@ -217,13 +276,17 @@ hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32
  * block_len[src] = 0.  src data is left in place.  FP8 pools: src and dst
  * share the plane's key scale, so the codes are rotated and rounded to the
  * nearest E4M3 code (saturating at 448).
- * Host-checked: HW_EINVAL (ids, src == dst), HW_ECAPACITY (cap_src > cap_dst
- * is allowed; only the run-time lengths decide, see HW_DEV_APPEND_OVERFLOW).
+ * Host-checked: HW_EINVAL (ids, src == dst, theta).  Capacities are checked
+ * on the device against the run-time lengths (HW_DEV_APPEND_OVERFLOW).
  */
 hw_status hw_block_append(const hw_pool* pool, int32_t src_block, int32_t dst_block,
                           double rope_theta, void* stream);
 
-/* Sets block_len[block] = 0 on the device (a worker starts a new step). */
+/*
+ * Sets block_len[block] = 0 on the device: a worker whose step was moved into
+ * the shared history starts its next step in an empty block (key design 2,
+ * last paragraph).  Host-checked: HW_EINVAL (id).
+ */
 hw_status hw_block_reset(const hw_pool* pool, int32_t block, void* stream);
 
 /*
@@ -288,19 +351,32 @@ hw_status hw_build_view_tables(const hw_pool* pool, int32_t layout, int32_t num_
                                hw_entry* tables, int32_t* num_entries, void* stream);
 
 /*
- * Reads the pool's sticky HW_DEV_* bits into *flags (host).  Synchronizes the
- * device first.  clear != 0 zeroes the word afterwards.
+ * Reads the pool's sticky HW_DEV_* bits into *flags (host) once the work
+ * enqueued on `stream` so far has completed (synchronizes that stream only).
+ * clear != 0 zeroes the word afterwards (on the same stream, completed
+ * before the call returns).
  */
-hw_status hw_pool_status(const hw_pool* pool, int32_t* flags, int32_t clear);
+hw_status hw_pool_status(const hw_pool* pool, int32_t* flags, int32_t clear, void* stream);
 
 /*
  * Process-wide tuning (not thread-safe against concurrent decode calls).
  *   path:           0 auto, 1 VALU fp32 kernel (fp32 and bf16 pools), 2 MFMA
  *                   bf16 kernel (bf16 and FP8 pools).
- *   units_per_head: number of split-K work units per kv head; 0 = automatic.
+ *   units_per_head: number of split-K work units per kv head; 0 = automatic
+ *                   (the device's resident workgroups divided by the kv
+ *                   heads).  Values above what the device holds at once are
+ *                   lowered to it.
+ *   balance:        0 (default): every unit takes a fixed contiguous range
+ *                   of the visible tiles, and results are bitwise the same
+ *                   on every run.  1: each wave takes one tile and then
+ *                   tiles from a per-kv-head counter, so units that HBM
+ *                   serves faster take more tiles (the MFMA path, when
+ *                   every visible block's rotated queries fit in LDS: at
+ *                   most 6 visible blocks); results then vary in the last
+ *                   bits from run to run.
  * Returns HW_EINVAL for values out of range.
  */
-hw_status hw_set_tuning(int32_t path, int32_t units_per_head);
+hw_status hw_set_tuning(int32_t path, int32_t units_per_head, int32_t balance);
 
 #ifdef __cplusplus
 }

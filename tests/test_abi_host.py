@@ -14,6 +14,13 @@ from decode_attention_shared_hw_amd import layout
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+# The descriptors below carry made-up device pointers: every call must be rejected on
+# the host.  Where a GPU is visible a call that slipped through would launch on them, so
+# these checks run only where none is.
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="host-only checks with made-up device pointers")
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(hw.LIB_PATH):
@@ -37,7 +44,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert hw.hw_abi_version() == 2
+    assert hw.hw_abi_version() == 3
     assert hw.hw_status_str(hw.HW_OK) == "ok"
     assert "workspace" in hw.hw_status_str(hw.HW_EWORKSPACE)
 
@@ -82,7 +89,8 @@ def test_decode_host_validation(lib):
     assert decode_rc(lib, ok, layer=1) == hw.HW_EINVAL           # layer out of range
     assert decode_rc(lib, ok, W=0) == hw.HW_ERANGE
     assert decode_rc(lib, ok, W=33) == hw.HW_ERANGE
-    assert decode_rc(lib, ok, W=32, Hq=8) == hw.HW_ERANGE        # rows 128 > 64
+    assert decode_rc(lib, ok, W=32, Hq=8) == hw.HW_ERANGE        # rows 128 > 80
+    assert decode_rc(lib, ok, W=21, Hq=8) == hw.HW_ERANGE        # rows 84 > 80
     assert decode_rc(lib, ok, E=0) == hw.HW_ERANGE
     assert decode_rc(lib, ok, theta=-1.0) == hw.HW_EINVAL
     assert decode_rc(lib, ok, theta=float("nan")) == hw.HW_EINVAL
@@ -92,34 +100,84 @@ def test_decode_host_validation(lib):
     assert decode_rc(lib, FakePool(caps=(64, 32), starts=[0, 32])) == hw.HW_EINVAL  # overlap
     assert decode_rc(lib, FakePool(caps=(64,), slots=32)) == hw.HW_EINVAL    # beyond slots
     assert decode_rc(lib, FakePool(caps=tuple([32] * 65))) == hw.HW_ERANGE   # too many blocks
-    # kv heads x split units must stay below 2^16 workgroups
+    # kv heads x split units must stay below 2^16 workgroups (units are lowered to what the
+    # device holds at once, so only 2^16 kv heads at one unit each reach the bound)
     hw.hw_set_tuning(hw.PATH_AUTO, 256)
     try:
-        big = FakePool(caps=(256 * 32,), Hkv=256)
-        assert decode_rc(lib, big, Hq=256) == hw.HW_ERANGE
+        big = FakePool(caps=(256 * 32,), Hkv=65536)
+        assert decode_rc(lib, big, Hq=65536) == hw.HW_ERANGE
     finally:
         hw.hw_set_tuning(hw.PATH_AUTO, 0)
 
 
 def test_workspace_bytes(lib):
-    pool = FakePool()
+    pool = FakePool(caps=(4096, 32, 32))
     n = lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4)
-    # (m, l) + accumulators for Hkv=2 heads, rows 4, D=128, 128 units per head by default
-    units = 256 // 2
-    assert n >= 2 * units * 4 * (128 + 2) * 4
+    # merge counters (16 KB), a plan, then (m, l) + accumulators for Hkv=2 heads, rows 4,
+    # D=128 and at least 2 units per head (the device's resident workgroups / Hkv)
+    assert n >= 16384 + 2 * 2 * 4 * (128 + 2) * 4
     assert lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 3) == 0
-    hw.hw_set_tuning(hw.PATH_AUTO, 8)
+    hw.hw_set_tuning(hw.PATH_AUTO, 2)
     try:
         assert lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4) < n
+    finally:
+        hw.hw_set_tuning(hw.PATH_AUTO, 0)
+    # at most one unit per tile the blocks can hold
+    small = FakePool(caps=(64, 32, 32))
+    assert lib.hw_attn_workspace_bytes(ctypes.byref(small.desc), 2, 4) <= \
+        16384 + 4 * (600 + 3 * 2) + 2 * 4 * 4 * (128 + 2) * 4 + 512
+    # plans: 600 header words + one row end per (block, query row)
+    assert lib.hw_attn_plan_bytes(ctypes.byref(pool.desc), 2, 1, 4) == 4 * (600 + 3 * 2)
+    assert lib.hw_attn_plan_bytes(ctypes.byref(pool.desc), 2, 5, 4) == 4 * (600 + 3 * 10)
+    assert lib.hw_attn_plan_bytes(ctypes.byref(pool.desc), 2, 1, 3) == 0
+
+
+def test_plan_and_run_host_validation(lib):
+    pool = FakePool()
+    P = ctypes.byref(pool.desc)
+    p = ctypes.c_void_p(0x5000)
+    nb = lib.hw_attn_plan_bytes(P, 2, 1, 4)
+    plan = lambda W=2, n=1, Hq=4, E=3, ptr=p, pb=nb: lib.hw_attn_plan(
+        P, W, n, Hq, ptr, E, ptr, ptr, pb, None)
+    assert plan(W=0) == hw.HW_ERANGE
+    assert plan(n=0) == hw.HW_ERANGE
+    assert plan(Hq=3) == hw.HW_EINVAL
+    assert plan(E=0) == hw.HW_ERANGE
+    assert plan(E=65) == hw.HW_ERANGE
+    assert plan(ptr=None) == hw.HW_EINVAL
+    assert plan(pb=nb - 4) == hw.HW_EWORKSPACE
+    assert plan(W=21, Hq=8) == hw.HW_ERANGE     # 84 rows
+    run = lambda layer=0, W=2, n=1, Hq=4, ptr=p, pb=nb, theta=1e4, ws=1 << 30: lib.hw_attn_run(
+        P, layer, ptr, W, n, Hq, ptr, pb, theta, ptr, ptr, ws, None)
+    assert run(layer=1) == hw.HW_EINVAL
+    assert run(Hq=3) == hw.HW_EINVAL
+    assert run(W=33) == hw.HW_ERANGE
+    assert run(ptr=None) == hw.HW_EINVAL
+    assert run(pb=nb - 4) == hw.HW_EWORKSPACE
+    assert run(ws=16) == hw.HW_EWORKSPACE
+    assert run(theta=0.0) == hw.HW_EINVAL
+    assert run(theta=float("inf")) == hw.HW_EINVAL
+    assert run(n=2) == hw.HW_EWORKSPACE         # the plan is for one query token
+    # fp32 pools: the VALU kernel only, up to 64 rows
+    f32 = FakePool(dtype=hw.HW_F32, Hkv=1)
+    assert lib.hw_attn_plan(ctypes.byref(f32.desc), 1, 65, 1, p, 3, p, p, 1 << 20,
+                            None) == hw.HW_ERANGE
+    try:
+        hw.hw_set_tuning(hw.PATH_MFMA, 0)
+        assert lib.hw_attn_plan(ctypes.byref(f32.desc), 1, 1, 1, p, 3, p, p, 1 << 20,
+                                None) == hw.HW_EUNSUPPORTED
     finally:
         hw.hw_set_tuning(hw.PATH_AUTO, 0)
 
 
 def test_tuning_validation(lib):
-    assert lib.hw_set_tuning(3, 0) == hw.HW_EINVAL
-    assert lib.hw_set_tuning(0, -1) == hw.HW_EINVAL
-    assert lib.hw_set_tuning(0, 257) == hw.HW_EINVAL
-    assert lib.hw_set_tuning(0, 0) == hw.HW_OK
+    assert lib.hw_set_tuning(3, 0, 1) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, -1, 1) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, 257, 1) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, 0, 2) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, 0, -1) == hw.HW_EINVAL
+    assert lib.hw_set_tuning(0, 0, 0) == hw.HW_OK
+    assert lib.hw_set_tuning(0, 0, 1) == hw.HW_OK
 
 
 def test_append_reset_tables_host_validation(lib):
@@ -139,7 +197,7 @@ def test_append_reset_tables_host_validation(lib):
                                         None) == hw.HW_EINVAL
     assert lib.hw_build_combined_tables(P, 0, 0, ctypes.cast(wb, ctypes.c_void_p), p, p,
                                         None) == hw.HW_ERANGE
-    assert lib.hw_pool_status(None, None, 0) == hw.HW_EINVAL
+    assert lib.hw_pool_status(None, None, 0, None) == hw.HW_EINVAL
 
 
 def test_layout_positions_follow_the_documented_formula():
@@ -195,15 +253,15 @@ def test_chunk_host_validation(lib):
     p = ctypes.c_void_p(0x5000)
     call = lambda W, n, Hq: lib.hw_attn_chunk(P, 0, p, W, n, Hq, p, 3, p, 1e4, p, p, 1 << 30, None)
     assert call(2, 0, 4) == hw.HW_ERANGE          # chunk < 1
-    assert call(2, 17, 4) == hw.HW_ERANGE         # 2 * 17 * 2 rows > 64
+    assert call(2, 21, 4) == hw.HW_ERANGE         # 2 * 21 * 2 rows > 80
     assert call(2, 16, 3) == hw.HW_EINVAL         # Hq % Hkv
-    assert lib.hw_attn_workspace_bytes(P, 64, 2) > 0      # 64 stacked rows (chunk of 64, G = 1)
-    assert lib.hw_attn_workspace_bytes(P, 65, 2) == 0
+    assert lib.hw_attn_workspace_bytes(P, 80, 2) > 0      # 80 stacked rows (chunk of 80, G = 1)
+    assert lib.hw_attn_workspace_bytes(P, 81, 2) == 0
 
 
 def test_fp8_pool_host_validation(lib):
-    """FP8 pools need positive finite scales for every (layer, kv head), at most
-    HW_MAX_FP8_KV_HEADS kv heads, and run on the MFMA kernel only (<= 32 rows)."""
+    """FP8 pools need positive finite scales for the layer's kv heads, at most
+    HW_MAX_FP8_KV_HEADS kv heads, and run on the MFMA kernel only (<= 80 rows)."""
     good = [0.5, 0.25]
     assert decode_rc(lib, FakePool(dtype=hw.HW_FP8)) == hw.HW_EINVAL                # no scales
     assert decode_rc(lib, FakePool(dtype=hw.HW_FP8, k_scale=good)) == hw.HW_EINVAL  # no v scales
@@ -214,7 +272,7 @@ def test_fp8_pool_host_validation(lib):
     assert decode_rc(lib, FakePool(dtype=hw.HW_FP8, Hkv=65, k_scale=many, v_scale=many),
                      Hq=65) == hw.HW_ERANGE
     fp8 = FakePool(dtype=hw.HW_FP8, k_scale=good, v_scale=good)
-    assert decode_rc(lib, fp8, W=17, Hq=4) == hw.HW_EUNSUPPORTED   # 34 rows > 32
+    assert decode_rc(lib, fp8, W=21, Hq=8) == hw.HW_ERANGE   # 84 rows > 80
     try:
         hw.hw_set_tuning(hw.PATH_VALU, 0)
         assert decode_rc(lib, fp8) == hw.HW_EUNSUPPORTED

@@ -61,6 +61,8 @@ def test_fp8_qwq_layer_matches_oracle():
     (2, 16, 2, 128, [300, 7, 33]),       # 16 rows
     (8, 32, 8, 128, [5000] + [17] * 8),  # 32 rows
     (4, 40, 8, 128, [2047, 511, 2, 64, 96]),
+    (12, 48, 8, 64, [900] + [33] * 12),  # 72 rows
+    (16, 40, 8, 128, [700] + [9] * 16),  # 80 rows
 ])
 def test_fp8_ragged_shapes_match_oracle(case):
     W, Hq, Hkv, D, lens = case

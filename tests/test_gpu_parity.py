@@ -94,8 +94,6 @@ def test_ragged_shapes_match_oracle(path, case):
     W, Hq, Hkv, D, lens = case
     hw.hw_set_tuning(path, 0)
     wl = _custom(W, Hq, Hkv, D, lens)
-    if path == hw.PATH_MFMA and wl.rows > 32:
-        pytest.skip("MFMA path holds at most 32 rows")
     s = Setup(wl, poison_unused=True)
     ref, rc = s.oracle_decode()
     assert rc == 0
@@ -107,9 +105,10 @@ def test_ragged_shapes_match_oracle(path, case):
 @pytest.mark.parametrize("path", PATHS)
 def test_fp32_ragged_matches_oracle(path):
     if path == hw.PATH_MFMA:
-        hw.hw_set_tuning(path, 0)
         wl = _custom(2, 4, 2, 64, [40, 3, 9], dtype=torch.float32, theta=1e4, sigma=0.0)
         s = Setup(wl)
+        hw.hw_set_tuning(path, 0)
+        assert hw.hw_attn_workspace_bytes(s.pool, 2, 4) == 0
         q = s.q[0].cuda()
         out = torch.zeros(2, 4, 64, device="cuda")
         with pytest.raises(hw.HWError) as e:
@@ -170,11 +169,20 @@ def test_unit_count_does_not_change_the_result(path):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_deterministic_across_runs(path):
-    hw.hw_set_tuning(path, 0)
+    """Static tile ranges (balance 0): bitwise the same result on every run; balanced
+    tile order: the same result within rounding, and both match the oracle."""
+    hw.hw_set_tuning(path, 0, 0)
     s = Setup(workloads.qwq_layer())
     a = s.decode()
     b = s.decode()
     assert np.array_equal(a, b)
+    hw.hw_set_tuning(path, 0, 1)
+    c = s.decode()
+    d = s.decode()
+    assert np.abs(c - a).max() < 1e-4 and np.abs(d - a).max() < 1e-4
+    ref, _ = s.oracle_decode()
+    assert_close(c, ref, torch.bfloat16, "balanced")
+    assert hw.hw_pool_status(s.pool) == 0
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -382,15 +390,18 @@ def test_interleaved_layout_attention_matches_oracle(path):
     # (W, n, Hq, Hkv, D, lens): rows = W * n * Hq / Hkv
     (2, 4, 4, 2, 128, [900, 70, 45]),
     (4, 8, 8, 8, 64, [300, 9, 33, 64, 1]),        # chunk longer than some own blocks
-    (1, 16, 16, 4, 128, [2048, 100]),            # 64 rows: VALU only
+    (1, 16, 16, 4, 128, [2048, 100]),            # 64 rows
     (2, 3, 40, 8, 128, [4000, 333, 517]),        # QwQ heads, 30 rows
+    (4, 4, 40, 8, 128, [3000, 200, 5, 64, 77]),  # four 4-token block headers at G = 5: 80 rows
+    (1, 12, 40, 8, 128, [5000, 900]),            # a 12-token prompt of one worker: 60 rows
+    (3, 3, 40, 8, 64, [700, 40, 41, 3]),         # 45 rows, D = 64
 ])
 def test_chunk_matches_oracle(path, case):
     W, n, Hq, Hkv, D, lens = case
     hw.hw_set_tuning(path, 0)
     wl = _custom(W, Hq, Hkv, D, lens)
-    if path == hw.PATH_MFMA and W * n * (Hq // Hkv) > 32:
-        pytest.skip("MFMA path holds at most 32 rows")
+    if path == hw.PATH_VALU and W * n * (Hq // Hkv) > 64:
+        pytest.skip("the VALU kernel holds at most 64 rows")
     s = Setup(wl, poison_unused=True)
     g = torch.Generator().manual_seed(9)
     q = torch.randn(W, n, Hq, D, generator=g).to(wl.dtype)
