@@ -84,20 +84,28 @@ def parse():
                     help="step: the headline 64-layer step (default); sweep: context x workers "
                          "grid, per-layer time on both paths; loop: 36-layer generation loop "
                          "with appends")
-    ap.add_argument("--loop-steps", type=int, default=2048)
+    ap.add_argument("--loop-steps", type=int, default=512)
+    ap.add_argument("--api", choices=["decode", "plan_run"], default="decode",
+                    help="decode: hw_attn_decode per layer (plan built in-kernel, the default); "
+                         "plan_run: hw_attn_plan once per step + hw_attn_run per layer")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline step only: no plan_run A/B, sweep, loop or chunk objects")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 E4M3 pool variant of the step (reported as fp8_step)")
     return ap.parse_args()
 
 
-def _graph_layers_us(hw, torch, pool, wl, q, reps=20):
-    """Per-layer time of one decode call over every layer of `pool`, in graph replay."""
+def _graph_layers_us(hw, torch, pool, wl, q, reps=20, api="decode", chunk=1):
+    """Per-layer time of one decode (or chunk) call over every layer of `pool`, in
+    graph replay."""
     W, L = wl.W, pool.num_layers
     out = torch.zeros(L, W, wl.Hq, wl.D, device="cuda")
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
-    ws = hw.alloc_workspace(pool, W, wl.Hq)
-    plan = hw.alloc_plan(pool, W, wl.Hq)
+    ws = hw.alloc_workspace(pool, W * chunk, wl.Hq)
+    plan = hw.alloc_plan(pool, W, wl.Hq, chunk=chunk)
+    if chunk > 1:
+        out = torch.zeros(L, W, chunk, wl.Hq, wl.D, device="cuda")
     # the inputs were written on the default stream: complete them before the
     # side stream reads them, and build the tables on the side stream itself
     torch.cuda.synchronize()
@@ -105,9 +113,16 @@ def _graph_layers_us(hw, torch, pool, wl, q, reps=20):
     hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
 
     def body():
-        hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=st)
-        for layer in range(L):
-            hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, st)
+        if api == "plan_run":
+            hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, chunk=chunk, stream=st)
+            for layer in range(L):
+                hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, st)
+        elif chunk > 1:
+            for layer in range(L):
+                hw.hw_attn_chunk(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
+        else:
+            for layer in range(L):
+                hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
 
     with torch.cuda.stream(st):
         body()
@@ -127,7 +142,7 @@ def _graph_layers_us(hw, torch, pool, wl, q, reps=20):
     return e0.elapsed_time(e1) * 1e3 / (reps * L)
 
 
-def run_sweep(args):
+def run_sweep(args, paths=("mfma", "valu"), reps=20):
     """Context x workers grid (40 q / 8 kv heads, D 128, bf16): per-layer time of
     one decode call.  The K/V bytes do not depend on W, so with the reads shared
     by all workers the time stays flat in W.  Each point cycles through enough
@@ -139,6 +154,8 @@ def run_sweep(args):
 
     points = []
     for path_name, path in (("mfma", hw.PATH_MFMA), ("valu", hw.PATH_VALU)):
+        if path_name not in paths:
+            continue
         hw.hw_set_tuning(path, args.units)
         for C in (1024, 8192, 16384):
             for W in (1, 2, 4):
@@ -152,7 +169,7 @@ def run_sweep(args):
                     pool.store_layer(layer, K, V)
                     del K, V
                 q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
-                us = _graph_layers_us(hw, torch, pool, wl, q)
+                us = _graph_layers_us(hw, torch, pool, wl, q, reps=reps)
                 b = wl.algorithmic_bytes_per_layer()
                 points.append({"path": path_name, "context": C, "workers": W, "layers_cycled": L,
                                "us_per_layer": us, "worker_tokens_per_s_per_layer": W / (us * 1e-6),
@@ -163,8 +180,41 @@ def run_sweep(args):
                 del pool, q
                 torch.cuda.empty_cache()
     hw.hw_set_tuning(hw.PATH_AUTO, 0)
-    print(json.dumps({"config": "sweep", "unit": "us per layer (graph replay)",
-                      "data": "synthetic, seeded", "points": points}), flush=True)
+    return {"config": "sweep", "unit": "us per layer (graph replay, hw_attn_decode)",
+            "data": "synthetic, seeded", "points": points}
+
+
+def run_chunk(args, chunk=4, reps=10):
+    """One chunk call (chunked prefill: each worker's last `chunk` tokens as
+    queries, causal inside the chunk) at the QwQ heads, 4 workers, 16K context:
+    4 * chunk * 5 = 80 stacked rows per kv head on the MFMA path.  Per-layer time
+    in graph replay, cycling layers of distinct K/V."""
+    import torch
+
+    from decode_attention_shared_hw_amd import hogwild_attn as hw
+    from decode_attention_shared_hw_amd import workloads
+
+    wl = workloads.sweep(16384, 4)
+    L = max(8, -(-2 * 256 * 2**20 // wl.kv_bytes_per_layer()))
+    wl.layers = L
+    pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
+    pool.set_lengths(wl.lens)
+    for layer in range(L):
+        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+        pool.store_layer(layer, K, V)
+        del K, V
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 21)
+    q = torch.randn(L, wl.W, chunk, wl.Hq, wl.D, generator=gen, device="cuda").to(wl.q_dtype)
+    us = _graph_layers_us(hw, torch, pool, wl, q, reps=reps, chunk=chunk)
+    b = wl.kv_bytes_per_layer() + wl.W * chunk * wl.Hq * wl.D * (q.element_size() + 4)
+    res = {"workload": f"chunk_16384_4w_x{chunk}", "rows_per_kv_head": wl.W * chunk * wl.G,
+           "kernel": "run_mfma<128,5,bf16> + merge_kernel<128>", "us_per_layer": us,
+           "algorithmic_bytes": b, "achieved_gbs": b / (us * 1e-6) / 1e9,
+           "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "status": hw.hw_pool_status(pool)}
+    del pool, q
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_loop(args):
@@ -201,16 +251,14 @@ def run_loop(args):
     tables = torch.zeros(W, W + 1, 2, dtype=torch.int32, device="cuda")
     ne = torch.zeros(W, dtype=torch.int32, device="cuda")
     ws = hw.alloc_workspace(pool, W, wl.Hq)
-    plan = hw.alloc_plan(pool, W, wl.Hq)
     st = torch.cuda.Stream()
 
     def step_body():
         hw.hw_block_advance(pool, wl.worker_block, st)
         hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, st)
-        hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=st)
         for layer in range(L):
             hw.hw_block_write(pool, layer, wl.worker_block, k_new[layer], v_new[layer], wl.theta, st)
-            hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, st)
+            hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws, st)
 
     lens = np.array(wl.lens, np.int64)
     dec_bytes = 0
@@ -239,13 +287,16 @@ def run_loop(args):
     step_us = ms * 1e3 / steps
     res = {"config": "loop", "workload": wl.name, "steps": steps, "layers": L, "workers": W,
            "appends": len(sched), "common_tokens": [int(wl.lens[0]), int(lens[0])],
-           "step": "advance + tables + plan + 36 x (token write + decode), HIP graph; appends between",
+           "step": "advance + tables + 36 x (token write + decode), HIP graph; appends between",
            "us_per_step": step_us, "us_per_layer": step_us / L,
            "worker_tokens_per_s_per_layer": W * L / (step_us * 1e-6),
            "decode_achieved_gbs": dec_bytes / (ms * 1e-3) / 1e9,
            "status": hw.hw_pool_status(pool),
            "final_lengths": pool.block_len.cpu().tolist(), "expected_lengths": lens.tolist()}
-    print(json.dumps(res), flush=True)
+    res["lengths_ok"] = res["final_lengths"] == res["expected_lengths"]
+    del pool, q, k_new, v_new, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_threads() -> int:
@@ -339,7 +390,7 @@ def make_step_pool(hw, torch, workloads, wl, keep_layer0):
     return pool, q, host_layer0
 
 
-def time_step(args, hw, torch, np, wl, pool, q):
+def time_step(args, hw, torch, np, wl, pool, q, api="decode"):
     """Graph (or eager) replay of the step, then per-launch HIP-event durations of
     the decode calls and the append in an eager replay behind a GPU spin."""
     L, W = wl.layers, wl.W
@@ -357,11 +408,16 @@ def time_step(args, hw, torch, np, wl, pool, q):
         k = counter[0]
         counter[0] += 1
         hw.hw_build_combined_tables(pool, W, wl.common_block, wl.worker_block, tables, ne, stream)
-        hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=stream)
+        if api == "plan_run":
+            hw.hw_attn_plan(pool, tables, ne, plan, wl.Hq, stream=stream)
         if events is not None:
             events["dec"][0].record(stream)
         for layer in range(L):
-            hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, stream)
+            if api == "plan_run":
+                hw.hw_attn_run(pool, layer, q[layer], plan, wl.theta, out[layer], ws, stream)
+            else:
+                hw.hw_attn_decode(pool, layer, q[layer], tables, ne, wl.theta, out[layer], ws,
+                                  stream)
         if events is not None:
             events["dec"][1].record(stream)
         src = wl.worker_block[k % W]
@@ -441,16 +497,18 @@ def main():
         sys.exit(1)
     hw.lib()  # fail loudly if the library is missing
     if args.config == "sweep":
-        return run_sweep(args)
+        print(json.dumps(run_sweep(args)), flush=True)
+        return
     if args.config == "loop":
-        return run_loop(args)
+        print(json.dumps(run_loop(args)), flush=True)
+        return
     path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
     hw.hw_set_tuning(path, args.units, 1 if args.balance else 0)
 
     wl = workloads.qwq_step(layers=args.layers)
     L, W = wl.layers, wl.W
     pool, q, host_layer0 = make_step_pool(hw, torch, workloads, wl, not args.no_cpu_baseline)
-    t = time_step(args, hw, torch, np, wl, pool, q)
+    t = time_step(args, hw, torch, np, wl, pool, q, api=args.api)
     if args.calibrate_copy > 0:
         # one plain copy of a known size: HBM counters of this dispatch scale
         # the decode kernel's counters (bytes read = bytes written = MIB MiB)
@@ -483,15 +541,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q; K,V N(0,1) + per-channel N(0,0.5) offset)",
-        "config": {**workloads.summary(wl), "parallelism": "single GPU",
-                   "step": "tables + plan + 64 x decode + 1 block append (graph replay)"
-                   if use_graph else "tables + plan + 64 x decode + 1 block append (eager)"},
+        "config": {**workloads.summary(wl), "parallelism": "single GPU", "api": args.api,
+                   "step": ("tables + " + ("plan + " if args.api == "plan_run" else "")
+                            + "64 x decode + 1 block append ("
+                            + ("graph replay)" if use_graph else "eager)"))},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic() if path != hw.PATH_VALU else None,
-            "kernel": ("decode call = run_mfma<128,2,bf16> (one launch)"
-                       if path != hw.PATH_VALU else "decode call = run_valu<bf16,128,10> (one launch)"),
+            "kernel": ("decode call = run_valu<bf16,128,10> + merge_kernel<128>"
+                       if path == hw.PATH_VALU else
+                       "decode call = run_mfma<128,2,bf16> + merge_kernel<128>"
+                       if args.api == "plan_run" else
+                       "decode call = decode_mfma<128,2,bf16> (fused plan) + merge_kernel<128>"),
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": dec_avg,
             "p10_us": float(np.percentile(dec_us, 10)),
@@ -502,6 +564,15 @@ def main():
         "wall_s": t["wall"],
         "device_status": t["flags"],
     }
+    if not args.no_extras and path != hw.PATH_VALU:
+        # A/B: the same step with the plan computed once per step (hw_attn_plan)
+        # and read by every layer's call (hw_attn_run)
+        other = "plan_run" if args.api == "decode" else "decode"
+        ta = time_step(args, hw, torch, np, wl, pool, q, api=other)
+        da = float(np.mean(ta["dec_us"]))
+        result["ab_api"] = {"api": other, "us_per_layer": ta["ms_per_step"] * 1e3 / L,
+                            "avg_launch_us": da, "frac": bytes_per_launch / (da * 1e-6) / 1e9
+                            / HBM_PEAK_GBS, "device_status": ta["flags"]}
     if not args.no_cpu_baseline:
         K0, V0 = host_layer0
         result["cpu_baseline"] = cpu_baseline(wl, pool.block_start, K0, V0, q[0].cpu(),
@@ -514,7 +585,7 @@ def main():
         torch.cuda.empty_cache()
         wl8 = workloads.with_fp8(wl)
         pool8, q8, _ = make_step_pool(hw, torch, workloads, wl8, False)
-        t8 = time_step(args, hw, torch, np, wl8, pool8, q8)
+        t8 = time_step(args, hw, torch, np, wl8, pool8, q8, api=args.api)
         d8 = float(np.mean(t8["dec_us"]))
         b8 = wl8.algorithmic_bytes_per_layer()
         result["fp8_step"] = {
@@ -526,6 +597,16 @@ def main():
             "frac_of_peak": b8 / (d8 * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "append_us": float(np.mean(t8["app_us"])), "device_status": t8["flags"],
         }
+        del pool8, q8
+    if not args.no_extras and path != hw.PATH_VALU:
+        pool = q = None  # (the FP8 variant may have released them already)
+        torch.cuda.empty_cache()
+        hw.hw_set_tuning(hw.PATH_AUTO, args.units)
+        result["chunk"] = run_chunk(args)
+        sw = run_sweep(args, paths=("mfma",), reps=10)
+        result["sweep"] = [{k: p[k] for k in ("context", "workers", "us_per_layer",
+                                               "frac_of_peak", "status")} for p in sw["points"]]
+        result["loop"] = run_loop(args)
     print(json.dumps(result), flush=True)
 
 

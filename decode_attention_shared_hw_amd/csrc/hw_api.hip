@@ -20,14 +20,15 @@ int g_balance = 0;         // 1: balanced tile order in the split launch
 struct DeviceInfo {
   bool ready = false;
   int cus = 0;
-  int occ[3][3][2][5] = {};  // [path][dtype][D == 128][rows class: <=16, 32, 48, 64, 80]
+  int occ[4][3][2][5] = {};  // [path: -, VALU, MFMA, fused][dtype][D == 128][rows class: <=16, 32, 48, 64, 80]
 };
 std::mutex g_dev_mu;
 DeviceInfo g_dev[64];
 
 int row_class(int rows) { return rows <= 16 ? 0 : rows <= 32 ? 1 : rows <= 48 ? 2 : rows <= 64 ? 3 : 4; }
 
-// Resident run workgroups of the whole device for this launch shape.  Where
+// Resident split-launch workgroups of the whole device for this launch shape
+// (path 3: the fused kernel).  Where
 // no device answers (a host without a GPU: only argument checks and sizes
 // are asked for there), an MI355X with one workgroup per CU is assumed.
 constexpr int kDefaultCUs = 256;
@@ -43,7 +44,7 @@ int device_capacity(int path, int dtype, int D, int rows) {
     d.ready = true;
   }
   int& o = d.occ[path][dtype][D == 128 ? 1 : 0][row_class(rows)];
-  if (o == 0) o = run_blocks_per_cu(path, dtype, D, rows);
+  if (o == 0) o = path == 3 ? fused_blocks_per_cu(dtype, D, rows) : run_blocks_per_cu(path, dtype, D, rows);
   return d.cus * (o > 0 ? o : 1);
 }
 
@@ -159,7 +160,8 @@ hw_status call_shape(const hw_pool* pool, int W, int nq, int Hq, Shape* s) {
   if (s->path == 2 && pool->dtype == HW_F32) return HW_EUNSUPPORTED;
   if (s->path == 1 && pool->dtype == HW_FP8) return HW_EUNSUPPORTED;
   if (s->path == 1 && s->R > kValuMaxRows) return HW_ERANGE;
-  const int cap = device_capacity(s->path, pool->dtype, pool->head_dim, s->R);
+  const bool fused = s->path == 2 && pool->dtype != HW_F32 && s->R <= kFusedMaxRows;
+  const int cap = device_capacity(fused ? 3 : s->path, pool->dtype, pool->head_dim, s->R);
   int64_t P = cap / pool->num_kv_heads;
   if (g_units_per_head > 0 && g_units_per_head < P) P = g_units_per_head;
   if (P > kMaxUnits) P = kMaxUnits;
@@ -182,21 +184,29 @@ size_t plan_bytes(const hw_pool* pool, const Shape& s) {
 }
 
 struct WsLayout {
-  size_t plan_off, ml_off, acc_off, cnt_off, total;
+  size_t plan_off, ml_off, acc_off, cnt_off, hint_off, total;
 };
 
 // [tile counters][plan][Hkv][R][P] (m, l) pairs [Hkv][R][P][D] accumulators
-// [Hkv][P] tile counts.
+// [Hkv][P] tile counts [Hkv][P][kMfmaWaves] first-tile hints (fused path).
 WsLayout ws_layout(const hw_pool* pool, const Shape& s) {
   WsLayout w;
   auto up = [](size_t x) { return 256 * ((x + 255) / 256); };
+  const size_t units = static_cast<size_t>(pool->num_kv_heads) * s.P;
   w.plan_off = kSyncBytes;
   w.ml_off = up(w.plan_off + plan_bytes(pool, s));
-  const size_t rows = static_cast<size_t>(pool->num_kv_heads) * s.P * s.R;
+  const size_t rows = units * s.R;
   w.acc_off = up(w.ml_off + rows * sizeof(float2));
   w.cnt_off = up(w.acc_off + rows * pool->head_dim * sizeof(float));
-  w.total = w.cnt_off + static_cast<size_t>(pool->num_kv_heads) * s.P * sizeof(int32_t);
+  w.hint_off = up(w.cnt_off + units * sizeof(int32_t));
+  w.total = w.hint_off + units * kMfmaWaves * sizeof(uint32_t);
   return w;
+}
+
+// Decode calls that take the fused kernel (plan built in-kernel): MFMA path,
+// bf16 or FP8 pool, up to 32 stacked rows.
+bool fused_path(const hw_pool* pool, const Shape& s) {
+  return s.path == 2 && pool->dtype != HW_F32 && s.R <= kFusedMaxRows;
 }
 
 hw_status plan_call(const hw_pool* pool, const Shape& s, const hw_entry* tables,
@@ -288,6 +298,87 @@ hw_status run_call(const hw_pool* pool, int32_t layer, const void* q, const Shap
   if (a.Hkv > 256) a.mHkv = 0;
   hipError_t e = s.path == 2 ? launch_run_mfma(a, stream) : launch_run_valu(a, stream);
   if (e == hipSuccess && s.P > 1) e = launch_merge(a, stream);
+  return e == hipSuccess ? HW_OK : HW_EHIP;
+}
+
+// Split launch with the plan built in-kernel (hw_fused.hip), then the merge.
+// The caller has validated the shape, the pointers and the workspace.
+hw_status fused_call(const hw_pool* pool, int32_t layer, const void* q, const Shape& s,
+                     const hw_entry* tables, int32_t max_entries, const int32_t* num_entries,
+                     double theta, float* out, void* workspace, const WsLayout& wl,
+                     hipStream_t stream) {
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  const size_t esz = elem_bytes(pool->dtype);
+  const int64_t plane = pool->num_slots * pool->head_dim;
+  const int64_t layer_off = static_cast<int64_t>(layer) * pool->num_kv_heads * plane;
+  a.q = q;
+  a.k = static_cast<const char*>(pool->k) + layer_off * esz;
+  a.v = static_cast<const char*>(pool->v) + layer_off * esz;
+  a.block_len = pool->block_len;
+  a.tables = tables;
+  a.num_entries = num_entries;
+  a.out = out;
+  a.status = pool->status;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_ml = reinterpret_cast<float2*>(ws + wl.ml_off);
+  a.ws_acc = reinterpret_cast<float*>(ws + wl.acc_off);
+  a.ws_hint = reinterpret_cast<uint32_t*>(ws + wl.hint_off);
+  a.plane_elems = plane;
+  a.plane_bytes = static_cast<int32_t>(plane * static_cast<int64_t>(esz));
+  a.W = s.W;
+  a.Hq = s.Hq;
+  a.Hkv = pool->num_kv_heads;
+  a.G = s.G;
+  a.R = s.R;
+  a.nq = s.nq;
+  a.E = max_entries;
+  a.NB = pool->num_blocks;
+  a.P = s.P;
+  a.D = pool->head_dim;
+  a.dtype = pool->dtype;
+  a.mP = div_magic(static_cast<uint32_t>(a.P));
+  a.rP = 1.0 / a.P;
+  a.mE = div_magic(static_cast<uint32_t>(a.E));
+  a.mG = div_magic(static_cast<uint32_t>(a.G));
+  a.mGnq = div_magic(static_cast<uint32_t>(a.G * a.nq));
+  a.mR = div_magic(static_cast<uint32_t>(a.R));
+  a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
+  for (int b = 0; b < pool->num_blocks; ++b) {
+    a.tab.block_start[b] = pool->block_start[b];
+    a.tab.block_cap[b] = pool->block_cap[b];
+  }
+  rope_tables(theta, pool->head_dim, a.tab.inv_freq, a.tab.rope_frac);
+  if (pool->dtype == HW_FP8) {
+    const int64_t l0 = static_cast<int64_t>(layer) * pool->num_kv_heads;
+    for (int g = 0; g < pool->num_kv_heads; ++g) {
+      a.tab.k_scale[g] = pool->k_scale[l0 + g];
+      a.tab.v_scale[g] = pool->v_scale[l0 + g];
+    }
+  }
+  hipError_t e = launch_fused_mfma(a, s.P * pool->num_kv_heads, stream);
+  if (e == hipSuccess) {
+    // the merge reads the partials in the same [Hkv][R][P] layout
+    RunArgs m;
+    memset(&m, 0, sizeof(m));
+    m.out = out;
+    m.status = pool->status;
+    m.ws_ml = a.ws_ml;
+    m.ws_acc = a.ws_acc;
+    m.Hq = s.Hq;
+    m.Hkv = pool->num_kv_heads;
+    m.G = s.G;
+    m.R = s.R;
+    m.qrows = s.qrows;
+    m.NB = pool->num_blocks;
+    m.P = s.P;
+    m.D = pool->head_dim;
+    m.mG = a.mG;
+    m.mR = a.mR;
+    m.dtype = pool->dtype;
+    memcpy(m.v_scale, a.tab.v_scale, sizeof(m.v_scale));
+    e = launch_merge(m, stream);
+  }
   return e == hipSuccess ? HW_OK : HW_EHIP;
 }
 
@@ -386,9 +477,12 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   if (!aligned16(workspace)) return HW_EINVAL;
   st = check_scales(pool, layer);
   if (st != HW_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (fused_path(pool, s))
+    return fused_call(pool, layer, q, s, tables, max_entries, num_entries, rope_theta, out,
+                      workspace, wl, hs);
   char* plan = static_cast<char*>(workspace) + wl.plan_off;
   const size_t pb = wl.ml_off - wl.plan_off;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
   st = plan_call(pool, s, tables, max_entries, num_entries, plan, pb, hs);
   if (st != HW_OK) return st;
   return run_call(pool, layer, q, s, plan, pb, rope_theta, out, workspace, workspace_bytes, hs);

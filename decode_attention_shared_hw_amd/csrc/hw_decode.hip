@@ -31,123 +31,10 @@
 #include <type_traits>
 
 #include "hw_internal.h"
+#include "hw_kernels.h"
 
 namespace hw {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two floats rounded to bf16 (nearest even), low half first.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-// cos/sin of delta * w with the angle formed and reduced mod 2*pi in fp64,
-// so that positions of ~1e5 keep ~1e-7 rad of accuracy (fp32 pools).
-__device__ __forceinline__ void rope_cos_sin(int64_t delta, double w, float* c, float* s) {
-  const double a = static_cast<double>(delta) * w;
-  const double k = rint(a * 0.15915494309189535);      // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586, a);            // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);              // 2 pi, low part
-  sincosf(static_cast<float>(r), s, c);
-}
-
-// Same angle in revolutions, reduced exactly: frac is theta^(-2i/D)/(2 pi)
-// mod 1 as a 64-bit binary fraction, so delta * frac mod 2^64 (integer
-// wrap-around) is the angle's fractional revolution; its top 32 bits, as a
-// signed value, give the angle in [-1/2, 1/2) revolution.  The hardware
-// v_sin/v_cos take revolutions; the result carries ~1e-6 absolute error, far
-// below the bf16 rounding applied to the rotated query on the MFMA path.
-__device__ __forceinline__ void rope_cos_sin_fx(uint32_t delta, uint64_t frac, float* c,
-                                                float* s) {
-  // bits 32..63 of delta * frac (mod 2^64), delta < 2^32
-  const uint32_t ph = __umulhi(delta, static_cast<uint32_t>(frac)) +
-                      delta * static_cast<uint32_t>(frac >> 32);
-  const float fr = static_cast<float>(static_cast<int32_t>(ph)) * 0x1p-32f;
-  *s = __builtin_amdgcn_sinf(fr);
-  *c = __builtin_amdgcn_cosf(fr);
-}
-
-// Lane l and lane l ^ 16 (l ^ 32) exchange values through the permlane swap
-// instructions (no LDS round trip): the pair returned holds the lane's own
-// value and its partner's, so a symmetric operation on the pair gives the
-// same result in both lanes.
-__device__ __forceinline__ float max_x16(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float max_x32(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ __forceinline__ float sum_x16(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float sum_x32(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-// DPP move inside rows of 16 lanes.  The four patterns quad_perm [1,0,3,2],
-// quad_perm [2,3,0,1], row_half_mirror and row_mirror, applied in turn with a
-// symmetric combine, leave every lane with the combination of its 16-lane row.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppRow16[4] = {0xb1, 0x4e, 0x141, 0x140};
-
-// max / sum over the 32 lanes of each half of the wave (every lane gets it)
-__device__ __forceinline__ float half_max(float x) {
-  x = fmaxf(x, dpp_mov<0xb1>(x));
-  x = fmaxf(x, dpp_mov<0x4e>(x));
-  x = fmaxf(x, dpp_mov<0x141>(x));
-  x = fmaxf(x, dpp_mov<0x140>(x));
-  return max_x16(x);
-}
-__device__ __forceinline__ float half_sum(float x) {
-  x += dpp_mov<0xb1>(x);
-  x += dpp_mov<0x4e>(x);
-  x += dpp_mov<0x141>(x);
-  x += dpp_mov<0x140>(x);
-  return sum_x16(x);
-}
-
-constexpr int cmax(int x, int y) { return x > y ? x : y; }
-
-// Raw buffer resource (gfx9 descriptor word 3): lane offsets are range-checked
-// against `bytes`, so an offset past the end reads zero and writes nothing.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes,
-                                           0x00020000);
-}
-
-// Cache policy bits of gfx950 buffer accesses.
-constexpr int kPolicySC0 = 1;   // past the CU's L1 (L2 of the XCD)
-constexpr int kPolicyNT = 2;    // non-temporal: data read once (the K/V stream)
-constexpr int kPolicySC1 = 16;  // device scope: coherent between all CUs of the GPU
-
-// Phase timestamps of an instrumented build (HW_STAMPS, never in the
-// library's own build): thread 0 of each workgroup (lane 0 of each wave for
-// the per-wave stamps) records the 100 MHz real-time clock at fixed points.
-#ifdef HW_STAMPS
-__device__ uint64_t g_stamps[4096 * 32];
-#define HW_STAMP(k) (g_stamps[blockIdx.x * 32 + (k)] = __builtin_amdgcn_s_memrealtime())
-#define HW_MSTAMP(k) (g_stamps[(1024 + blockIdx.x) * 32 + (k)] = __builtin_amdgcn_s_memrealtime())
-#else
-#define HW_STAMP(k) ((void)0)
-#define HW_MSTAMP(k) ((void)0)
-#endif
 
 // ------------------------------------------------------------- plan in LDS
 struct PlanLds {
@@ -289,9 +176,56 @@ __device__ __forceinline__ TileRef tile_ref(const PlanLds& pl, int j, int& bcur)
 }
 
 // ------------------------------------------------------------ unit finish
+// A value the compiler must keep in SGPRs from here on.  Kernel arguments
+// are otherwise reloaded at their uses (a reload is cheaper for it than a
+// live register), and in the epilogue each reload is a round trip queued
+// behind the chip's K/V stream.
+template <typename T>
+__device__ __forceinline__ T pin_sgpr(T x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// The epilogue's scalars, read from the arguments at kernel entry.
+struct EpiArgs {
+  float* out;
+  float2* ws_ml;
+  float* ws_acc;
+  int32_t* ws_cnt;
+  int32_t* status;
+  int R, P, Hq, G;
+  uint32_t mG;
+  float vsc;  // FP8 pools: value scale of the kv head, else 1
+};
+
+// kPin: keep them in SGPRs (kernels with SGPRs to spare).
+template <bool kFp8, bool kPin>
+__device__ __forceinline__ EpiArgs epi_args(const RunArgs& a, int g) {
+  auto pin = [](auto x) { return kPin ? pin_sgpr(x) : x; };
+  EpiArgs e;
+  e.out = pin(a.out);
+  e.ws_ml = pin(a.ws_ml);
+  e.ws_acc = pin(a.ws_acc);
+  e.ws_cnt = pin(a.ws_cnt);
+  e.status = pin(a.status);
+  e.R = pin(a.R);
+  e.P = pin(a.P);
+  e.Hq = pin(a.Hq);
+  e.G = pin(a.G);
+  e.mG = pin(a.mG);
+  e.vsc = 1.f;
+  if (kFp8) {
+    const float v = reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a) +
+                                                   offsetof(RunArgs, v_scale))[g];
+    e.vsc = __int_as_float(pin(__builtin_amdgcn_readfirstlane(__float_as_int(v))));
+  }
+  return e;
+}
+
 // Stacked rows of kv head g: r = i * G + (h - g * G) for query row i
 // (= w * nq + j) and q-head h; output row (i, h) of out [qrows][Hq][D].
-__device__ __forceinline__ int64_t out_row(const RunArgs& a, int g, int r) {
+template <typename A>
+__device__ __forceinline__ int64_t out_row(const A& a, int g, int r) {
   const int i = fast_div(r, a.mG);
   return static_cast<int64_t>(i) * a.Hq + g * a.G + (r - i * a.G);
 }
@@ -302,16 +236,13 @@ __device__ __forceinline__ int64_t out_row(const RunArgs& a, int g, int r) {
 // the unit's partial ([Hkv][R][P] (m, l) pairs, [Hkv][R][P][D]
 // accumulators), or, with one unit per head, the final rows out = O / L.
 template <int NTHR, int D>
-__device__ void emit_unit(const RunArgs& a, PlanLds& pl, int g, int u, const float* sbuf, int ns,
+__device__ void emit_unit(const EpiArgs& a, PlanLds& pl, int g, int u, const float* sbuf, int ns,
                           int sstride, int rc) {
   constexpr int ACC_STRIDE = D + 4;
   constexpr int kMaxStates = 8;
   const int tid = threadIdx.x;
   const int R = a.R, P = a.P;
-  const float vsc = a.dtype == HW_FP8
-                        ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(&a) +
-                                                         offsetof(RunArgs, v_scale))[g]
-                        : 1.f;
+  const float vsc = a.vsc;
   for (int x = tid; x < R * (D / 8); x += NTHR) {
     const int r = x / (D / 8), d8 = 8 * (x - r * (D / 8));
     float mw[kMaxStates];
@@ -356,170 +287,9 @@ __device__ void emit_unit(const RunArgs& a, PlanLds& pl, int g, int u, const flo
 // ------------------------------------------------------------- MFMA kernel
 // bf16 and FP8 pools, rows R = W*G <= 16*NT.  Each of the NW waves owns every
 // NW-th tile of the workgroup's range and keeps its own (m, l, O^T) for all
-// rows; the waves' states are combined in LDS at the end.
-//
-// Fragments (v_mfma_f32_16x16x32_bf16, lane l: i = l%16, q4 = l/16):
-//   S^T[tok][row] = K[tok][:] . Q~[row][:]
-//     A (K):  token i of half a, dims 8*(4s+q4)..+8  (one 16-B load)
-//     B (Q~): row 16t+i, same dims
-//     D:      tokens 16a + 4*q4 + v, row 16t+i
-//   O^T[d][row] = V^T[d][tok] . P^T[tok][row]
-//     A (V^T): dim 16m+i, tokens {4*q4+v, 16+4*q4+v} (one 16-B load)
-//     B (P^T): row 16t+i, the same 8 tokens = this lane's S^T outputs
-//     D:       dims 16m + 4*q4 + v, row 16t+i
+// rows; the waves' states are combined in LDS at the end.  Fragment layouts:
+// hw_kernels.h.
 
-// Stored K/V elements as MFMA A fragments (8 elements per lane): bf16 pools
-// load 16 bytes and use them as they are; FP8 E4M3 pools load 8 bytes, which
-// are widened to bf16 (exactly: every E4M3 value is a bf16 value) just before
-// the product that consumes them, so the registers of a tile in flight hold
-// the narrow codes.  Every K/V fragment is read exactly once per call: the
-// loads carry the non-temporal policy.
-template <typename E>
-struct KvFrag;
-template <>
-struct KvFrag<uint16_t> {
-  typedef u32x4 type;
-  static constexpr int kBytes = 2;
-  __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kPolicyNT);
-  }
-  __device__ static u32x4 widen(const type& f) { return f; }
-};
-template <>
-struct KvFrag<uint8_t> {
-  typedef u32x2 type;
-  static constexpr int kBytes = 1;
-  __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kPolicyNT);
-  }
-  template <bool HI>
-  __device__ static uint32_t pair(uint32_t w) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-  }
-  __device__ static u32x4 widen(const type& f) {
-    return u32x4{pair<false>(f[0]), pair<true>(f[0]), pair<false>(f[1]), pair<true>(f[1])};
-  }
-};
-
-// (a3) one buffer load per lane per fragment: every key load of a wave is one
-// contiguous run (1 KB bf16, 512 B FP8), every value load four contiguous
-// runs.  koff / voff: this lane's byte offsets inside a tile; tile: the tile's
-// byte offset in the plane (wave-uniform, an SGPR operand).  The plane's
-// resource range-checks the lane offsets; the tile offset is inside the plane
-// by construction (a tile lies inside its block's capacity, whose slots the
-// host checked against the plane).
-template <int D, typename E>
-__device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t tile, uint32_t koff,
-                                          typename KvFrag<E>::type (&kf)[2][D / 32]) {
-  constexpr int B = KvFrag<E>::kBytes;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      kf[h2][s] = KvFrag<E>::load(krs, koff + (h2 * 16 * D + 4 * s * 128) * B, tile);
-}
-
-template <int D, typename E>
-__device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t tile,
-                                            uint32_t voff, typename KvFrag<E>::type (&vf)[D / 16]) {
-  constexpr int B = KvFrag<E>::kBytes;
-#pragma unroll
-  for (int m = 0; m < D / 16; ++m) vf[m] = KvFrag<E>::load(vrs, voff + 16 * m * 8 * B, tile);
-}
-
-// S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
-// qf: this lane's rotated-query B fragments, [NT][KS] x 64 lanes in LDS.
-template <int D, int NT, typename E>
-__device__ __forceinline__ void tile_scores(const typename KvFrag<E>::type (&kf)[2][D / 32],
-                                            const bf16x8* qf, int lane, f32x4 (&sc)[2][NT]) {
-  constexpr int KS = D / 32;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 qv = qf[(t * KS + s) * 64 + lane];
-      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, KvFrag<E>::widen(kf[0][s])), qv, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, KvFrag<E>::widen(kf[1][s])), qv, c1, 0, 0, 0);
-    }
-    sc[0][t] = c0;
-    sc[1][t] = c1;
-  }
-}
-
-// Online softmax of one tile's scores and the P.V update of the running
-// (m, l, O^T).  Row t keeps the tile's tokens up to rowlim[t] (its causal
-// limit, below `valid`); values of tokens at or past `valid` are zeroed.  The
-// row sum adds the bf16-rounded weights the P.V product uses, so numerator
-// and denominator carry the same weights.
-template <int D, int NT, typename E>
-__device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
-                                            const typename KvFrag<E>::type (&vf)[D / 16],
-                                            const bool (&rowvis)[NT], const int (&rowlim)[NT],
-                                            int valid, int q4,
-                                            f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
-                                            float (&l_run)[NT]) {
-  constexpr int MT = D / 16;
-  bf16x8 pf[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float sv[8];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = 16 * h2 + 4 * q4 + v;
-        sv[4 * h2 + v] = (rowvis[t] && tok <= rowlim[t]) ? sc[h2][t][v] : -INFINITY;
-      }
-    float mt = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-    mt = max_x32(max_x16(mt));
-    const float mn = fmaxf(m_run[t], mt);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float al = __builtin_amdgcn_exp2f(m_run[t] - mu);
-    float sum = 0.f;
-    bf16x8 f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[e] - mu));
-      sum += static_cast<float>(f[e]);
-    }
-    pf[t] = f;
-    l_run[t] = l_run[t] * al + sum;
-    m_run[t] = mn;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m][t] *= al;
-  }
-  // tokens past the block's length may hold anything (even NaN): zero them
-  u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
-  if (valid < kTile) {
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const int t0 = 16 * ((2 * e2) >> 2) + 4 * q4 + ((2 * e2) & 3);
-      const int t1 = 16 * ((2 * e2 + 1) >> 2) + 4 * q4 + ((2 * e2 + 1) & 3);
-      keep[e2] = (t0 < valid ? 0x0000ffffu : 0u) | (t1 < valid ? 0xffff0000u : 0u);
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const u32x4 v = KvFrag<E>::widen(vf[m]) & keep;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pf[t],
-                                                          acc[m][t], 0, 0, 0);
-  }
-}
-
-// A group's first tile is requested after its rotated queries are published
-// (0), its keys before the rotation (1), keys and values before it (2), or
-// (3) keys and values before it by the upper half of the waves while the
-// lower half rotates.  A
-// CU takes about 64 KB of outstanding loads before a wave's next load blocks
-// at issue, so requesting 8 waves' 16 KB tiles first stalls the rotation and
-// the barrier behind it until the first tiles return.
 #ifndef HW_ISSUE_BEFORE_ROTATION
 #define HW_ISSUE_BEFORE_ROTATION 1
 #endif
@@ -557,12 +327,27 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   // done with its tiles deposits its state while the others still stream
   __shared__ __attribute__((aligned(16))) float ebuf[kEpiFloats];
 
+  // every scalar argument, requested at entry in one round trip: otherwise
+  // each first use (epilogue included) waits for its own kernel-argument load
+  // behind the chip's K/V stream (kernels of up to 32 rows: the larger ones
+  // have no SGPRs to spare)
+  if constexpr (NT <= 2)
+    asm volatile("" ::"s"(a.q), "s"(a.k), "s"(a.v), "s"(a.plan), "s"(a.block_len), "s"(a.out),
+                 "s"(a.status), "s"(a.sync), "s"(a.ws_ml), "s"(a.ws_acc), "s"(a.ws_cnt),
+                 "s"(a.plane_elems), "s"(a.plane_bytes), "s"(a.Hq), "s"(a.Hkv), "s"(a.G), "s"(a.R),
+                 "s"(a.qrows), "s"(a.NB), "s"(a.P), "s"(a.mG), "s"(a.mHkv), "s"(a.mR),
+                 "s"(a.mP), "s"(a.balance), "s"(a.dtype), "s"(a.qscale));
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;
   if (tid == 0) HW_STAMP(0);
   int g, u;
   head_unit(a, &g, &u);
+  const EpiArgs ea = epi_args<EB == 1, (NT <= 2)>(a, g);
+  // the rotation's and the loop's row scalars, kept in SGPRs likewise
+  const int nrows = ea.R;
+  const uint32_t mG = ea.mG;
+  const int qrows = NT <= 2 ? pin_sgpr(a.qrows) : a.qrows;
 
   // ---- 1. one round trip: plan, lengths, rotation steps, this head's rows
   constexpr int kQVec = RP * D / 8;
@@ -579,8 +364,8 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
     const int x = tid + k * NTHR;
     const int r = (8 * x) / D, d = (8 * x) - r * D;
     qv[k] = u32x4{0u, 0u, 0u, 0u};
-    if (x < kQVec && r < a.R)
-      qv[k] = *reinterpret_cast<const u32x4*>(qg + out_row(a, g, r) * D + d);
+    if (x < kQVec && r < nrows)
+      qv[k] = *reinterpret_cast<const u32x4*>(qg + out_row(ea, g, r) * D + d);
   }
   // this head's K/V plane descriptors and the query scale (FP8 pools: times
   // the key scale of the kv head)
@@ -639,7 +424,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
       const int r = 16 * t + (ln & 15);
       const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner dims are d0 + HALF
       int re = -1;
-      if (r < a.R) re = rows_lds[(gb + bi) * a.qrows + fast_div(r, a.mG)];
+      if (r < nrows) re = rows_lds[(gb + bi) * qrows + fast_div(r, mG)];
       const float sc = re >= 0 ? qsc : 0.f;
       const uint32_t delta = static_cast<uint32_t>(re >= 0 ? re : 0);
       const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
@@ -678,7 +463,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int r = 16 * t + li;
-        rowend[t] = r < a.R ? rows_lds[qb * a.qrows + fast_div(r, a.mG)] : -1;
+        rowend[t] = r < nrows ? rows_lds[qb * qrows + fast_div(r, mG)] : -1;
         rowvis[t] = rowend[t] >= 0;
       }
     }
@@ -816,7 +601,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + li;
-      if (r >= a.R) continue;
+      if (r >= nrows) continue;
       if (q4 == 0) {
         buf[rc * ACC_STRIDE + r] = m_run[t];
         buf[rc * ACC_STRIDE + rc + r] = l_run[t];
@@ -827,7 +612,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
     }
   };
   int ns, sstride, rc;
-  if (kOneLevelOk && a.R <= RC1) {
+  if (kOneLevelOk && nrows <= RC1) {
     deposit(ebuf + wave * kState1, RC1);
     ns = NWAVE;
     sstride = kState1;
@@ -841,7 +626,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int r = 16 * t + li;
-        if (r >= a.R) continue;
+        if (r >= nrows) continue;
         const float m2 = src[RP * ACC_STRIDE + r];
         const float l2 = src[RP * ACC_STRIDE + RP + r];
         const float M = fmaxf(m_run[t], m2);
@@ -863,7 +648,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   }
   __syncthreads();
   if (tid == 0) HW_STAMP(11);
-  emit_unit<NTHR, D>(a, pl, g, u, ebuf, ns, sstride, rc);
+  emit_unit<NTHR, D>(ea, pl, g, u, ebuf, ns, sstride, rc);
   if (lane == 0) HW_STAMP(16 + wave);
 }
 
@@ -926,6 +711,7 @@ __global__ __launch_bounds__(kThreads) void run_valu(RunArgs a) {
   const int tl = lane & 31, rg = lane >> 5;
   int g, u;
   head_unit(a, &g, &u);
+  const EpiArgs ea = epi_args<false, false>(a, g);
   int lo, hi, b_first, b_last;
   {
     constexpr int kQVec = RM * D / 4;  // float4 of staged query
@@ -1209,7 +995,7 @@ __global__ __launch_bounds__(kThreads) void run_valu(RunArgs a) {
   __syncthreads();
   if (wave < 2) deposit(ubuf + wave * kState);
   __syncthreads();
-  emit_unit<NTHR, D>(a, pl, g, u, ubuf, 2, kState, RM);
+  emit_unit<NTHR, D>(ea, pl, g, u, ubuf, 2, kState, RM);
 }
 
 // ----------------------------------------------------------- merge kernel

@@ -126,6 +126,49 @@ struct alignas(16) RunArgs {
   float v_scale[HW_MAX_FP8_KV_HEADS];
 };
 
+// Split launch of decode calls with the plan built in-kernel (hw_fused.hip).
+constexpr int kMfmaThreads = 512;  // threads per workgroup (8 waves)
+constexpr int kMfmaWaves = kMfmaThreads / 64;
+constexpr int kQfBlocks = 4;       // blocks whose rotated queries are held in LDS at once
+constexpr int kFusedMaxRows = 32;  // stacked rows of the fused kernel
+
+// Per-call arrays of the fused kernel, passed in the kernel arguments and read
+// at kernel start with one load per array element per thread.
+struct alignas(16) DecodeTables {
+  int64_t block_start[HW_MAX_BLOCKS];
+  int32_t block_cap[HW_MAX_BLOCKS];
+  double inv_freq[kMaxHalf];     // theta^(-2i/D), i < D/2
+  uint64_t rope_frac[kMaxHalf];  // frac(theta^(-2i/D) / (2 pi)) * 2^64, i < D/2
+  float k_scale[HW_MAX_FP8_KV_HEADS];  // FP8 pools: this layer's scales per kv head
+  float v_scale[HW_MAX_FP8_KV_HEADS];
+};
+
+struct alignas(16) DecodeArgs {
+  const void* q;            // [W * nq][Hq][D] bf16
+  const void* k;            // plane of (layer, kv head 0)
+  const void* v;
+  const int32_t* block_len; // [NB]
+  const hw_entry* tables;   // [W][E]
+  const int32_t* num_entries;
+  float* out;               // [W * nq][Hq][D]
+  int32_t* status;
+  float2* ws_ml;            // [Hkv][R][P] (m, l) partials
+  float* ws_acc;            // [Hkv][R][P][D] partial accumulators
+  uint32_t* ws_hint;        // [Hkv][P][kMfmaWaves] first tile (byte offset) of the last call
+  int64_t plane_elems;      // num_slots * D
+  int32_t plane_bytes;      // plane_elems * element size (< 2^31)
+  int32_t W, Hq, Hkv, G, R, E, NB, P, D;
+  int32_t nq;               // query tokens per worker; rows are (w*nq + j)*G + h
+  uint32_t mP, mE, mG, mGnq, mR;  // div_magic of P, E, G, G * nq and R (indices < 2^16)
+  int32_t dtype;            // HW_BF16 / HW_FP8
+  float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
+  double rP;                // 1 / P (rounded)
+  DecodeTables tab;
+};
+
+hipError_t launch_fused_mfma(const DecodeArgs& a, int grid, hipStream_t s);
+int fused_blocks_per_cu(int dtype, int D, int rows);
+
 // Launchers (hw_plan.hip, hw_decode.hip).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_run_valu(const RunArgs& a, hipStream_t s);

@@ -12,6 +12,12 @@ BF16_MAX_ABS, BF16_REL_L2 = 5e-3, 1e-2   # bf16 inputs, fp32 accumulation
 F32_REL = 1e-5                           # fp32 inputs
 
 
+# Entry point of Setup.decode: "decode" (hw_attn_decode: up to 32 stacked MFMA
+# rows take the kernel that builds its plan in-kernel) or "plan_run"
+# (hw_attn_plan + hw_attn_run: the plan kernel and the run kernels).
+API = "decode"
+
+
 def errors(got: np.ndarray, ref: np.ndarray):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -76,15 +82,23 @@ class Setup:
                                     self.tables, self.num_entries)
         self.ws = hw.alloc_workspace(self.pool, wl.W, wl.Hq)
 
-    def decode(self, layer=0, q=None, tables=None, num_entries=None):
+    def decode(self, layer=0, q=None, tables=None, num_entries=None, api=None):
+        """One attention call through the C ABI: hw_attn_decode (api "decode"), or
+        hw_attn_plan + hw_attn_run (api "plan_run"); the module's API by default."""
         wl = self.wl
+        api = API if api is None else api
         q = (self.q[layer] if q is None else q).to("cuda")
+        tables = self.tables if tables is None else tables
+        num_entries = self.num_entries if num_entries is None else num_entries
         out = torch.full((q.shape[0], wl.Hq, wl.D), float("nan"), device="cuda")
         if self.ws.numel() < hw.hw_attn_workspace_bytes(self.pool, q.shape[0], wl.Hq):
             self.ws = hw.alloc_workspace(self.pool, q.shape[0], wl.Hq)
-        hw.hw_attn_decode(self.pool, layer, q, self.tables if tables is None else tables,
-                          self.num_entries if num_entries is None else num_entries, wl.theta,
-                          out, self.ws)
+        if api == "plan_run":
+            plan = hw.alloc_plan(self.pool, q.shape[0], wl.Hq)
+            hw.hw_attn_plan(self.pool, tables, num_entries, plan, wl.Hq)
+            hw.hw_attn_run(self.pool, layer, q, plan, wl.theta, out, self.ws)
+        else:
+            hw.hw_attn_decode(self.pool, layer, q, tables, num_entries, wl.theta, out, self.ws)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 

@@ -122,10 +122,12 @@ def test_workspace_bytes(lib):
         assert lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4) < n
     finally:
         hw.hw_set_tuning(hw.PATH_AUTO, 0)
-    # at most one unit per tile the blocks can hold
+    # at most one unit per tile the blocks can hold: counters, plan, partials,
+    # tile counts and the fused kernel's first-tile hints (8 waves per unit),
+    # each region 256-byte aligned
     small = FakePool(caps=(64, 32, 32))
     assert lib.hw_attn_workspace_bytes(ctypes.byref(small.desc), 2, 4) <= \
-        16384 + 4 * (600 + 3 * 2) + 2 * 4 * 4 * (128 + 2) * 4 + 512
+        16384 + 4 * (600 + 3 * 2) + 2 * 4 * 4 * (128 + 2) * 4 + 2 * 4 * 4 + 2 * 4 * 8 * 4 + 4 * 256
     # plans: 600 header words + one row end per (block, query row)
     assert lib.hw_attn_plan_bytes(ctypes.byref(pool.desc), 2, 1, 4) == 4 * (600 + 3 * 2)
     assert lib.hw_attn_plan_bytes(ctypes.byref(pool.desc), 2, 5, 4) == 4 * (600 + 3 * 10)

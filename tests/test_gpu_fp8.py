@@ -20,6 +20,8 @@ from hw_harness import Setup, assert_close, errors
 pytestmark = pytest.mark.gpu
 
 FP8 = torch.float8_e4m3fn
+# hw_attn_decode (in-kernel plan up to 32 rows) and hw_attn_plan + hw_attn_run
+APIS = ["decode", "plan_run"]
 
 
 def _say(msg):
@@ -40,12 +42,13 @@ def _custom(W, Hq, Hkv, D, lens, theta=1e6, caps=None, sigma=0.5, seed=7, layers
                               layers, list(lens), list(caps), sigma, seed)
 
 
-def test_fp8_qwq_layer_matches_oracle():
+@pytest.mark.parametrize("api", APIS)
+def test_fp8_qwq_layer_matches_oracle(api):
     s = Setup(workloads.with_fp8(workloads.qwq_layer()))
     ref, rc = s.oracle_decode()
     assert rc == 0
-    got = s.decode()
-    ma, rl = assert_close(got, ref, FP8, "qwq layer fp8")
+    got = s.decode(api=api)
+    ma, rl = assert_close(got, ref, FP8, f"qwq layer fp8 {api}")
     # informational: the distance to attention over the unquantized bf16 pool
     sb = Setup(workloads.qwq_layer())
     refb, _ = sb.oracle_decode()
@@ -64,20 +67,22 @@ def test_fp8_qwq_layer_matches_oracle():
     (12, 48, 8, 64, [900] + [33] * 12),  # 72 rows
     (16, 40, 8, 128, [700] + [9] * 16),  # 80 rows
 ])
-def test_fp8_ragged_shapes_match_oracle(case):
+@pytest.mark.parametrize("api", APIS)
+def test_fp8_ragged_shapes_match_oracle(case, api):
     W, Hq, Hkv, D, lens = case
     s = Setup(_custom(W, Hq, Hkv, D, lens), poison_unused=True)
     ref, rc = s.oracle_decode()
     assert rc == 0
-    got = s.decode()
+    got = s.decode(api=api)
     assert np.isfinite(got).all()
-    assert_close(got, ref, FP8, f"fp8 {case}")
+    assert_close(got, ref, FP8, f"fp8 {case} {api}")
     assert hw.hw_pool_status(s.pool) == 0
 
 
-def test_fp8_single_visible_token_returns_its_value():
+@pytest.mark.parametrize("api", APIS)
+def test_fp8_single_visible_token_returns_its_value(api):
     s = Setup(_custom(2, 4, 2, 128, [1, 0, 0]))
-    got = s.decode()
+    got = s.decode(api=api)
     V = s.V[0]
     for w in range(2):
         for h in range(4):
@@ -103,13 +108,15 @@ def test_fp8_chunk_matches_oracle():
     assert_close(out.cpu().numpy(), ref, FP8, "fp8 chunk")
 
 
-def test_fp8_unit_count_does_not_change_the_result():
+@pytest.mark.parametrize("api", APIS)
+def test_fp8_unit_count_does_not_change_the_result(api):
     s = Setup(_custom(4, 40, 8, 128, [3000, 100, 200, 64, 5]))
     ref, _ = s.oracle_decode()
     for units in (1, 3, 16, 64):
         hw.hw_set_tuning(hw.PATH_AUTO, units)
-        got = s.decode()
-        assert_close(got, ref, FP8, f"units {units}")
+        s.ws = hw.alloc_workspace(s.pool, 4, 40)
+        got = s.decode(api=api)
+        assert_close(got, ref, FP8, f"units {units} {api}")
 
 
 def test_fp8_append_matches_oracle_bit_exact():

@@ -13,11 +13,20 @@ import torch
 import oracle
 from decode_attention_shared_hw_amd import hogwild_attn as hw
 from decode_attention_shared_hw_amd import workloads
+import hw_harness
 from hw_harness import Setup, assert_close, errors
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [hw.PATH_VALU, hw.PATH_MFMA]
+# The MFMA path through both entry points: hw_attn_decode (the kernel with the
+# in-kernel plan, up to 32 rows) and hw_attn_plan + hw_attn_run (MFMA_RUN).
+MFMA_RUN = "mfma_plan_run"
+PATHS = [hw.PATH_VALU, hw.PATH_MFMA, MFMA_RUN]
+
+
+def _tune(path, units=0, balance=0):
+    hw_harness.API = "plan_run" if path == MFMA_RUN else "decode"
+    hw.hw_set_tuning(hw.PATH_MFMA if path == MFMA_RUN else path, units, balance)
 
 
 def _say(msg):
@@ -29,6 +38,7 @@ def _say(msg):
 def _tuning(request):
     _say(f"[case] {request.node.name}")
     yield
+    hw_harness.API = "decode"
     hw.hw_set_tuning(hw.PATH_AUTO, 0)
 
 
@@ -67,7 +77,7 @@ def test_tiny_fp32_matches_oracle_definition_form():
 
 @pytest.mark.parametrize("path", PATHS)
 def test_qwq_layer_bf16_matches_oracle(path):
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     s = Setup(workloads.qwq_layer())
     ref, rc = s.oracle_decode()
     assert rc == 0
@@ -92,7 +102,7 @@ def test_qwq_layer_bf16_matches_oracle(path):
 ])
 def test_ragged_shapes_match_oracle(path, case):
     W, Hq, Hkv, D, lens = case
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     wl = _custom(W, Hq, Hkv, D, lens)
     s = Setup(wl, poison_unused=True)
     ref, rc = s.oracle_decode()
@@ -104,10 +114,10 @@ def test_ragged_shapes_match_oracle(path, case):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_fp32_ragged_matches_oracle(path):
-    if path == hw.PATH_MFMA:
+    if path != hw.PATH_VALU:
         wl = _custom(2, 4, 2, 64, [40, 3, 9], dtype=torch.float32, theta=1e4, sigma=0.0)
         s = Setup(wl)
-        hw.hw_set_tuning(path, 0)
+        _tune(path, 0)
         assert hw.hw_attn_workspace_bytes(s.pool, 2, 4) == 0
         q = s.q[0].cuda()
         out = torch.zeros(2, 4, 64, device="cuda")
@@ -125,7 +135,7 @@ def test_fp32_ragged_matches_oracle(path):
 # ------------------------------------------------------------- invariants
 @pytest.mark.parametrize("path", PATHS)
 def test_single_visible_token_returns_value_exactly(path):
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     wl = _custom(2, 4, 2, 128, [1, 0, 0], seed=3)
     s = Setup(wl, poison_unused=True)
     got = s.decode()
@@ -142,7 +152,7 @@ def test_unit_spanning_many_blocks(path, units):
     # the rotated queries are built for several groups of blocks in turn
     # inside one workgroup
     wl = _custom(16, 2, 1, 128, [40] + [3] * 12 + [0, 33, 1, 64])
-    hw.hw_set_tuning(path, units)
+    _tune(path, units)
     s = Setup(wl, poison_unused=True)
     ref, rc = s.oracle_decode()
     assert rc == 0
@@ -157,7 +167,7 @@ def test_unit_count_does_not_change_the_result(path):
     s = Setup(wl)
     outs = []
     for units in (1, 3, 16, 64):
-        hw.hw_set_tuning(path, units)
+        _tune(path, units)
         s.ws = hw.alloc_workspace(s.pool, wl.W, wl.Hq)
         outs.append(s.decode())
     ref, _ = s.oracle_decode()
@@ -171,12 +181,12 @@ def test_unit_count_does_not_change_the_result(path):
 def test_deterministic_across_runs(path):
     """Static tile ranges (balance 0): bitwise the same result on every run; balanced
     tile order: the same result within rounding, and both match the oracle."""
-    hw.hw_set_tuning(path, 0, 0)
+    _tune(path, 0, 0)
     s = Setup(workloads.qwq_layer())
     a = s.decode()
     b = s.decode()
     assert np.array_equal(a, b)
-    hw.hw_set_tuning(path, 0, 1)
+    _tune(path, 0, 1)
     c = s.decode()
     d = s.decode()
     assert np.abs(c - a).max() < 1e-4 and np.abs(d - a).max() < 1e-4
@@ -187,7 +197,7 @@ def test_deterministic_across_runs(path):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_batched_workers_equal_single_worker_calls(path):
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     wl = _custom(4, 16, 4, 128, [500, 40, 90, 3, 77])
     s = Setup(wl)
     full = s.decode()
@@ -201,7 +211,7 @@ def test_batched_workers_equal_single_worker_calls(path):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_partial_visibility_and_entry_order(path):
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     wl = _custom(3, 6, 2, 64, [120, 50, 60, 70])
     s = Setup(wl)
     # worker 0: only common and its own block; worker 1: reversed order of entries;
@@ -218,13 +228,14 @@ def test_partial_visibility_and_entry_order(path):
 
 
 # ------------------------------------------------------- device error paths
-def test_bad_table_entry_sets_status_and_zeroes_that_worker():
+@pytest.mark.parametrize("api", ["decode", "plan_run"])
+def test_bad_table_entry_sets_status_and_zeroes_that_worker(api):
     wl = _custom(2, 4, 2, 64, [64, 32, 32])
     s = Setup(wl)
     hw.hw_pool_status(s.pool, clear=True)
     tables = s.tables.clone()
     tables[1, 1, 0] = 99  # block id out of range for worker 1
-    got = s.decode(tables=tables)
+    got = s.decode(tables=tables, api=api)
     flags = hw.hw_pool_status(s.pool, clear=True)
     assert flags & hw.HW_DEV_BAD_ENTRY
     assert (got[1] == 0).all()
@@ -232,20 +243,22 @@ def test_bad_table_entry_sets_status_and_zeroes_that_worker():
     assert_close(got[0], ref[0], torch.bfloat16, "healthy worker")
 
 
-def test_length_beyond_capacity_sets_status():
+@pytest.mark.parametrize("api", ["decode", "plan_run"])
+def test_length_beyond_capacity_sets_status(api):
     wl = _custom(1, 2, 2, 64, [64, 32])
     s = Setup(wl)
     hw.hw_pool_status(s.pool, clear=True)
     s.pool.set_lengths([64, 33])  # capacity of block 1 is 32
-    s.decode()
+    s.decode(api=api)
     assert hw.hw_pool_status(s.pool, clear=True) & hw.HW_DEV_BAD_LENGTH
 
 
-def test_worker_without_tokens_gets_zeros_and_status():
+@pytest.mark.parametrize("api", ["decode", "plan_run"])
+def test_worker_without_tokens_gets_zeros_and_status(api):
     wl = _custom(2, 4, 2, 64, [0, 0, 0])
     s = Setup(wl)
     hw.hw_pool_status(s.pool, clear=True)
-    got = s.decode()
+    got = s.decode(api=api)
     assert (got == 0).all()
     assert hw.hw_pool_status(s.pool, clear=True) & hw.HW_DEV_NO_TOKENS
 
@@ -372,7 +385,7 @@ def test_view_tables_match_oracle(layout, W):
 
 @pytest.mark.parametrize("path", PATHS)
 def test_interleaved_layout_attention_matches_oracle(path):
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     wl = _custom(4, 40, 8, 128, [3000, 500, 77, 300, 129])
     s = Setup(wl, poison_unused=True)
     hw.hw_build_view_tables(s.pool, hw.HW_LAYOUT_INTERLEAVED, wl.W, 0, wl.worker_block, s.tables,
@@ -398,7 +411,7 @@ def test_interleaved_layout_attention_matches_oracle(path):
 ])
 def test_chunk_matches_oracle(path, case):
     W, n, Hq, Hkv, D, lens = case
-    hw.hw_set_tuning(path, 0)
+    _tune(path, 0)
     wl = _custom(W, Hq, Hkv, D, lens)
     if path == hw.PATH_VALU and W * n * (Hq // Hkv) > 64:
         pytest.skip("the VALU kernel holds at most 64 rows")
@@ -407,7 +420,12 @@ def test_chunk_matches_oracle(path, case):
     q = torch.randn(W, n, Hq, D, generator=g).to(wl.dtype)
     out = torch.full((W, n, Hq, D), float("nan"), device="cuda")
     ws = hw.alloc_workspace(s.pool, W * n, Hq)
-    hw.hw_attn_chunk(s.pool, 0, q.cuda(), s.tables, s.num_entries, wl.theta, out, ws)
+    if path == MFMA_RUN:
+        plan = hw.alloc_plan(s.pool, W, Hq, chunk=n)
+        hw.hw_attn_plan(s.pool, s.tables, s.num_entries, plan, Hq, chunk=n)
+        hw.hw_attn_run(s.pool, 0, q.cuda(), plan, wl.theta, out, ws)
+    else:
+        hw.hw_attn_chunk(s.pool, 0, q.cuda(), s.tables, s.num_entries, wl.theta, out, ws)
     torch.cuda.synchronize()
     tb, to, ne = s.oracle_tables()
     ref, rc = oracle.attn_chunk(oracle.FORM_METHOD, q.double().numpy(), s.K[0].double().numpy(),
