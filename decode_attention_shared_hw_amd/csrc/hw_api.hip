@@ -11,6 +11,29 @@
 namespace hw {
 namespace {
 
+// Workspace of hw_attn_decode_noalloc: one array per GPU, held from the
+// library's load until the process ends.  Host code uses its device address
+// (scratch_address), never the name: on the host the name is a stand-in.
+constexpr size_t kScratchBytes = HW_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];  // per device, from hipGetSymbolAddress on its first call
+
+// The device address of the current device's scratch, looked up once per
+// device with that device current.
+hw_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return HW_EHIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HW_EHIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return HW_OK;
+}
+
 int g_path = 0;            // 0 auto, 1 VALU, 2 MFMA
 int g_units_per_head = 0;  // 0 automatic
 int g_balance = 0;         // 1: balanced tile order in the split launch
@@ -236,9 +259,11 @@ hw_status plan_call(const hw_pool* pool, const Shape& s, const hw_entry* tables,
   return launch_plan(a, stream) == hipSuccess ? HW_OK : HW_EHIP;
 }
 
+// balance: 1 for the balanced tile order (tiles after each wave's first from
+// the head's counter in the workspace), 0 for fixed tile ranges.
 hw_status run_call(const hw_pool* pool, int32_t layer, const void* q, const Shape& s,
                    const void* plan, size_t pbytes, double theta, float* out, void* workspace,
-                   size_t ws_bytes, hipStream_t stream) {
+                   size_t ws_bytes, hipStream_t stream, int balance) {
   if (!q || !out || !plan) return HW_EINVAL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(plan)) return HW_EINVAL;
   if (layer < 0 || layer >= pool->num_layers) return HW_EINVAL;
@@ -281,7 +306,7 @@ hw_status run_call(const hw_pool* pool, int32_t layer, const void* q, const Shap
   a.mHkv = div_magic(static_cast<uint32_t>(a.Hkv));
   a.mR = div_magic(static_cast<uint32_t>(s.R));
   a.mP = div_magic(static_cast<uint32_t>(s.P));
-  a.balance = g_balance;
+  a.balance = balance;
   a.dtype = pool->dtype;
   a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
   rope_tables(theta, pool->head_dim, a.inv_freq, a.rope_frac);
@@ -454,13 +479,14 @@ hw_status hw_attn_run(const hw_pool* pool, int32_t layer, const void* q, int32_t
   st = call_shape(pool, num_workers, chunk, num_q_heads, &s);
   if (st != HW_OK) return st;
   return run_call(pool, layer, q, s, plan, plan_bytes_, rope_theta, out, workspace,
-                  workspace_bytes, static_cast<hipStream_t>(stream));
+                  workspace_bytes, static_cast<hipStream_t>(stream), g_balance);
 }
 
 static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
                            int32_t nq, int32_t num_q_heads, const hw_entry* tables,
                            int32_t max_entries, const int32_t* num_entries, double rope_theta,
-                           float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                           float* out, void* workspace, size_t workspace_bytes, void* stream,
+                           int balance) {
   hw_status st = check_pool(pool);
   if (st != HW_OK) return st;
   Shape s;
@@ -485,7 +511,8 @@ static hw_status attn_call(const hw_pool* pool, int32_t layer, const void* q, in
   const size_t pb = wl.ml_off - wl.plan_off;
   st = plan_call(pool, s, tables, max_entries, num_entries, plan, pb, hs);
   if (st != HW_OK) return st;
-  return run_call(pool, layer, q, s, plan, pb, rope_theta, out, workspace, workspace_bytes, hs);
+  return run_call(pool, layer, q, s, plan, pb, rope_theta, out, workspace, workspace_bytes, hs,
+                  balance);
 }
 
 hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
@@ -493,7 +520,7 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
                          const int32_t* num_entries, double rope_theta, float* out,
                          void* workspace, size_t workspace_bytes, void* stream) {
   return attn_call(pool, layer, q, num_workers, 1, num_q_heads, tables, max_entries, num_entries,
-                   rope_theta, out, workspace, workspace_bytes, stream);
+                   rope_theta, out, workspace, workspace_bytes, stream, g_balance);
 }
 
 hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32_t num_workers,
@@ -502,7 +529,26 @@ hw_status hw_attn_chunk(const hw_pool* pool, int32_t layer, const void* q, int32
                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (chunk < 1 || chunk > HW_MAX_ROWS) return HW_ERANGE;
   return attn_call(pool, layer, q, num_workers, chunk, num_q_heads, tables, max_entries,
-                   num_entries, rope_theta, out, workspace, workspace_bytes, stream);
+                   num_entries, rope_theta, out, workspace, workspace_bytes, stream, g_balance);
+}
+
+hw_status hw_attn_decode_noalloc(const hw_pool* pool, int32_t layer, const void* q,
+                                 int32_t num_workers, int32_t num_q_heads, const hw_entry* tables,
+                                 int32_t max_entries, const int32_t* num_entries,
+                                 double rope_theta, float* out, void* stream) {
+  hw_status st = check_pool(pool);
+  if (st != HW_OK) return st;
+  Shape s;
+  st = call_shape(pool, num_workers, 1, num_q_heads, &s);
+  if (st != HW_OK) return st;
+  // the call's workspace must fit the scratch (checked before any device call)
+  if (ws_layout(pool, s).total > kScratchBytes) return HW_ERANGE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != HW_OK) return st;
+  // fixed tile ranges: no region of the scratch has to start at zero
+  return attn_call(pool, layer, q, num_workers, 1, num_q_heads, tables, max_entries, num_entries,
+                   rope_theta, out, ws, kScratchBytes, stream, 0);
 }
 
 hw_status hw_block_append(const hw_pool* pool, int32_t src_block, int32_t dst_block,

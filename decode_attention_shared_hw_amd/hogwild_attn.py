@@ -66,7 +66,7 @@ def query_dtype(pool_dtype: torch.dtype) -> torch.dtype:
 
 EXPORTED = [
     "hw_abi_version", "hw_status_str", "hw_attn_plan_bytes", "hw_attn_plan", "hw_attn_run",
-    "hw_attn_workspace_bytes", "hw_attn_decode", "hw_attn_chunk",
+    "hw_attn_workspace_bytes", "hw_attn_decode", "hw_attn_decode_noalloc", "hw_attn_chunk",
     "hw_block_append", "hw_block_reset", "hw_block_advance", "hw_block_write",
     "hw_build_combined_tables", "hw_build_view_tables", "hw_pool_status", "hw_set_tuning",
 ]
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.hw_attn_workspace_bytes.argtypes = [PP, i32, i32]
         L.hw_attn_decode.restype = i32
         L.hw_attn_decode.argtypes = [PP, i32, P, i32, i32, P, i32, P, d, P, P, sz, P]
+        L.hw_attn_decode_noalloc.restype = i32
+        L.hw_attn_decode_noalloc.argtypes = [PP, i32, P, i32, i32, P, i32, P, d, P, P]
         L.hw_attn_chunk.restype = i32
         L.hw_attn_chunk.argtypes = [PP, i32, P, i32, i32, i32, P, i32, P, d, P, P, sz, P]
         L.hw_block_append.restype = i32
@@ -344,6 +346,28 @@ def hw_attn_decode(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor
                                 _ptr(out), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check(code, "hw_attn_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # HW_NOALLOC_SCRATCH_BYTES
+
+
+def hw_attn_decode_noalloc(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,
+                           num_entries: torch.Tensor, rope_theta: float, out: torch.Tensor,
+                           stream=None):
+    """hw_attn_decode with the library's static per-GPU scratch as its workspace: the
+    call allocates no device memory (neither here nor in the library).  Calls that may
+    overlap on one GPU race on the scratch."""
+    dev = pool.k.device
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q: expected [W][Hq][D]")
+    W, Hq, _ = q.shape
+    _expect(q, "q", query_dtype(pool.dtype), (W, Hq, pool.head_dim), dev)
+    _expect(out, "out", torch.float32, (W, Hq, pool.head_dim), dev)
+    _check_views(pool, tables, num_entries, W)
+    code = lib().hw_attn_decode_noalloc(ctypes.byref(pool.desc), int(layer), _ptr(q), W, Hq,
+                                        _ptr(tables), int(tables.shape[1]), _ptr(num_entries),
+                                        float(rope_theta), _ptr(out), _stream(stream))
+    _check(code, "hw_attn_decode_noalloc")
 
 
 def hw_attn_chunk(pool: Pool, layer: int, q: torch.Tensor, tables: torch.Tensor,

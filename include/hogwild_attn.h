@@ -263,6 +263,25 @@ hw_status hw_attn_decode(const hw_pool* pool, int32_t layer, const void* q, int3
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hw_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation).  The call's workspace is a static array of
+ * HW_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the
+ * process ends; the call allocates nothing and always uses the fixed tile
+ * order (bitwise the same result as hw_attn_decode with balance 0).
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap
+ * (on different streams) race and must be ordered by the caller.
+ * Errors as hw_attn_decode, and HW_ERANGE when the call's workspace
+ * (hw_attn_workspace_bytes(pool, num_workers, num_q_heads)) exceeds the
+ * scratch.
+ */
+#define HW_NOALLOC_SCRATCH_BYTES (16u << 20)
+hw_status hw_attn_decode_noalloc(const hw_pool* pool, int32_t layer, const void* q,
+                                 int32_t num_workers, int32_t num_q_heads, const hw_entry* tables,
+                                 int32_t max_entries, const int32_t* num_entries,
+                                 double rope_theta, float* out, void* stream);
+
+/*
  * Multi-token query chunk: every worker attends with its last `chunk` tokens
  * at once (a prompt injected into, or a header prefilled in, its own block,
  * whose K/V are already stored; key design 2's "\n\n + worker" header, key

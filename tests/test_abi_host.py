@@ -110,6 +110,23 @@ def test_decode_host_validation(lib):
         hw.hw_set_tuning(hw.PATH_AUTO, 0)
 
 
+def test_noalloc_host_validation(lib):
+    p = ctypes.c_void_p(0x5000)
+
+    def rc(pool, W, Hq):
+        return lib.hw_attn_decode_noalloc(ctypes.byref(pool.desc), 0, p, W, Hq, p, 3, p, 1e4, p,
+                                          None)
+    ok = FakePool()
+    assert rc(ok, 0, 4) == hw.HW_ERANGE
+    assert rc(ok, 2, 3) == hw.HW_EINVAL  # Hq % Hkv
+    assert rc(FakePool(D=96), 2, 4) == hw.HW_EUNSUPPORTED
+    # 1024 kv heads at one unit each and 80 stacked rows: ~42 MB of workspace,
+    # more than the static scratch; rejected before any device call
+    big = FakePool(Hkv=1024, caps=(32,))
+    assert lib.hw_attn_workspace_bytes(ctypes.byref(big.desc), 16, 5120) > hw.NOALLOC_SCRATCH_BYTES
+    assert rc(big, 16, 5120) == hw.HW_ERANGE
+
+
 def test_workspace_bytes(lib):
     pool = FakePool(caps=(4096, 32, 32))
     n = lib.hw_attn_workspace_bytes(ctypes.byref(pool.desc), 2, 4)
