@@ -328,43 +328,6 @@ def test_reset_block():
 
 
 # ------------------------------------------- full-size step (sampled outputs)
-def test_qwq_step_full_size_sampled():
-    """64-layer pool of the 16K / 4-worker step, outputs sampled against the oracle."""
-    wl = workloads.qwq_step()
-    pool = hw.Pool(wl.layers, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
-    pool.set_lengths(wl.lens)
-    sample_layers = [0, 31, 63]
-    host = {}
-    for layer in range(wl.layers):
-        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
-        pool.store_layer(layer, K, V)
-        if layer in sample_layers:
-            host[layer] = (K.cpu(), V.cpu(), workloads.make_q(wl, layer, device="cuda").cpu())
-        del K, V
-    tables = torch.zeros(wl.W, wl.W + 1, 2, dtype=torch.int32, device="cuda")
-    ne = torch.zeros(wl.W, dtype=torch.int32, device="cuda")
-    hw.hw_build_combined_tables(pool, wl.W, 0, wl.worker_block, tables, ne)
-    ws = hw.alloc_workspace(pool, wl.W, wl.Hq)
-    tb, to, one = oracle.build_combined_tables(0, wl.worker_block, wl.lens)
-    rng = np.random.default_rng(0)
-    for layer in sample_layers:
-        K, V, q = host[layer]
-        out = torch.empty(wl.W, wl.Hq, wl.D, device="cuda")
-        hw.hw_attn_decode(pool, layer, q.cuda(), tables, ne, wl.theta, out, ws)
-        got = out.cpu().numpy()
-        for _ in range(4):
-            w, h = int(rng.integers(wl.W)), int(rng.integers(wl.Hq))
-            g = h // wl.G
-            ref, rc = oracle.attn_one(oracle.FORM_METHOD, q[w, h].double().numpy(),
-                                      K[g].double().numpy(), V[g].double().numpy(), tb[w], to[w],
-                                      np.asarray(wl.lens, np.int32),
-                                      np.asarray(pool.block_start, np.int64), wl.theta)
-            assert rc == 0
-            ma, rl = errors(got[w, h], ref)
-            assert ma <= 5e-3 and rl <= 1e-2, (layer, w, h, ma, rl)
-    assert hw.hw_pool_status(pool) == 0
-
-
 # ------------------------------------------------------ cache layouts (NEXT-2)
 @pytest.mark.parametrize("layout", [hw.HW_LAYOUT_COMBINED, hw.HW_LAYOUT_INTERLEAVED,
                                     hw.HW_LAYOUT_CONTIGUOUS])
