@@ -299,12 +299,80 @@ def run_loop(args):
     return res
 
 
-def cpu_threads() -> int:
+def host_cpus() -> int:
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def cpu_threads() -> int:
+    """Threads of the CPU baseline: the host CPUs this process may use, at most 16
+    (the host share of one GPU on the machines this runs on)."""
+    return max(1, min(host_cpus(), 16))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _oracle_layer_seconds(wl, K, V, q, starts, threads):
+    """Wall time of every (worker, q-head) row of one layer with the fp64 oracle
+    (definition form) on `threads` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import oracle
+
+    tb, to, _ = oracle.build_combined_tables(wl.common_block, wl.worker_block, wl.lens)
+    lens = np.asarray(wl.lens, np.int32)
+    starts = np.asarray(starts, np.int64)
+    Kd, Vd, qd = K.double().numpy(), V.double().numpy(), q.double().numpy()
+
+    def one(pair):
+        w, h = pair
+        _, rc = oracle.attn_one(oracle.FORM_DEFINITION, qd[w, h], Kd[h // wl.G], Vd[h // wl.G],
+                                tb[w], to[w], lens, starts, wl.theta)
+        assert rc == 0
+
+    pairs = [(w, h) for w in range(wl.W) for h in range(wl.Hq)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, pairs))
+    return time.perf_counter() - t0
+
+
+def cpu_breadth(threads):
+    """The oracle on one layer of every other configuration (all rows): the tiny
+    fp32 layer, the QwQ single layer, the workers x context grid and a layer of
+    the generation loop at its initial 32K history."""
+    import numpy as np
+
+    from decode_attention_shared_hw_amd import workloads
+
+    cases = [("tiny_fp32_2w", workloads.tiny()), ("qwq32b_layer_bf16_2w", workloads.qwq_layer())]
+    cases += [(f"sweep_{C}_{W}w", workloads.sweep(C, W)) for C in (1024, 8192, 16384)
+              for W in (1, 2, 4)]
+    cases += [("qwen3_8b_loop_bf16_4w (layer 0, first step)", workloads.qwen3_loop())]
+    out = []
+    for name, wl in cases:
+        slots = max(sum(wl.caps), 32)
+        starts = np.cumsum([0] + list(wl.caps[:-1]))
+        K, V = workloads.make_kv(wl, 0, slots)
+        q = workloads.make_q(wl, 0)
+        sec = _oracle_layer_seconds(wl, K, V, q, starts, threads)
+        b = wl.algorithmic_bytes_per_layer()
+        out.append({"workload": name, "rows": wl.W * wl.Hq, "tokens": wl.tokens,
+                    "seconds_per_layer": sec, "worker_tokens_per_s_per_layer": wl.W / sec,
+                    "equivalent_gbs": b / sec / 1e9})
+    return out
 
 
 def cpu_baseline(wl, pool_block_start, K, V, q, pairs):
@@ -343,6 +411,7 @@ def cpu_baseline(wl, pool_block_start, K, V, q, pairs):
     with ThreadPoolExecutor(max_workers=n) as ex:
         list(ex.map(one, all_pairs))
     layer_s = time.perf_counter() - t0
+    b = wl.algorithmic_bytes_per_layer()
     return {
         "value": wl.W / layer_s, "unit": "worker-tokens/s per layer", "cores": n,
         "kind": "oracle",
@@ -350,7 +419,12 @@ def cpu_baseline(wl, pool_block_start, K, V, q, pairs):
                   f"({wl.tokens} tokens each) on {n} threads in {layer_s:.1f} s; single thread: "
                   f"{len(sample)} pairs in {dt1:.1f} s, scaled to the layer",
         "seconds_per_layer": layer_s,
+        "seconds_per_step": layer_s * wl.layers,
+        "equivalent_gbs": b / layer_s / 1e9,
         "value_1_thread": wl.W / layer_s1,
+        "cpu_model": cpu_model(), "host_cpus": host_cpus(),
+        "threads_note": "at most 16 threads: the host share of one GPU",
+        "other_configs": cpu_breadth(n),
     }
 
 
@@ -577,7 +651,6 @@ def main():
         K0, V0 = host_layer0
         result["cpu_baseline"] = cpu_baseline(wl, pool.block_start, K0, V0, q[0].cpu(),
                                               args.cpu_pairs)
-        result["cpu_baseline"]["host"] = platform.processor() or platform.machine()
     if not args.no_fp8 and path != hw.PATH_VALU:
         # the same step over an FP8 E4M3 pool (half the K/V bytes; a separate
         # numerics contract: bf16 queries, codes widened exactly)

@@ -2,6 +2,7 @@
 // geometry, workspace layout.  Every host-visible error is returned before
 // anything is enqueued.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -326,6 +327,18 @@ hw_status run_call(const hw_pool* pool, int32_t layer, const void* q, const Shap
   return e == hipSuccess ? HW_OK : HW_EHIP;
 }
 
+// Polls before a wait between the waves of a work unit gives up: 2^22 (about
+// 0.25 s), or HW_SPIN_LIMIT from the environment (tests force the limit).
+uint32_t spin_limit() {
+  const char* e = getenv("HW_SPIN_LIMIT");
+  if (e && *e) {
+    char* end = nullptr;
+    const unsigned long long v = strtoull(e, &end, 10);
+    if (end && *end == 0) return v > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(v);
+  }
+  return 1u << 22;
+}
+
 // Split launch with the plan built in-kernel (hw_fused.hip), then the merge.
 // The caller has validated the shape, the pointers and the workspace.
 hw_status fused_call(const hw_pool* pool, int32_t layer, const void* q, const Shape& s,
@@ -368,6 +381,7 @@ hw_status fused_call(const hw_pool* pool, int32_t layer, const void* q, const Sh
   a.mG = div_magic(static_cast<uint32_t>(a.G));
   a.mGnq = div_magic(static_cast<uint32_t>(a.G * a.nq));
   a.mR = div_magic(static_cast<uint32_t>(a.R));
+  a.spin_limit = spin_limit();
   a.qscale = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(pool->head_dim)));
   for (int b = 0; b < pool->num_blocks; ++b) {
     a.tab.block_start[b] = pool->block_start[b];

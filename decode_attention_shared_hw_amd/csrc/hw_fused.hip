@@ -234,7 +234,8 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
 #pragma unroll 1
       for (uint32_t m = vis; m != 0u; m &= m - 1u) {
         const int w = __builtin_ctz(m);
-        atomicMax(&p.iq[w], static_cast<long long>(p.off[w * a.NB + b]) + len - 1);
+        if (w < a.W)  // (always, unless a wait gave up and the mask is half built)
+          atomicMax(&p.iq[w], static_cast<long long>(p.off[w * a.NB + b]) + len - 1);
       }
     }
   }
@@ -253,26 +254,57 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
 // and the wave waits until the counter reaches count * phase.  The counter
 // only grows; it must be zero before the first phase.  Every wave of the
 // group reaches every phase (no early exits), so every wait ends.
+//
+// Every wait between waves is bounded: after `limit` polls (the argument
+// spin_limit, 2^22 by default: about 0.25 s, against microseconds for any
+// wait of a healthy launch) the wave stops waiting and sets the workgroup's
+// abort word.  A wave uses the plan only after a wait that either succeeded
+// (and so is ordered after any abort set before the waited-for arrivals) or
+// set the abort itself, and checks the word first: an aborted workgroup
+// loads no tile through a plan offset, stores its partial from its own
+// (head, unit) and reports HW_DEV_SPIN_LIMIT, so a lost arrival ends the
+// launch with a flagged wrong result instead of a hang or a stray access.
 struct LdsWaveBarrier {
   uint32_t* ctr;
   uint32_t count;
   uint32_t phase;
+  uint32_t* abort_word;
+  uint32_t limit;
   __device__ void operator()() {
     ++phase;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if ((threadIdx.x & 63) == 0)
       __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count * phase)
+    for (uint32_t n = 0;
+         __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count * phase;
+         ++n) {
+      if (n >= limit) {
+        __hip_atomic_fetch_or(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
 };
 
-// Waits until an LDS counter that other waves advance reaches `target`.
-__device__ __forceinline__ void lds_wait_at_least(uint32_t* ctr, uint32_t target) {
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+// Waits until an LDS counter that other waves advance reaches `target`, at
+// most `limit` polls (then sets the abort word, as above).
+__device__ __forceinline__ void lds_wait_at_least(uint32_t* ctr, uint32_t target,
+                                                  uint32_t* abort_word, uint32_t limit) {
+  for (uint32_t n = 0;
+       __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target; ++n) {
+    if (n >= limit) {
+      __hip_atomic_fetch_or(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
+  }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ bool spin_aborted(uint32_t* abort_word) {
+  return __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u;
 }
 
 // Block holding global tile j of the plan (cursor walks forward).
@@ -282,10 +314,6 @@ __device__ __forceinline__ int block_of_tile(const Plan& p, int nb, int j, int b
 }
 
 // Per-unit partial: (m, l) per row and the unnormalised accumulator.
-__device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, const Plan& p) {
-  return static_cast<int64_t>(p.head) * a.R * a.P + p.unit;
-}
-
 // ------------------------------------------------------------- MFMA kernel
 struct TileRef {
   int b;          // block
@@ -376,8 +404,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int NF = kFront * 64;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const bool front = wave_u < kFront;  // wave-uniform: one side of each branch per wave
-  __shared__ uint32_t sync_ctr[3];  // front barrier, front loads issued, rotation done
-  if (tid < 3) sync_ctr[tid] = 0u;
+  // front barrier, front loads issued, rotation done, abort word
+  __shared__ uint32_t sync_ctr[4];
+  if (tid < 4) sync_ctr[tid] = 0u;
+  uint32_t* const spin_abort = &sync_ctr[3];
   // publishes the zeroed counters; each wave passes it once, the front waves
   // right after requesting the plan's loads, the back waves first
   auto init_barrier = [] {
@@ -411,7 +441,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   };
   uint32_t spec = 0xffffffffu;  // back waves: the hinted first tile
   Frag kf[2][KS], vf[MT];
-  LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u};
+  LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u, spin_abort, a.spin_limit};
   if (front) {
     u32x4 qv[kQRegs];
     auto issue = [&] {
@@ -447,7 +477,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     const uint32_t hv = *hint;  // (loaded by the back waves only)
     init_barrier();
     spec = __builtin_amdgcn_readfirstlane(hv);
-    lds_wait_at_least(&sync_ctr[1], kFront);
+    lds_wait_at_least(&sync_ctr[1], kFront, spin_abort, a.spin_limit);
     load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
   }
   bool rowvis[NT];
@@ -526,7 +556,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   uint32_t first = 0xffffffffu;  // this wave's first tile (byte offset), none: all ones
   // the first group's rotation (front waves), published to the back waves
   if (front) {
-    if (plan.lo < plan.hi) {
+    if (plan.lo < plan.hi && !spin_aborted(spin_abort)) {
       const int b_first = plan.b_first;
       const int b_last = plan.b_last;
       rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NF);
@@ -535,9 +565,9 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     if (lane == 0)
       __hip_atomic_fetch_add(&sync_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
-    lds_wait_at_least(&sync_ctr[2], kFront);
+    lds_wait_at_least(&sync_ctr[2], kFront, spin_abort, a.spin_limit);
   }
-  if (plan.lo < plan.hi) {
+  if (plan.lo < plan.hi && !spin_aborted(spin_abort)) {
     const int b_first = plan.b_first;
     const int b_last = plan.b_last;
     for (int gb = b_first; gb <= b_last; gb += kQfBlocks) {
@@ -633,7 +663,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
         *reinterpret_cast<f32x4*>(buf + r * ACC_STRIDE + 16 * m + 4 * q4) = acc[m][t];
     }
   };
-  const int64_t pu = partial_index(a, plan);
+  const int64_t pu = static_cast<int64_t>(h0) * a.R * a.P + u0;  // (not from the plan)
   auto combine_store = [&](auto nstate_c, int state, int rc) {
     constexpr int NS = decltype(nstate_c)::value;
     // 8 outputs per item: R * D / 8 items (320 at 20 rows), one per thread
@@ -697,7 +727,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     combine_store(std::integral_constant<int, NSTATE>{}, kState2, RP);
   }
   if (lane == 0) *hint = first;
-  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
+  if (tid == 0) {
+    const int32_t f = plan.flags | (spin_aborted(spin_abort) ? HW_DEV_SPIN_LIMIT : 0);
+    if (f) atomicOr(a.status, f);
+  }
   if (lane == 0) HW_STAMP(16 + wave);
 }
 

@@ -163,6 +163,7 @@ struct alignas(16) DecodeArgs {
   int32_t dtype;            // HW_BF16 / HW_FP8
   float qscale;             // log2(e) / sqrt(D): scores in the exp2 domain
   double rP;                // 1 / P (rounded)
+  uint32_t spin_limit;      // polls before a wait between waves gives up
   DecodeTables tab;
 };
 

@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(_PKG, "libhogwild_attn.so")
 
 HW_OK, HW_EINVAL, HW_ERANGE, HW_ECAPACITY, HW_EUNSUPPORTED, HW_EWORKSPACE, HW_EHIP = range(7)
 HW_DEV_BAD_ENTRY, HW_DEV_BAD_LENGTH, HW_DEV_NO_TOKENS, HW_DEV_APPEND_OVERFLOW = 1, 2, 4, 8
-HW_DEV_WRITE_OVERFLOW, HW_DEV_STALE_PLAN, HW_DEV_WORKSPACE = 16, 32, 64
+HW_DEV_WRITE_OVERFLOW, HW_DEV_STALE_PLAN, HW_DEV_WORKSPACE, HW_DEV_SPIN_LIMIT = 16, 32, 64, 128
 HW_F32, HW_BF16, HW_FP8 = 0, 1, 2
 HW_TILE_TOKENS = 32
+HW_ABI_VERSION = 3
+HW_MAX_BLOCKS, HW_MAX_WORKERS, HW_MAX_ROWS, HW_MAX_ENTRIES, HW_MAX_FP8_KV_HEADS = 64, 32, 80, 64, 64
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 HW_LAYOUT_COMBINED, HW_LAYOUT_INTERLEAVED, HW_LAYOUT_CONTIGUOUS = 0, 1, 2
 

@@ -85,6 +85,10 @@ typedef int32_t hw_status;
                                     block length changed since the plan was made                   */
 #define HW_DEV_WORKSPACE 64      /* a run's work units did not cover every tile exactly once: the
                                     workspace's counters were not zero when the call started       */
+#define HW_DEV_SPIN_LIMIT 128    /* a wait between the waves of one work unit of a decode call gave up
+                                    after its limit (about 0.25 s; HW_SPIN_LIMIT in the environment
+                                    sets it in polls, for tests): that unit skipped its tiles, so the
+                                    call's outputs are wrong, but the launch ended                 */
 
 /* Storage types. */
 #define HW_F32 0

@@ -43,6 +43,19 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(hw.EXPORTED)
 
 
+def test_header_constants_match_binding():
+    """Every #define of the header that the binding mirrors has the same value."""
+    src = open(os.path.join(ROOT, "include", "hogwild_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    defs = dict(re.findall(r"^#define\s+(HW_\w+)\s+(.+?)\s*$", src, flags=re.M))
+    value = lambda v: eval(re.sub(r"(\d)u\b", r"\1", v), {})  # noqa: E731
+    checked = [n for n in defs if hasattr(hw, n)]
+    for n in checked:
+        assert getattr(hw, n) == value(defs[n]), n
+    assert {"HW_DEV_SPIN_LIMIT", "HW_DEV_WORKSPACE", "HW_MAX_ROWS", "HW_TILE_TOKENS"} <= set(checked)
+    assert hw.NOALLOC_SCRATCH_BYTES == value(defs["HW_NOALLOC_SCRATCH_BYTES"])
+
+
 def test_abi_version_and_status_text(lib):
     assert hw.hw_abi_version() == 3
     assert hw.hw_status_str(hw.HW_OK) == "ok"

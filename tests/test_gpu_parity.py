@@ -228,6 +228,32 @@ def test_partial_visibility_and_entry_order(path):
 
 
 # ------------------------------------------------------- device error paths
+def test_spin_limit_ends_the_launch_and_reports(monkeypatch):
+    """The waits between the waves of a work unit are bounded.  Forced from the host
+    (HW_SPIN_LIMIT=0 polls: a wait not satisfied at its first poll gives up), every
+    launch still ends; a call either matches the oracle (all its waits happened to
+    be satisfied at once) or reports HW_DEV_SPIN_LIMIT.  At the default limit the
+    result is exact again and no bit is set."""
+    s = Setup(workloads.qwq_layer())
+    ref, rc = s.oracle_decode()
+    assert rc == 0
+    hw.hw_pool_status(s.pool, clear=True)
+    monkeypatch.setenv("HW_SPIN_LIMIT", "0")
+    hits = 0
+    for _ in range(5):
+        got = s.decode(api="decode")
+        flags = hw.hw_pool_status(s.pool, clear=True)
+        assert not np.isnan(got).any()
+        if flags & hw.HW_DEV_SPIN_LIMIT:
+            hits += 1
+        else:
+            assert_close(got, ref, torch.bfloat16, "zero spin limit, no wait gave up")
+    monkeypatch.delenv("HW_SPIN_LIMIT")
+    assert_close(s.decode(api="decode"), ref, torch.bfloat16, "default spin limit")
+    assert hw.hw_pool_status(s.pool) == 0
+    _say(f"  {hits} of 5 calls at a zero limit reported HW_DEV_SPIN_LIMIT")
+
+
 @pytest.mark.parametrize("api", ["decode", "plan_run"])
 def test_bad_table_entry_sets_status_and_zeroes_that_worker(api):
     wl = _custom(2, 4, 2, 64, [64, 32, 32])
