@@ -102,10 +102,6 @@ __device__ __forceinline__ void plan_entry(const DecodeArgs& a, Plan& p, int i, 
 // issue(): the kernel's own loads, issued with the plan's; commit(): their
 // LDS stores, run once they have arrived.  NTHR threads (the first NTHR of
 // the workgroup) take part; sync() is their barrier.
-struct WorkgroupBarrier {
-  __device__ void operator()() const { __syncthreads(); }
-};
-
 template <int NTHR, typename Issue, typename Commit, typename Sync>
 __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit, Sync& sync) {
   const int tid = threadIdx.x;
@@ -149,7 +145,6 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   }
   for (int i = tid; i < a.W * a.NB; i += NTHR) p.off[i] = 0;
   if (tid == 0) {
-    p.flags = 0;
     p.bad_workers = 0u;
     plan_head_unit(a, &p.head, &p.unit);
   }
@@ -242,12 +237,6 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
   sync();
 }
 
-template <int NTHR, typename Issue, typename Commit>
-__device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit commit) {
-  WorkgroupBarrier sync;
-  build_plan<NTHR>(a, p, issue, commit, sync);
-}
-
 // Waves of one workgroup that synchronize through a counter in LDS instead of
 // s_barrier, so that the other waves of the workgroup never have to join:
 // each wave's LDS writes complete (release fence on LDS), lane 0 adds one,
@@ -257,10 +246,10 @@ __device__ void build_plan(const DecodeArgs& a, Plan& p, Issue issue, Commit com
 //
 // Every wait between waves is bounded: after `limit` polls (the argument
 // spin_limit, 2^22 by default: about 0.25 s, against microseconds for any
-// wait of a healthy launch) the wave stops waiting and sets the workgroup's
-// abort word.  A wave uses the plan only after a wait that either succeeded
-// (and so is ordered after any abort set before the waited-for arrivals) or
-// set the abort itself, and checks the word first: an aborted workgroup
+// wait of a healthy launch) the wave stops waiting and sets HW_DEV_SPIN_LIMIT
+// in the plan's flags.  A wave uses the plan only after a wait that either
+// succeeded (and so is ordered after any bit set before the waited-for
+// arrivals) or set the bit itself, and checks the bit first: an aborted workgroup
 // loads no tile through a plan offset, stores its partial from its own
 // (head, unit) and reports HW_DEV_SPIN_LIMIT, so a lost arrival ends the
 // launch with a flagged wrong result instead of a hang or a stray access.
@@ -268,18 +257,18 @@ struct LdsWaveBarrier {
   uint32_t* ctr;
   uint32_t count;
   uint32_t phase;
-  uint32_t* abort_word;
+  int32_t* flags;  // the plan's HW_DEV_* bits (HW_DEV_SPIN_LIMIT when a wait gives up)
   uint32_t limit;
   __device__ void operator()() {
     ++phase;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if ((threadIdx.x & 63) == 0)
       __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (uint32_t n = 0;
-         __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count * phase;
-         ++n) {
-      if (n >= limit) {
-        __hip_atomic_fetch_or(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    uint32_t left = limit;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < count * phase) {
+      if (left-- == 0u) {
+        __hip_atomic_fetch_or(flags, HW_DEV_SPIN_LIMIT, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_WORKGROUP);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -289,22 +278,19 @@ struct LdsWaveBarrier {
 };
 
 // Waits until an LDS counter that other waves advance reaches `target`, at
-// most `limit` polls (then sets the abort word, as above).
-__device__ __forceinline__ void lds_wait_at_least(uint32_t* ctr, uint32_t target,
-                                                  uint32_t* abort_word, uint32_t limit) {
-  for (uint32_t n = 0;
-       __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target; ++n) {
-    if (n >= limit) {
-      __hip_atomic_fetch_or(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// most `limit` polls (then records HW_DEV_SPIN_LIMIT, as above).
+__device__ __forceinline__ void lds_wait_at_least(uint32_t* ctr, uint32_t target, int32_t* flags,
+                                                  uint32_t limit) {
+  uint32_t left = limit;
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    if (left-- == 0u) {
+      __hip_atomic_fetch_or(flags, HW_DEV_SPIN_LIMIT, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ bool spin_aborted(uint32_t* abort_word) {
-  return __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u;
 }
 
 // Block holding global tile j of the plan (cursor walks forward).
@@ -404,10 +390,11 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int NF = kFront * 64;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const bool front = wave_u < kFront;  // wave-uniform: one side of each branch per wave
-  // front barrier, front loads issued, rotation done, abort word
-  __shared__ uint32_t sync_ctr[4];
-  if (tid < 4) sync_ctr[tid] = 0u;
-  uint32_t* const spin_abort = &sync_ctr[3];
+  __shared__ uint32_t sync_ctr[3];  // front barrier, front loads issued, rotation done
+  // (with the plan's flags, in one store: zeroed before the barrier that every
+  // wave passes once, so a wave that gives up a later wait records
+  // HW_DEV_SPIN_LIMIT there)
+  if (tid < 4) *(tid < 3 ? &sync_ctr[tid] : reinterpret_cast<uint32_t*>(&plan.flags)) = 0u;
   // publishes the zeroed counters; each wave passes it once, the front waves
   // right after requesting the plan's loads, the back waves first
   auto init_barrier = [] {
@@ -441,7 +428,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   };
   uint32_t spec = 0xffffffffu;  // back waves: the hinted first tile
   Frag kf[2][KS], vf[MT];
-  LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u, spin_abort, a.spin_limit};
+  LdsWaveBarrier front_sync{&sync_ctr[0], kFront, 0u, &plan.flags, a.spin_limit};
   if (front) {
     u32x4 qv[kQRegs];
     auto issue = [&] {
@@ -477,7 +464,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     const uint32_t hv = *hint;  // (loaded by the back waves only)
     init_barrier();
     spec = __builtin_amdgcn_readfirstlane(hv);
-    lds_wait_at_least(&sync_ctr[1], kFront, spin_abort, a.spin_limit);
+    lds_wait_at_least(&sync_ctr[1], kFront, &plan.flags, a.spin_limit);
     load_tile_checked<D, E>(krs, vrs, spec, koff, voff, kf, vf);
   }
   bool rowvis[NT];
@@ -556,7 +543,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   uint32_t first = 0xffffffffu;  // this wave's first tile (byte offset), none: all ones
   // the first group's rotation (front waves), published to the back waves
   if (front) {
-    if (plan.lo < plan.hi && !spin_aborted(spin_abort)) {
+    if (plan.lo < plan.hi && !(plan.flags & HW_DEV_SPIN_LIMIT)) {
       const int b_first = plan.b_first;
       const int b_last = plan.b_last;
       rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NF);
@@ -565,9 +552,9 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     if (lane == 0)
       __hip_atomic_fetch_add(&sync_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
-    lds_wait_at_least(&sync_ctr[2], kFront, spin_abort, a.spin_limit);
+    lds_wait_at_least(&sync_ctr[2], kFront, &plan.flags, a.spin_limit);
   }
-  if (plan.lo < plan.hi && !spin_aborted(spin_abort)) {
+  if (plan.lo < plan.hi && !(plan.flags & HW_DEV_SPIN_LIMIT)) {
     const int b_first = plan.b_first;
     const int b_last = plan.b_last;
     for (int gb = b_first; gb <= b_last; gb += kQfBlocks) {
@@ -727,10 +714,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     combine_store(std::integral_constant<int, NSTATE>{}, kState2, RP);
   }
   if (lane == 0) *hint = first;
-  if (tid == 0) {
-    const int32_t f = plan.flags | (spin_aborted(spin_abort) ? HW_DEV_SPIN_LIMIT : 0);
-    if (f) atomicOr(a.status, f);
-  }
+  if (tid == 0 && plan.flags) atomicOr(a.status, plan.flags);
   if (lane == 0) HW_STAMP(16 + wave);
 }
 
