@@ -34,14 +34,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_qwq32b_step_hbm_traffic.md")
 
 
+# the sources a decode call's kernels and launch geometry come from (the
+# traffic summary stays valid while these are unchanged)
+DECODE_SOURCES = ("hw_api.hip", "hw_decode.hip", "hw_fused.hip", "hw_internal.h", "hw_kernels.h",
+                  "hw_plan.hip")
+
+
 def kernel_source_sha256() -> str:
     import glob
     import hashlib
 
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "decode_attention_shared_hw_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        if os.path.basename(f) in DECODE_SOURCES:
+            with open(f, "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()
 
 
@@ -80,10 +87,14 @@ def parse():
     ap.add_argument("--kernel-timing-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--config", choices=["step", "sweep", "loop"], default="step",
+    ap.add_argument("--config", choices=["step", "sweep", "loop", "cell", "chunk"],
+                    default="step",
                     help="step: the headline 64-layer step (default); sweep: context x workers "
                          "grid, per-layer time on both paths; loop: 36-layer generation loop "
-                         "with appends")
+                         "with appends; cell: one grid point (--context, --workers); chunk: "
+                         "one 80-row chunk call")
+    ap.add_argument("--context", type=int, default=16384, help="cell: visible context tokens")
+    ap.add_argument("--workers", type=int, default=4, help="cell: workers")
     ap.add_argument("--loop-steps", type=int, default=512)
     ap.add_argument("--api", choices=["decode", "plan_run"], default="decode",
                     help="decode: hw_attn_decode per layer (plan built in-kernel, the default); "
@@ -184,6 +195,49 @@ def run_sweep(args, paths=("mfma", "valu"), reps=20):
             "data": "synthetic, seeded", "points": points}
 
 
+def calibrate_copy(torch, mib):
+    """One plain device copy of `mib` MiB (bytes read = bytes written = mib MiB):
+    its HBM counters scale the decode kernels' counters in the same run."""
+    if mib <= 0:
+        return
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def run_cell(args, reps=10):
+    """One point of the workers x context grid (40 q / 8 kv heads, D 128, bf16):
+    per-layer time of hw_attn_decode in graph replay, cycling layers of distinct K/V."""
+    import torch
+
+    from decode_attention_shared_hw_amd import hogwild_attn as hw
+    from decode_attention_shared_hw_amd import workloads
+
+    wl = workloads.sweep(args.context, args.workers)
+    L = min(256, max(8, -(-2 * 256 * 2**20 // wl.kv_bytes_per_layer())))
+    wl.layers = L
+    pool = hw.Pool(L, wl.Hkv, wl.D, wl.caps, dtype=wl.dtype)
+    pool.set_lengths(wl.lens)
+    for layer in range(L):
+        K, V = workloads.make_kv(wl, layer, pool.num_slots, device="cuda")
+        pool.store_layer(layer, K, V)
+        del K, V
+    q = torch.stack([workloads.make_q(wl, layer, device="cuda") for layer in range(L)])
+    us = _graph_layers_us(hw, torch, pool, wl, q, reps=reps)
+    b = wl.algorithmic_bytes_per_layer()
+    res = {"config": "cell", "workload": wl.name, "context": args.context,
+           "workers": args.workers, "layers_cycled": L, "us_per_layer": us,
+           "algorithmic_bytes": b, "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "status": hw.hw_pool_status(pool)}
+    del pool, q
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_chunk(args, chunk=4, reps=10):
     """One chunk call (chunked prefill: each worker's last `chunk` tokens as
     queries, causal inside the chunk) at the QwQ heads, 4 workers, 16K context:
@@ -206,9 +260,12 @@ def run_chunk(args, chunk=4, reps=10):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(wl.seed + 21)
     q = torch.randn(L, wl.W, chunk, wl.Hq, wl.D, generator=gen, device="cuda").to(wl.q_dtype)
-    us = _graph_layers_us(hw, torch, pool, wl, q, reps=reps, chunk=chunk)
+    # the plan once per step (every layer's call has the same views), then one
+    # run per layer
+    us = _graph_layers_us(hw, torch, pool, wl, q, reps=reps, api="plan_run", chunk=chunk)
     b = wl.kv_bytes_per_layer() + wl.W * chunk * wl.Hq * wl.D * (q.element_size() + 4)
     res = {"workload": f"chunk_16384_4w_x{chunk}", "rows_per_kv_head": wl.W * chunk * wl.G,
+           "api": "hw_attn_plan once + hw_attn_run per layer",
            "kernel": "run_mfma<128,5,bf16> + merge_kernel<128>", "us_per_layer": us,
            "algorithmic_bytes": b, "achieved_gbs": b / (us * 1e-6) / 1e9,
            "frac_of_peak": b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "status": hw.hw_pool_status(pool)}
@@ -576,6 +633,14 @@ def main():
     if args.config == "loop":
         print(json.dumps(run_loop(args)), flush=True)
         return
+    if args.config == "cell":
+        res = run_cell(args)
+        calibrate_copy(torch, args.calibrate_copy)
+        print(json.dumps(res), flush=True)
+        return
+    if args.config == "chunk":
+        print(json.dumps(run_chunk(args)), flush=True)
+        return
     path = {"auto": hw.PATH_AUTO, "valu": hw.PATH_VALU, "mfma": hw.PATH_MFMA}[args.path]
     hw.hw_set_tuning(path, args.units, 1 if args.balance else 0)
 
@@ -583,16 +648,7 @@ def main():
     L, W = wl.layers, wl.W
     pool, q, host_layer0 = make_step_pool(hw, torch, workloads, wl, not args.no_cpu_baseline)
     t = time_step(args, hw, torch, np, wl, pool, q, api=args.api)
-    if args.calibrate_copy > 0:
-        # one plain copy of a known size: HBM counters of this dispatch scale
-        # the decode kernel's counters (bytes read = bytes written = MIB MiB)
-        n = args.calibrate_copy << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibrate_copy(torch, args.calibrate_copy)
 
     ms_per_step = t["ms_per_step"]
     step_s = ms_per_step / 1e3
