@@ -154,7 +154,7 @@ struct ChunkOf {
 // the run touches is rebuilt, keeping the tokens outside the run, and stored
 // whole.  FP8 pools: src and dst share the plane's scale, so the codes
 // themselves are rotated and rounded.
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma clang fp contract(off)
   typedef typename ChunkOf<T>::type Chunk;
@@ -164,22 +164,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   int lin = blockIdx.x;
   if (a.xcd_map) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int64_t plane = lin / a.tiles_per_plane;
-  const int k = lin - static_cast<int>(plane * a.tiles_per_plane);
+  const int k = lin - static_cast<int>(plane * a.tiles_per_plane);  // dst tile of the run
   if (plane >= a.planes) return;
   const int32_t ls = a.block_len[a.src];
   const int32_t ld = a.block_len[a.dst];
   if (ls <= 0 || ld < 0 || ls > a.cap_src || static_cast<int64_t>(ld) + ls > a.cap_dst) return;
   const int64_t first = a.start_dst + ld;  // first destination slot
   const int64_t last = first + ls;
-  const int64_t t0 = ((first >> 5) + k) << 5;  // this dst tile's first slot
+  const int64_t t0 = ((first >> 5) + k) << 5;  // the dst tile's first slot
   const int64_t s_begin = first > t0 ? first : t0;
   const int64_t s_end = last < t0 + 32 ? last : t0 + 32;
-  if (s_begin >= s_end) return;
-  const int D = a.D, half = D / 2;
-  const int n = static_cast<int>(s_end - s_begin);
-  const int64_t ss0 = a.start_src + (s_begin - first);  // src slot of the first token
+  if (s_begin >= s_end) return;  // the run ends before this tile
+  // (D a template parameter: the chunk index arithmetic below is shifts and masks)
+  constexpr int half = D / 2;
   __shared__ double cs[2 * kMaxHalf];
-  __shared__ T vstage[32 * 128];  // run values, [token - s_begin][dim]
+  __shared__ T vstage[32 * D];  // run values, [token - s_begin][dim]
   if (tid < half) {
     double s, c;
     sincos(static_cast<double>(ld) * a.inv_freq[tid], &s, &c);
@@ -188,27 +187,33 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
   T* kp = static_cast<T*>(a.k) + plane * a.plane_elems;
   T* vp = static_cast<T*>(a.v) + plane * a.plane_elems;
+  constexpr int cpt = 32 * D / kChunk;  // chunks per tile
+  constexpr int cph = half / kChunk;    // key chunks per half
+  const int n = static_cast<int>(s_end - s_begin);
+  const int64_t ss0 = a.start_src + (s_begin - first);  // src slot of the first token
+  // In the value layout element i of the chunk at element offset off of a tile
+  // holds token (r8 / 4) * 16 + 4 g + r8 % 4 and dim d, where g = off / (8 D),
+  // d = (off / 8) % D and r8 = off % 8 + i.
   // ---- values, phase 1: src chunks of the (at most two) src tiles the run
   // reads, scattered into LDS
   const int64_t st_lo = ss0 >> 5, st_hi = (ss0 + n - 1) >> 5;
-  const int cpt = 32 * D / kChunk;  // chunks per tile
+  const int lo_j = static_cast<int>(st_lo * 32 - ss0);  // run position of the first src tile's slot 0
   for (int x = tid; x < static_cast<int>(st_hi - st_lo + 1) * cpt; x += 256) {
-    const int64_t st = st_lo + x / cpt;
+    const int tl = x / cpt;              // src tile of the run (0 or 1)
     const int off = (x % cpt) * kChunk;  // element offset inside the tile
-    const int g = off / (8 * D), d = (off % (8 * D)) / 8, r0 = off % 8;
-    const Chunk raw = *reinterpret_cast<const Chunk*>(vp + st * 32 * D + off);
+    const int g = off / (8 * D), d = (off / 8) % D, r0 = off % 8;
+    const Chunk raw = *reinterpret_cast<const Chunk*>(vp + (st_lo + tl) * 32 * D + off);
     const T* e = reinterpret_cast<const T*>(&raw);
+    const int jb = lo_j + tl * 32 + 4 * g;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const int r8 = r0 + i;
-      const int64_t slot = st * 32 + (r8 >> 2) * 16 + 4 * g + (r8 & 3);
-      const int64_t j = slot - ss0;
+      const int j = jb + (r8 >> 2) * 16 + (r8 & 3);
       if (j >= 0 && j < n) vstage[j * D + d] = e[i];
     }
   }
   __syncthreads();
   // ---- keys: chunk pairs (token, dims c*kChunk.. and + D/2)
-  const int cph = half / kChunk;  // chunks per half
   for (int x = tid; x < n * cph; x += 256) {
     const int j = x / cph;
     const int d0 = (x % cph) * kChunk;
@@ -233,27 +238,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int tb = static_cast<int>(s_begin - t0), te = static_cast<int>(s_end - t0);
   for (int x = tid; x < cpt; x += 256) {
     const int off = x * kChunk;
-    const int g = off / (8 * D), d = (off % (8 * D)) / 8, r0 = off % 8;
-    int tmin = 64, tmax = -1;
+    const int g = off / (8 * D), d = (off / 8) % D, r0 = off % 8;
+    bool any = false, whole = true;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       const int r8 = r0 + i;
       const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
-      if (t >= tb && t < te) {
-        tmin = min(tmin, t);
-        tmax = max(tmax, t);
-      }
+      const bool in = t >= tb && t < te;
+      any = any || in;
+      whole = whole && in;
     }
-    if (tmax < 0) continue;  // no run token in this chunk
+    if (!any) continue;  // no run token in this chunk
     T* dst = vp + t0 * D + off;
     Chunk raw = {};
-    bool whole = true;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      const int r8 = r0 + i;
-      const int t = (r8 >> 2) * 16 + 4 * g + (r8 & 3);
-      whole = whole && t >= tb && t < te;
-    }
     if (!whole) raw = *reinterpret_cast<const Chunk*>(dst);  // keep tokens outside the run
     T* e = reinterpret_cast<T*>(&raw);
 #pragma unroll
@@ -452,12 +449,17 @@ hipError_t launch_append(const hw_pool& pool, int32_t src, int32_t dst, double t
   if (a.cap_src > 0 && grid > 0) {
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 g(static_cast<unsigned>(grid));
-    if (pool.dtype == HW_F32)
-      hipLaunchKernelGGL(append_kernel<float>, g, dim3(256), 0, s, a);
-    else if (pool.dtype == HW_BF16)
-      hipLaunchKernelGGL(append_kernel<uint16_t>, g, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(append_kernel<uint8_t>, g, dim3(256), 0, s, a);
+    const bool d128 = pool.head_dim == 128;
+    if (pool.dtype == HW_F32) {
+      if (d128) hipLaunchKernelGGL((append_kernel<float, 128>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((append_kernel<float, 64>), g, dim3(256), 0, s, a);
+    } else if (pool.dtype == HW_BF16) {
+      if (d128) hipLaunchKernelGGL((append_kernel<uint16_t, 128>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((append_kernel<uint16_t, 64>), g, dim3(256), 0, s, a);
+    } else {
+      if (d128) hipLaunchKernelGGL((append_kernel<uint8_t, 128>), g, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((append_kernel<uint8_t, 64>), g, dim3(256), 0, s, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
