@@ -141,6 +141,31 @@ struct ChunkOf {
   typedef typename std::conditional<kBytes == 16, u32x4, u32x2>::type type;
 };
 
+// A chunk's elements as doubles (exact).  FP8 codes widen through the
+// hardware's exact E4M3 -> bf16 conversion (unit scale).
+template <typename T, typename Chunk, int N>
+__device__ __forceinline__ void widen_chunk(const Chunk& c, double (&x)[N]) {
+  const T* e = reinterpret_cast<const T*>(&c);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = to_f64(e[i]);
+}
+template <>
+__device__ __forceinline__ void widen_chunk<uint8_t>(const ChunkOf<uint8_t>::type& c,
+                                                       double (&x)[8]) {
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t lo = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, false));
+    const uint32_t hi = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, true));
+    x[4 * w + 0] = __uint_as_float(lo << 16);
+    x[4 * w + 1] = __uint_as_float(lo & 0xffff0000u);
+    x[4 * w + 2] = __uint_as_float(hi << 16);
+    x[4 * w + 3] = __uint_as_float(hi & 0xffff0000u);
+  }
+}
+
+
 // One workgroup per (layer*kv head plane, destination tile).  A src key at
 // local position j moves to dst position len_dst + j: rotating it by len_dst
 // re-encodes it there (rho(rho(x, j), n) = rho(x, j + n)).
@@ -219,17 +244,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int d0 = (x % cph) * kChunk;
     const Chunk r0 = *reinterpret_cast<const Chunk*>(kp + key_offset(ss0 + j, d0, D));
     const Chunk r1 = *reinterpret_cast<const Chunk*>(kp + key_offset(ss0 + j, d0 + half, D));
-    const T* e0 = reinterpret_cast<const T*>(&r0);
-    const T* e1 = reinterpret_cast<const T*>(&r1);
     Chunk w0, w1;
     T* o0 = reinterpret_cast<T*>(&w0);
     T* o1 = reinterpret_cast<T*>(&w1);
+    double x0[kChunk], x1[kChunk];
+    widen_chunk<T>(r0, x0);
+    widen_chunk<T>(r1, x1);
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      const double x0 = to_f64(e0[i]), x1 = to_f64(e1[i]);
       const double c = cs[2 * (d0 + i)], s = cs[2 * (d0 + i) + 1];
-      o0[i] = round_to<T>(x0 * c - x1 * s);
-      o1[i] = round_to<T>(x1 * c + x0 * s);
+      o0[i] = round_to<T>(x0[i] * c - x1[i] * s);
+      o1[i] = round_to<T>(x1[i] * c + x0[i] * s);
     }
     *reinterpret_cast<Chunk*>(kp + key_offset(s_begin + j, d0, D)) = w0;
     *reinterpret_cast<Chunk*>(kp + key_offset(s_begin + j, d0 + half, D)) = w1;
