@@ -285,9 +285,13 @@ __device__ void emit_unit(const EpiArgs& a, PlanLds& pl, int g, int u, const flo
 }
 
 // ------------------------------------------------------------- MFMA kernel
-// bf16 and FP8 pools, rows R = W*G <= 16*NT.  Each of the NW waves owns every
-// NW-th tile of the workgroup's range and keeps its own (m, l, O^T) for all
-// rows; the waves' states are combined in LDS at the end.  Fragment layouts:
+// bf16 and FP8 pools, rows R = W*G <= 16*NT.  Eight waves.  Up to 32 rows
+// each wave owns every 8th tile of the workgroup's range and keeps its own
+// (m, l, O^T) for all rows.  Above 32 rows the rows split into two row groups
+// of ceil(NT/2) row tiles, four waves each: a wave owns every 4th tile for
+// its group's rows (the other group's wave reads the same tile, mostly from
+// L2), which keeps a wave's accumulators in its half of the register file.
+// The waves' states are combined in LDS at the end.  Fragment layouts:
 // hw_kernels.h.
 
 #ifndef HW_ISSUE_BEFORE_ROTATION
@@ -296,9 +300,9 @@ __device__ void emit_unit(const EpiArgs& a, PlanLds& pl, int g, int u, const flo
 constexpr int kIssueBeforeRotation = HW_ISSUE_BEFORE_ROTATION;
 // Rows up to which every wave's state has its own LDS slot (one-level combine).
 constexpr int kOneLevelRows = 20;
-// Waves of the MFMA kernel: 8 (two per SIMD) up to 32 rows; above that the
-// accumulators of 48..80 rows need the register file of one wave per SIMD.
-constexpr int mfma_waves(int NT) { return NT <= 2 ? 8 : 4; }
+// Waves of the MFMA kernel (two per SIMD) and its row groups.
+constexpr int mfma_waves(int) { return 8; }
+constexpr int mfma_row_groups(int NT) { return NT <= 2 ? 1 : 2; }
 
 template <int D, int NT, typename E>
 __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
@@ -306,14 +310,17 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   constexpr int EB = KvFrag<E>::kBytes;
   constexpr int NWAVE = mfma_waves(NT);
   constexpr int NTHR = 64 * NWAVE;
-  constexpr int NSTATE = NWAVE / 2;  // wave states held in LDS at once (two-level combine)
+  constexpr int RG = mfma_row_groups(NT);
+  constexpr int NTG = (NT + RG - 1) / RG;  // row tiles of a wave
+  constexpr int WPG = NWAVE / RG;          // waves of a row group
+  constexpr int NSTATE = WPG / 2;  // wave states held in LDS at once (two-level combine)
   constexpr int KS = D / 32;         // k-steps of the QK product
   constexpr int MT = D / 16;         // 16-dim tiles of the output
   constexpr int RP = 16 * NT;        // padded rows
   constexpr int HALF = D / 2;
   constexpr int ACC_STRIDE = D + 4;
   constexpr int kQf = NT <= 2 ? 6 : 1;  // blocks whose rotated queries are in LDS at once
-  constexpr bool kOneLevelOk = NWAVE == 8;
+  constexpr bool kOneLevelOk = NWAVE == 8 && RG == 1;
   constexpr int RC1 = RP < kOneLevelRows ? RP : kOneLevelRows;
   constexpr int kState1 = RC1 * ACC_STRIDE + 2 * RC1;
   constexpr int kState2 = RP * ACC_STRIDE + 2 * RP;
@@ -340,6 +347,12 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 15, q4 = lane >> 4;
+  // the wave's row group, its first row tile, its row tiles that exist and
+  // its place in the group (wave-uniform)
+  const int rg = RG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave) / WPG;
+  const int tb = rg * NTG;
+  const int ntv = RG == 1 ? NT : min(NTG, NT - tb);
+  const int wl = RG == 1 ? wave : __builtin_amdgcn_readfirstlane(wave) % WPG;
   if (tid == 0) HW_STAMP(0);
   int g, u;
   head_unit(a, &g, &u);
@@ -393,11 +406,11 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   const uint32_t koff = (q4 * 128 + li * 8) * EB;
   const uint32_t voff = (q4 * 8 * D + li * 8) * EB;
   Frag kf[2][KS], vf[MT];
-  bool rowvis[NT];
-  f32x4 acc[MT][NT];
-  float m_run[NT], l_run[NT];
+  bool rowvis[NTG];
+  f32x4 acc[MT][NTG];
+  float m_run[NTG], l_run[NTG];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < NTG; ++t) {
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
     rowvis[t] = false;
@@ -450,7 +463,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   // registers, the softmax and P.V update, the next tile's values requested.
   // Every wave keeps a tile in flight while it computes.
   int qb = -1;
-  int rowend[NT];
+  int rowend[NTG];
   const bf16x8* qf = qfs;
   // (`more` is a compile-time flag: with the next tile's loads conditional
   // the compiler cannot count the loads in flight and waits for all of them
@@ -459,23 +472,24 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
     constexpr bool more = decltype(more_c)::value;
     if (rt.b != qb) {
       qb = rt.b;
-      qf = qfs + (qb - gb) * NT * KS * 64;
+      qf = qfs + ((qb - gb) * NT + tb) * KS * 64;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int r = 16 * t + li;
+      for (int t = 0; t < NTG; ++t) {
+        const int r = 16 * (tb + t) + li;
         rowend[t] = r < nrows ? rows_lds[qb * qrows + fast_div(r, mG)] : -1;
         rowvis[t] = rowend[t] >= 0;
       }
     }
-    int rowlim[NT];
+    int rowlim[NTG];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) rowlim[t] = min(rt.valid - 1, rowend[t] - rt.first);
-    f32x4 sc[2][NT];
-    tile_scores<D, NT, E>(kf, qf, lane, sc);
+    for (int t = 0; t < NTG; ++t) rowlim[t] = min(rt.valid - 1, rowend[t] - rt.first);
+    f32x4 sc[2][NTG];
+    tile_scores<D, NTG, E>(kf, qf, lane, sc, ntv);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (more) load_keys<D, E>(krs, tn, koff, kf);
     __builtin_amdgcn_sched_barrier(0);
-    tile_update<D, NT, E>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run);
+    tile_update<D, NTG, E, (RG > 1)>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run,
+                                     ntv);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (more) load_values<D, E>(vrs, tn, voff, vf);
     __builtin_amdgcn_sched_barrier(0);
@@ -485,7 +499,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
 
   int done_tiles = 0;  // tiles this wave processed
   const int nvb = pl.w[kHdrNvb];
-  if (a.balance && plan_ok && nvb <= kQf && a.P > 1) {
+  if (RG == 1 && a.balance && plan_ok && nvb <= kQf && a.P > 1) {
     // Balanced: every visible block rotated at once; wave w of unit u takes
     // tile u*NWAVE + w, then tiles from the head's counter (tickets start
     // after the P*NWAVE first tiles; a wave without a first tile starts with
@@ -543,15 +557,18 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
       const int ge = min(gb + kQf, b_last + 1);
       const int t_lo = max(lo, pl.w[kPlanVbTile0 + gb]);
       const int t_hi = min(hi, pl.w[kPlanVbTile0 + ge]);
-      int j = t_lo + wave;
+      int j = t_lo + wl;
       int bcur = gb;
       TileRef rt = {0, 0, 0, 0u};
       uint32_t tile0 = 0;
       // mode 3: the upper half of the waves requests its first tiles at
       // once while the lower half rotates (a CU holds ~64 KB of requests:
       // half the waves' tiles), then requests its own
-      const bool early = kIssueBeforeRotation == 3 ? wave >= NWAVE / 2 : kIssueBeforeRotation >= 1;
-      const bool early_v = kIssueBeforeRotation == 3 ? early : kIssueBeforeRotation >= 2;
+      // (two row groups: not before the rotation, which reloads spilled
+      // values and would wait behind the tiles' loads)
+      const bool early = RG == 1 && (kIssueBeforeRotation == 3 ? wave >= NWAVE / 2
+                                                                : kIssueBeforeRotation >= 1);
+      const bool early_v = RG == 1 && (kIssueBeforeRotation == 3 ? early : kIssueBeforeRotation >= 2);
       if (j < t_hi) {
         rt = tile_ref<D, EB>(pl, j, bcur);
         tile0 = __builtin_amdgcn_readfirstlane(rt.byte);
@@ -568,7 +585,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
         if (!early) load_keys<D, E>(krs, tile0, koff, kf);
         if (!early_v) load_values<D, E>(vrs, tile0, voff, vf);
         for (;;) {
-          const int jn = j + NWAVE;
+          const int jn = j + WPG;
           ++done_tiles;
           if (jn >= t_hi) {
             step(rt, gb, kLast, 0u);
@@ -585,22 +602,24 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
 
   if (lane == 0) {
     HW_STAMP(3 + wave);
-    atomicAdd(&pl.tiles, done_tiles);
+    if (rg == 0) atomicAdd(&pl.tiles, done_tiles);  // (each row group takes every tile)
   }
   // full row sums (the four lanes of a row hold partial sums)
 #pragma unroll
-  for (int t = 0; t < NT; ++t) l_run[t] = sum_x32(sum_x16(l_run[t]));
+  for (int t = 0; t < NTG; ++t) l_run[t] = sum_x32(sum_x16(l_run[t]));
   // Combine the waves' states (O^T rows below R, m, l) in LDS.  When every
   // wave's state fits (R <= RC1 rows, 8 waves), each wave deposits its state
   // in its own slot as soon as its tiles are done; otherwise, after a
   // barrier, half of them at a time: the upper waves deposit, each lower wave
   // folds in its partner (same fragment positions, so lane-local), and the
-  // lower waves deposit.  Then every thread combines its share of the unit's
-  // R*D outputs over the deposited states.
+  // lower waves deposit (with row groups: the waves of a place in the group,
+  // one per group, share a slot, each writing its group's rows).  Then every
+  // thread combines its share of the unit's R*D outputs over the deposited
+  // states.
   auto deposit = [&](float* buf, int rc) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int r = 16 * t + li;
+    for (int t = 0; t < NTG; ++t) {
+      const int r = 16 * (tb + t) + li;
       if (r >= nrows) continue;
       if (q4 == 0) {
         buf[rc * ACC_STRIDE + r] = m_run[t];
@@ -619,13 +638,13 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
     rc = RC1;
   } else {
     __syncthreads();
-    if (wave >= NSTATE) deposit(ebuf + (wave - NSTATE) * kState2, RP);
+    if (wl >= NSTATE) deposit(ebuf + (wl - NSTATE) * kState2, RP);
     __syncthreads();
-    if (wave < NSTATE) {
-      const float* src = ebuf + wave * kState2;
+    if (wl < NSTATE) {
+      const float* src = ebuf + wl * kState2;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int r = 16 * t + li;
+      for (int t = 0; t < NTG; ++t) {
+        const int r = 16 * (tb + t) + li;
         if (r >= nrows) continue;
         const float m2 = src[RP * ACC_STRIDE + r];
         const float l2 = src[RP * ACC_STRIDE + RP + r];
@@ -641,7 +660,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
       }
     }
     __syncthreads();
-    if (wave < NSTATE) deposit(ebuf + wave * kState2, RP);
+    if (wl < NSTATE) deposit(ebuf + wl * kState2, RP);
     ns = NSTATE;
     sstride = kState2;
     rc = RP;

@@ -4,6 +4,7 @@
 // online-softmax update).  Internal linkage: each source gets its own copy.
 #pragma once
 
+#include <type_traits>
 #include <math.h>
 
 #include "hw_internal.h"
@@ -197,15 +198,17 @@ __device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t
 
 // S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
 // qf: this lane's rotated-query B fragments, [NT][KS] x 64 lanes in LDS.
+// Row tiles from ntv on (wave-uniform) have no fragments: their scores are 0.
 template <int D, int NT, typename E>
 __device__ __forceinline__ void tile_scores(const typename KvFrag<E>::type (&kf)[2][D / 32],
-                                            const bf16x8* qf, int lane, f32x4 (&sc)[2][NT]) {
+                                            const bf16x8* qf, int lane, f32x4 (&sc)[2][NT],
+                                            int ntv = NT) {
   constexpr int KS = D / 32;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KS && t < ntv; ++s) {
       const bf16x8 qv = qf[(t * KS + s) * 64 + lane];
       c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(bf16x8, KvFrag<E>::widen(kf[0][s])), qv, c0, 0, 0, 0);
@@ -221,63 +224,144 @@ __device__ __forceinline__ void tile_scores(const typename KvFrag<E>::type (&kf)
 // (m, l, O^T).  Row t keeps the tile's tokens up to rowlim[t] (its causal
 // limit, below `valid`); values of tokens at or past `valid` are zeroed.  The
 // row sum adds the bf16-rounded weights the P.V product uses, so numerator
-// and denominator carry the same weights.
-template <int D, int NT, typename E>
+// and denominator carry the same weights.  Row tiles from ntv on (wave-
+// uniform) are skipped.  BIG (kernels with many row tiles per wave, where
+// wave-uniform branches pay for the VALU work they skip): a row tile whose
+// rows all see the whole tile takes a path without the per-score masks, a
+// row tile's accumulators are rescaled only when some row's maximum moved
+// (the factor is otherwise exactly 1), and a whole tile's values are not
+// masked.
+template <int D, int NT, typename E, bool BIG = false>
 __device__ __forceinline__ void tile_update(const f32x4 (&sc)[2][NT],
                                             const typename KvFrag<E>::type (&vf)[D / 16],
                                             const bool (&rowvis)[NT], const int (&rowlim)[NT],
                                             int valid, int q4,
                                             f32x4 (&acc)[D / 16][NT], float (&m_run)[NT],
-                                            float (&l_run)[NT]) {
+                                            float (&l_run)[NT], int ntv = NT) {
   constexpr int MT = D / 16;
   bf16x8 pf[NT];
+  if constexpr (!BIG) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float sv[8];
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntv) break;
+      float sv[8];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = 16 * h2 + 4 * q4 + v;
-        sv[4 * h2 + v] = (rowvis[t] && tok <= rowlim[t]) ? sc[h2][t][v] : -INFINITY;
+        for (int v = 0; v < 4; ++v) {
+          const int tok = 16 * h2 + 4 * q4 + v;
+          sv[4 * h2 + v] = (rowvis[t] && tok <= rowlim[t]) ? sc[h2][t][v] : -INFINITY;
+        }
+      float mt = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+      mt = max_x32(max_x16(mt));
+      const float mn = fmaxf(m_run[t], mt);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float al = __builtin_amdgcn_exp2f(m_run[t] - mu);
+      float sum = 0.f;
+      bf16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        f[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[e] - mu));
+        sum += static_cast<float>(f[e]);
       }
-    float mt = sv[0];
+      pf[t] = f;
+      l_run[t] = l_run[t] * al + sum;
+      m_run[t] = mn;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-    mt = max_x32(max_x16(mt));
-    const float mn = fmaxf(m_run[t], mt);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float al = __builtin_amdgcn_exp2f(m_run[t] - mu);
-    float sum = 0.f;
-    bf16x8 f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      f[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[e] - mu));
-      sum += static_cast<float>(f[e]);
+      for (int m = 0; m < MT; ++m) acc[m][t] *= al;
     }
-    pf[t] = f;
-    l_run[t] = l_run[t] * al + sum;
-    m_run[t] = mn;
+    // tokens past the block's length may hold anything (even NaN): zero them
+    u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (valid < kTile) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m][t] *= al;
-  }
-  // tokens past the block's length may hold anything (even NaN): zero them
-  u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
-  if (valid < kTile) {
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const int t0 = 16 * ((2 * e2) >> 2) + 4 * q4 + ((2 * e2) & 3);
-      const int t1 = 16 * ((2 * e2 + 1) >> 2) + 4 * q4 + ((2 * e2 + 1) & 3);
-      keep[e2] = (t0 < valid ? 0x0000ffffu : 0u) | (t1 < valid ? 0xffff0000u : 0u);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int t0 = 16 * ((2 * e2) >> 2) + 4 * q4 + ((2 * e2) & 3);
+        const int t1 = 16 * ((2 * e2 + 1) >> 2) + 4 * q4 + ((2 * e2 + 1) & 3);
+        keep[e2] = (t0 < valid ? 0x0000ffffu : 0u) | (t1 < valid ? 0xffff0000u : 0u);
+      }
     }
-  }
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const u32x4 v = KvFrag<E>::widen(vf[m]) & keep;
+    for (int m = 0; m < MT; ++m) {
+      const u32x4 v = KvFrag<E>::widen(vf[m]) & keep;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pf[t],
-                                                          acc[m][t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) {
+        if (t >= ntv) break;
+        acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pf[t],
+                                                            acc[m][t], 0, 0, 0);
+      }
+    }
+  } else {
+    auto row_softmax = [&](int t, auto masked_c) {
+      constexpr bool masked = decltype(masked_c)::value;
+      float sv[8];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = 16 * h2 + 4 * q4 + v;
+          sv[4 * h2 + v] =
+              (!masked || (rowvis[t] && tok <= rowlim[t])) ? sc[h2][t][v] : -INFINITY;
+        }
+      float mt = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
+      mt = max_x32(max_x16(mt));
+      const float mn = fmaxf(m_run[t], mt);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float al = __builtin_amdgcn_exp2f(m_run[t] - mu);
+      float sum = 0.f;
+      bf16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        f[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[e] - mu));
+        sum += static_cast<float>(f[e]);
+      }
+      pf[t] = f;
+      l_run[t] = l_run[t] * al + sum;
+      m_run[t] = mn;
+      if (__builtin_amdgcn_ballot_w64(al != 1.f) != 0) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][t] *= al;
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntv) break;
+      if (__builtin_amdgcn_ballot_w64(!rowvis[t] || rowlim[t] < kTile - 1) == 0)
+        row_softmax(t, std::false_type{});
+      else
+        row_softmax(t, std::true_type{});
+    }
+    // tokens past the block's length may hold anything (even NaN): zero them
+    auto pv = [&](auto partial_c) {
+      constexpr bool partial = decltype(partial_c)::value;
+      u32x4 keep = u32x4{~0u, ~0u, ~0u, ~0u};
+      if (partial) {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int t0 = 16 * ((2 * e2) >> 2) + 4 * q4 + ((2 * e2) & 3);
+          const int t1 = 16 * ((2 * e2 + 1) >> 2) + 4 * q4 + ((2 * e2 + 1) & 3);
+          keep[e2] = (t0 < valid ? 0x0000ffffu : 0u) | (t1 < valid ? 0xffff0000u : 0u);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        u32x4 v = KvFrag<E>::widen(vf[m]);
+        if (partial) v &= keep;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t >= ntv) break;
+          acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v),
+                                                              pf[t], acc[m][t], 0, 0, 0);
+        }
+      }
+    };
+    if (valid < kTile)
+      pv(std::true_type{});
+    else
+      pv(std::false_type{});
   }
 }
 
