@@ -90,8 +90,15 @@ def test_fp8_single_visible_token_returns_its_value(api):
             np.testing.assert_allclose(got[w, h], V[h // 2, 0].numpy(), rtol=1e-6, atol=0)
 
 
-def test_fp8_chunk_matches_oracle():
-    W, n, Hq, Hkv, D, lens = 2, 3, 40, 8, 128, [4000, 333, 517]
+@pytest.mark.parametrize("case", [
+    # (W, n, Hq, Hkv, D, lens): rows = W * n * Hq / Hkv
+    (2, 3, 40, 8, 128, [4000, 333, 517]),        # 30 rows: one row group
+    (3, 3, 40, 8, 64, [700, 40, 41, 3]),         # 45 rows, D = 64: two row groups of 2 + 1 row tiles
+    (1, 12, 40, 8, 128, [5000, 900]),            # 60 rows
+    (4, 4, 40, 8, 128, [3000, 200, 5, 64, 77]),  # 80 rows: row groups of 3 + 2 row tiles
+])
+def test_fp8_chunk_matches_oracle(case):
+    W, n, Hq, Hkv, D, lens = case
     wl = _custom(W, Hq, Hkv, D, lens)
     s = Setup(wl, poison_unused=True)
     g = torch.Generator().manual_seed(9)
@@ -105,7 +112,10 @@ def test_fp8_chunk_matches_oracle():
                                 s.V[0].numpy(), tb, to, ne, np.array(lens, np.int32),
                                 np.asarray(s.pool.block_start, np.int64), wl.theta)
     assert rc == 0
-    assert_close(out.cpu().numpy(), ref, FP8, "fp8 chunk")
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, FP8, f"fp8 chunk {case}")
+    assert hw.hw_pool_status(s.pool) == 0
 
 
 @pytest.mark.parametrize("api", APIS)
