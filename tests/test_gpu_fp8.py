@@ -129,10 +129,11 @@ def test_fp8_unit_count_does_not_change_the_result(api):
         assert_close(got, ref, FP8, f"units {units} {api}")
 
 
-def test_fp8_append_matches_oracle_bit_exact():
+@pytest.mark.parametrize("D", [128, 64])
+def test_fp8_append_matches_oracle_bit_exact(D):
     theta = 1e6
     lens = [1000, 333, 17, 64]
-    wl = workloads.Workload("append_fp8", 3, 6, 2, 128, theta, FP8, 2, lens,
+    wl = workloads.Workload("append_fp8", 3, 6, 2, D, theta, FP8, 2, lens,
                             [2048, 352, 32, 64], 0.5, 11)
     s = Setup(wl, n_layers=2)
     src, dst = 1, 0

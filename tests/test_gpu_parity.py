@@ -290,11 +290,12 @@ def test_worker_without_tokens_gets_zeros_and_status(api):
 
 
 # ---------------------------------------------------------------- append (a5)
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_append_matches_oracle_bit_exact(dtype):
+def test_append_matches_oracle_bit_exact(dtype, D):
     theta = 1e6 if dtype == torch.bfloat16 else 1e4
     lens = [1000, 333, 17, 64]
-    wl = workloads.Workload("append", 3, 6, 2, 128, theta, dtype, 2, lens,
+    wl = workloads.Workload("append", 3, 6, 2, D, theta, dtype, 2, lens,
                             [2048, 352, 32, 64], 0.5, 11)
     s = Setup(wl, n_layers=2)
     src, dst = 1, 0
