@@ -95,7 +95,7 @@ def parse():
                          "one 80-row chunk call")
     ap.add_argument("--context", type=int, default=16384, help="cell: visible context tokens")
     ap.add_argument("--workers", type=int, default=4, help="cell: workers")
-    ap.add_argument("--loop-steps", type=int, default=512)
+    ap.add_argument("--loop-steps", type=int, default=2048)
     ap.add_argument("--api", choices=["decode", "plan_run"], default="decode",
                     help="decode: hw_attn_decode per layer (plan built in-kernel, the default); "
                          "plan_run: hw_attn_plan once per step + hw_attn_run per layer")
