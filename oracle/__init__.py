@@ -19,22 +19,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "hogwild_oracle.cpp")
-_LIB = os.path.join(_HERE, "libhogwild_oracle.so")
+# (HWO_LIB: another build of the same source, e.g. the sanitizer build of
+# tests/sanitize_host.py)
+_LIB = os.environ.get("HWO_LIB") or os.path.join(_HERE, "libhogwild_oracle.so")
 
 HWO_OK, HWO_EINVAL, HWO_ENOTOKENS, HWO_ECAPACITY = 0, 1, 2, 3
 HWO_F32, HWO_BF16, HWO_FP8 = 0, 1, 2
 FORM_DEFINITION, FORM_METHOD = 0, 1
 
 
-def build() -> str:
-    """Compile the oracle with g++ (fp64, no FMA contraction)."""
-    cmd = [
-        "g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
-        "-shared", "-fPIC", "-o", _LIB + ".tmp", _SRC,
-    ]
+def build(out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with g++ (fp64, no FMA contraction); sanitize: with
+    AddressSanitizer and UndefinedBehaviorSanitizer (host code only)."""
+    out = out or _LIB
+    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC"]
+    if sanitize:
+        cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=undefined"]
+    cmd += ["-o", out + ".tmp", _SRC]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 _lib = None
