@@ -491,6 +491,61 @@ def test_token_write_overflow_and_empty_block():
     assert torch.equal(K0, K1)
 
 
+def test_loop_checkpoint_resume_is_bit_exact():
+    """Checkpoint and resume: the pool, its lengths and the tables are caller-owned
+    tensors, so a checkpoint is a host copy of them.  A shortened config-5 loop run
+    straight through, and the same loop saved to host memory after step 99 (one
+    append done), restored into a freshly created pool and continued, give
+    bit-identical outputs at every later step and a bit-identical pool at the end
+    (the merge runs in a fixed order, so a call's result depends on its inputs only)."""
+    steps, L, cut = 160, 2, 100
+    wl = workloads.qwen3_loop(layers=L, common0=2048, steps=steps)
+    sched = workloads.loop_appends(wl, steps)
+    assert any(st < cut for st in sched) and any(st >= cut for st in sched)
+    gk = torch.Generator().manual_seed(23)
+    kn = [torch.randn(wl.W, wl.Hkv, wl.D, generator=gk).cuda() for _ in range(L)]
+    vn = [torch.randn(wl.W, wl.Hkv, wl.D, generator=gk).cuda() for _ in range(L)]
+
+    def run(s, lo, hi, outs):
+        out = torch.zeros(L, wl.W, wl.Hq, wl.D, device="cuda")
+        for step in range(lo, hi):
+            hw.hw_block_advance(s.pool, wl.worker_block)
+            hw.hw_build_combined_tables(s.pool, wl.W, wl.common_block, wl.worker_block, s.tables,
+                                        s.num_entries)
+            for layer in range(L):
+                hw.hw_block_write(s.pool, layer, wl.worker_block, kn[layer], vn[layer], wl.theta)
+                hw.hw_attn_decode(s.pool, layer, s.q[layer].cuda(), s.tables, s.num_entries,
+                                  wl.theta, out[layer], s.ws)
+            outs[step] = out.cpu()
+            if step in sched:
+                b = wl.worker_block[sched[step]]
+                hw.hw_block_append(s.pool, b, wl.common_block, wl.theta)
+                hw.hw_block_reset(s.pool, b)
+        torch.cuda.synchronize()
+
+    _say("  straight run")
+    a = Setup(wl, n_layers=L)
+    outs_a = {}
+    run(a, 0, steps, outs_a)
+    _say("  run to the checkpoint, save, restore into a new pool, continue")
+    b = Setup(wl, n_layers=L)
+    outs_b = {}
+    run(b, 0, cut, outs_b)
+    ck = {"k": b.pool.k.cpu(), "v": b.pool.v.cpu(), "len": b.pool.block_len.cpu()}
+    del b
+    torch.cuda.empty_cache()
+    c = Setup(wl, n_layers=L)
+    c.pool.k.copy_(ck["k"])
+    c.pool.v.copy_(ck["v"])
+    c.pool.block_len.copy_(ck["len"])
+    run(c, cut, steps, outs_b)
+    for step in range(steps):
+        assert torch.equal(outs_a[step], outs_b[step]), f"step {step}"
+    assert torch.equal(a.pool.block_len.cpu(), c.pool.block_len.cpu())
+    assert torch.equal(a.pool.k.cpu(), c.pool.k.cpu()) and torch.equal(a.pool.v.cpu(), c.pool.v.cpu())
+    assert hw.hw_pool_status(a.pool) == 0 and hw.hw_pool_status(c.pool) == 0
+
+
 # ------------------------------------------------- generation loop (config 5)
 def test_generation_loop_matches_oracle():
     """A shortened config-5 loop (Qwen3-8B heads, 4 workers): every step each
