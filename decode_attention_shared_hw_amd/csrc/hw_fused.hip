@@ -13,9 +13,9 @@
 //     previous call with this workspace (a hint: within a decode step every
 //     layer's call has the same plan), through range-checked offsets, and keep
 //     it when the plan confirms it;
-//  2. the front waves rotate the stacked query rows of each visible block by
-//     their delta i_q - lag - view_offset (key design 1: only the queries are
-//     rotated, never the cache)                                          [a2]
+//  2. all eight waves rotate the stacked query rows of each visible block by
+//     their delta i_q - lag - view_offset once the plan is complete (key
+//     design 1: only the queries are rotated, never the cache)          [a2]
 //  3. every wave streams its tiles (every 8th tile of the unit's range) with an
 //     online softmax in the exp2 domain (split-K / Flash-Decoding)      [a3]
 //  4. the waves' states are combined in LDS and the unit's partial (m, l, acc)
@@ -541,19 +541,21 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   // first tile is requested before its rotation; in the first group the back
   // waves keep their speculative tile when the plan confirms it.
   uint32_t first = 0xffffffffu;  // this wave's first tile (byte offset), none: all ones
-  // the first group's rotation (front waves), published to the back waves
+  // the first group's rotation by all eight waves once the plan is complete
+  // (build_plan ends with the front waves' barrier): the front waves publish
+  // it, the back waves (their speculative tiles requested) wait for it
   if (front) {
-    if (plan.lo < plan.hi && !(plan.flags & HW_DEV_SPIN_LIMIT)) {
-      const int b_first = plan.b_first;
-      const int b_last = plan.b_last;
-      rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NF);
-    }
-    front_sync();
     if (lane == 0)
       __hip_atomic_fetch_add(&sync_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
     lds_wait_at_least(&sync_ctr[2], kFront, &plan.flags, a.spin_limit);
   }
+  if (plan.lo < plan.hi && !(plan.flags & HW_DEV_SPIN_LIMIT)) {
+    const int b_first = plan.b_first;
+    const int b_last = plan.b_last;
+    rotate_blocks(b_first, min(b_first + kQfBlocks, b_last + 1), NTHR);
+  }
+  __syncthreads();  // the rotated queries are in LDS
   if (plan.lo < plan.hi && !(plan.flags & HW_DEV_SPIN_LIMIT)) {
     const int b_first = plan.b_first;
     const int b_last = plan.b_last;
