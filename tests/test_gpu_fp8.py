@@ -96,6 +96,7 @@ def test_fp8_single_visible_token_returns_its_value(api):
     (3, 3, 40, 8, 64, [700, 40, 41, 3]),         # 45 rows, D = 64: two row groups of 2 + 1 row tiles
     (1, 12, 40, 8, 128, [5000, 900]),            # 60 rows
     (4, 4, 40, 8, 128, [3000, 200, 5, 64, 77]),  # 80 rows: row groups of 3 + 2 row tiles
+    (2, 7, 40, 8, 128, [2500, 130, 7]),          # 70 rows
 ])
 def test_fp8_chunk_matches_oracle(case):
     W, n, Hq, Hkv, D, lens = case

@@ -398,6 +398,8 @@ def test_interleaved_layout_attention_matches_oracle(path):
     (4, 4, 40, 8, 128, [3000, 200, 5, 64, 77]),  # four 4-token block headers at G = 5: 80 rows
     (1, 12, 40, 8, 128, [5000, 900]),            # a 12-token prompt of one worker: 60 rows
     (3, 3, 40, 8, 64, [700, 40, 41, 3]),         # 45 rows, D = 64
+    (3, 3, 40, 8, 128, [1500, 70, 9, 300]),      # 45 rows, D = 128: row groups of 2 + 1 row tiles
+    (2, 7, 40, 8, 128, [2500, 130, 7]),          # 70 rows: the second group's last row tile partly used
 ])
 def test_chunk_matches_oracle(path, case):
     W, n, Hq, Hkv, D, lens = case
