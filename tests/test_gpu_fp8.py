@@ -97,6 +97,7 @@ def test_fp8_single_visible_token_returns_its_value(api):
     (1, 12, 40, 8, 128, [5000, 900]),            # 60 rows
     (4, 4, 40, 8, 128, [3000, 200, 5, 64, 77]),  # 80 rows: row groups of 3 + 2 row tiles
     (2, 7, 40, 8, 128, [2500, 130, 7]),          # 70 rows
+    (4, 4, 40, 8, 64, [900, 60, 5, 64, 33]),     # 80 rows, D = 64
 ])
 def test_fp8_chunk_matches_oracle(case):
     W, n, Hq, Hkv, D, lens = case

@@ -400,6 +400,8 @@ def test_interleaved_layout_attention_matches_oracle(path):
     (3, 3, 40, 8, 64, [700, 40, 41, 3]),         # 45 rows, D = 64
     (3, 3, 40, 8, 128, [1500, 70, 9, 300]),      # 45 rows, D = 128: row groups of 2 + 1 row tiles
     (2, 7, 40, 8, 128, [2500, 130, 7]),          # 70 rows: the second group's last row tile partly used
+    (4, 4, 40, 8, 64, [900, 60, 5, 64, 33]),     # 80 rows, D = 64: row groups of 3 + 2 row tiles
+    (1, 16, 32, 8, 64, [1300, 200]),             # 64 rows, D = 64: row groups of 2 + 2 row tiles
 ])
 def test_chunk_matches_oracle(path, case):
     W, n, Hq, Hkv, D, lens = case
