@@ -209,6 +209,30 @@ def calibrate_copy(torch, mib):
     del src, dst
 
 
+def copy_bandwidth(torch, mib=1024, reps=20):
+    """Device-to-device copy rate of this GPU in the same run (read + written
+    bytes per second, GB/s): a practical ceiling next to the 8 TB/s peak.  One
+    `mib` MiB buffer copied `reps` times between HIP events on one stream."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for _ in range(3):
+            dst.copy_(src)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(st)
+        st.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / sec / 1e9
+
+
 def run_cell(args, reps=10):
     """One point of the workers x context grid (40 q / 8 kv heads, D 128, bf16):
     per-layer time of hw_attn_decode in graph replay, cycling layers of distinct K/V."""
@@ -649,6 +673,7 @@ def main():
     pool, q, host_layer0 = make_step_pool(hw, torch, workloads, wl, not args.no_cpu_baseline)
     t = time_step(args, hw, torch, np, wl, pool, q, api=args.api)
     calibrate_copy(torch, args.calibrate_copy)
+    copy_gbs = copy_bandwidth(torch)
 
     ms_per_step = t["ms_per_step"]
     step_s = ms_per_step / 1e3
@@ -688,6 +713,9 @@ def main():
             "avg_launch_us": dec_avg,
             "p10_us": float(np.percentile(dec_us, 10)),
             "p90_us": float(np.percentile(dec_us, 90)),
+            "copy_gbs": copy_gbs,
+            "frac_of_copy": achieved / copy_gbs,
+            "copy_note": "1 GiB device-to-device copy in the same run, read + written bytes",
         },
         "us_per_layer": ms_per_step * 1e3 / L,
         "append_us": float(np.mean(t["app_us"])),
