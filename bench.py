@@ -209,6 +209,29 @@ def calibrate_copy(torch, mib):
     del src, dst
 
 
+def gpu_clocks(torch):
+    """The GPU's DPM clock levels from sysfs (read-only files; no tool is run),
+    matched to device 0 by its PCI address: {"pci", "sclk", "mclk"}, each
+    clock a list of levels with the current one marked '*', or None."""
+    import glob
+
+    try:
+        p = torch.cuda.get_device_properties(0)
+        slot = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        for dev in glob.glob("/sys/class/drm/card*/device"):
+            with open(os.path.join(dev, "uevent")) as f:
+                if f"PCI_SLOT_NAME={slot}" not in f.read().split():
+                    continue
+            res = {"pci": slot}
+            for k in ("sclk", "mclk"):
+                with open(os.path.join(dev, f"pp_dpm_{k}")) as f:
+                    res[k] = [ln.strip() for ln in f if ln.strip()]
+            return res
+    except Exception:  # metadata only: a host without these files reports None
+        pass
+    return None
+
+
 def copy_bandwidth(torch, mib=1024, reps=20):
     """Device-to-device copy rate of this GPU in the same run (read + written
     bytes per second, GB/s): a practical ceiling next to the 8 TB/s peak.  One
@@ -720,6 +743,7 @@ def main():
         "us_per_layer": ms_per_step * 1e3 / L,
         "append_us": float(np.mean(t["app_us"])),
         "wall_s": t["wall"],
+        "gpu_clocks": gpu_clocks(torch),
         "device_status": t["flags"],
     }
     if not args.no_extras and path != hw.PATH_VALU:
