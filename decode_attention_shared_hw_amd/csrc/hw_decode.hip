@@ -313,6 +313,10 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   constexpr int RG = mfma_row_groups(NT);
   constexpr int NTG = (NT + RG - 1) / RG;  // row tiles of a wave
   constexpr int WPG = NWAVE / RG;          // waves of a row group
+  // K/V cache policy: with row groups each tile is read by one wave of each
+  // group, and loads with the default policy let the second read find it in
+  // L2 (an 80-row call: 32.9 us, against 35.2 with non-temporal loads)
+  constexpr int KV_POL = RG > 1 ? 0 : kPolicyNT;
   constexpr int NSTATE = WPG / 2;  // wave states held in LDS at once (two-level combine)
   constexpr int KS = D / 32;         // k-steps of the QK product
   constexpr int MT = D / 16;         // 16-dim tiles of the output
@@ -486,12 +490,12 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
     f32x4 sc[2][NTG];
     tile_scores<D, NTG, E>(kf, qf, lane, sc, ntv);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (more) load_keys<D, E>(krs, tn, koff, kf);
+    if constexpr (more) load_keys<D, E, KV_POL>(krs, tn, koff, kf);
     __builtin_amdgcn_sched_barrier(0);
     tile_update<D, NTG, E, (RG > 1)>(sc, vf, rowvis, rowlim, rt.valid, q4, acc, m_run, l_run,
                                      ntv);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (more) load_values<D, E>(vrs, tn, voff, vf);
+    if constexpr (more) load_values<D, E, KV_POL>(vrs, tn, voff, vf);
     __builtin_amdgcn_sched_barrier(0);
   };
   const std::true_type kMore;
@@ -572,8 +576,8 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
       if (j < t_hi) {
         rt = tile_ref<D, EB>(pl, j, bcur);
         tile0 = __builtin_amdgcn_readfirstlane(rt.byte);
-        if (early) load_keys<D, E>(krs, tile0, koff, kf);
-        if (early_v) load_values<D, E>(vrs, tile0, voff, vf);
+        if (early) load_keys<D, E, KV_POL>(krs, tile0, koff, kf);
+        if (early_v) load_values<D, E, KV_POL>(vrs, tile0, voff, vf);
       }
       if (gb != b_first) __syncthreads();  // the previous group's fragments are consumed
       if (kIssueBeforeRotation != 3 || wave < NWAVE / 2)
@@ -582,8 +586,8 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
       if (tid == 0 && gb == b_first) HW_STAMP(2);
       qb = -1;
       if (j < t_hi) {
-        if (!early) load_keys<D, E>(krs, tile0, koff, kf);
-        if (!early_v) load_values<D, E>(vrs, tile0, voff, vf);
+        if (!early) load_keys<D, E, KV_POL>(krs, tile0, koff, kf);
+        if (!early_v) load_values<D, E, KV_POL>(vrs, tile0, voff, vf);
         for (;;) {
           const int jn = j + WPG;
           ++done_tiles;

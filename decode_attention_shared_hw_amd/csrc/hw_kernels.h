@@ -141,16 +141,19 @@ __device__ uint64_t g_stamps[4096 * 32];
 // load 16 bytes and use them as they are; FP8 E4M3 pools load 8 bytes, which
 // are widened to bf16 (exactly: every E4M3 value is a bf16 value) just before
 // the product that consumes them, so the registers of a tile in flight hold
-// the narrow codes.  Every K/V fragment is read exactly once per call: the
-// loads carry the non-temporal policy.
+// the narrow codes.  POL is the loads' cache policy: non-temporal where every
+// K/V fragment is read exactly once per call; the default (0) where two waves
+// read each tile (the row groups of the run kernel), so that the second read
+// finds it in L2.
 template <typename E>
 struct KvFrag;
 template <>
 struct KvFrag<uint16_t> {
   typedef u32x4 type;
   static constexpr int kBytes = 2;
+  template <int POL>
   __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kPolicyNT);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, POL);
   }
   __device__ static u32x4 widen(const type& f) { return f; }
 };
@@ -158,8 +161,9 @@ template <>
 struct KvFrag<uint8_t> {
   typedef u32x2 type;
   static constexpr int kBytes = 1;
+  template <int POL>
   __device__ static type load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kPolicyNT);
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, POL);
   }
   template <bool HI>
   __device__ static uint32_t pair(uint32_t w) {
@@ -177,7 +181,7 @@ struct KvFrag<uint8_t> {
 // resource range-checks the lane offsets; the tile offset is inside the plane
 // by construction (a tile lies inside its block's capacity, whose slots the
 // host checked against the plane).
-template <int D, typename E>
+template <int D, typename E, int POL = kPolicyNT>
 __device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t tile, uint32_t koff,
                                           typename KvFrag<E>::type (&kf)[2][D / 32]) {
   constexpr int B = KvFrag<E>::kBytes;
@@ -185,15 +189,16 @@ __device__ __forceinline__ void load_keys(__amdgpu_buffer_rsrc_t krs, uint32_t t
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
-      kf[h2][s] = KvFrag<E>::load(krs, koff + (h2 * 16 * D + 4 * s * 128) * B, tile);
+      kf[h2][s] = KvFrag<E>::template load<POL>(krs, koff + (h2 * 16 * D + 4 * s * 128) * B, tile);
 }
 
-template <int D, typename E>
+template <int D, typename E, int POL = kPolicyNT>
 __device__ __forceinline__ void load_values(__amdgpu_buffer_rsrc_t vrs, uint32_t tile,
                                             uint32_t voff, typename KvFrag<E>::type (&vf)[D / 16]) {
   constexpr int B = KvFrag<E>::kBytes;
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m) vf[m] = KvFrag<E>::load(vrs, voff + 16 * m * 8 * B, tile);
+  for (int m = 0; m < D / 16; ++m)
+    vf[m] = KvFrag<E>::template load<POL>(vrs, voff + 16 * m * 8 * B, tile);
 }
 
 // S^T for one tile: sc[h][t] holds tokens 16h + 4*q4 + v of rows 16t + li.
