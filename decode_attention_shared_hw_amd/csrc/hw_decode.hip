@@ -332,7 +332,10 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
   constexpr int kQfFloats = kQf * NT * KS * 64 * 4;
   __shared__ PlanLds pl;
   __shared__ uint64_t fracs[HALF];
-  __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
+  // the head's query rows, row stride D + 8: the rotation reads one column of
+  // 16 rows at a time, which then falls into distinct LDS banks
+  constexpr int QS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t qs[RP * QS];
   __shared__ __attribute__((aligned(16))) float qbuf[kQfFloats];
   // the waves' softmax states (epilogue); apart from qbuf, so that a wave
   // done with its tiles deposits its state while the others still stream
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
 #pragma unroll
   for (int k = 0; k < kQRegs; ++k) {
     const int x = tid + k * NTHR;
-    if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
+    if (x < kQVec) *reinterpret_cast<u32x4*>(qs + (8 * x) / D * QS + (8 * x) % D) = qv[k];
   }
   __syncthreads();
   if (tid == 0) HW_STAMP(1);
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(64 * mfma_waves(NT)) void run_mfma(RunArgs a) {
       if (r < nrows) re = rows_lds[(gb + bi) * qrows + fast_div(r, mG)];
       const float sc = re >= 0 ? qsc : 0.f;
       const uint32_t delta = static_cast<uint32_t>(re >= 0 ? re : 0);
-      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
+      const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * QS + d0);
       uint32_t* lo4 = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh) * 64 + ln);
       uint32_t* hi4 = reinterpret_cast<uint32_t*>(qfs + ((bi * NT + t) * KS + sh + KS / 2) * 64 + ln);
       // (rolled: this code runs once per launch and is fetched cold)

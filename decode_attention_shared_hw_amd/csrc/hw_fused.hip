@@ -356,7 +356,10 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
   constexpr int kQfFloats = kQfBlocks * NT * KS * 64 * 4;  // rotated-query fragments
   constexpr int kEpiFloats = cmax(NWAVE * kState1, NSTATE * kState2);
   __shared__ Plan plan;
-  __shared__ __attribute__((aligned(16))) uint16_t qs[RP * D];
+  // the head's query rows, row stride D + 8: the rotation reads one column of
+  // 16 rows at a time, which then falls into distinct LDS banks
+  constexpr int QS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t qs[RP * QS];
   // the rotated-query fragments of up to kQfBlocks blocks (main loop)
   __shared__ __attribute__((aligned(16))) float qbuf[kQfFloats];
   // the waves' softmax states (epilogue); apart from qbuf, so that a wave
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < kQRegs; ++k) {
         const int x = tid + k * NF;
-        if (x < kQVec) *reinterpret_cast<u32x4*>(qs + 8 * x) = qv[k];
+        if (x < kQVec) *reinterpret_cast<u32x4*>(qs + (8 * x) / D * QS + (8 * x) % D) = qv[k];
       }
       // the plan's loads are back: the back waves' tiles may now fill the
       // memory queues (issued earlier, they delay these small loads by the
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(kMfmaThreads) void decode_mfma(DecodeArgs a) {
     const int w = plan.row_w[r];
     const long long iq_lag = plan.iq[w] - plan.row_lag[r];
     const int d0 = 8 * (4 * sh + (ln >> 4));  // < HALF; its partner dims are d0 + HALF
-    const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * D + d0);
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(qs + r * QS + d0);
     uint32_t xw[4], yw[4];
     uint64_t fr[8];
 #pragma unroll
