@@ -432,6 +432,48 @@ def test_chunk_matches_oracle(path, case):
     assert hw.hw_pool_status(s.pool) == 0
 
 
+@pytest.mark.parametrize("path", [hw.PATH_MFMA, MFMA_RUN])
+@pytest.mark.parametrize("n", [3, 4])
+def test_chunk_partial_visibility_and_entry_order(path, n):
+    """Chunks over views that leave blocks out, list entries out of order and
+    shift offsets: 4 workers x n tokens x G = 5 (60 or 80 rows, the row-group
+    kernel).  Worker 0 sees the common block and its own; worker 1 three
+    blocks in reversed order; worker 2 only the common block, shifted (its
+    chunk is then the common block's last n tokens); worker 3 every block, its
+    own one first at a far offset."""
+    _tune(path, 0)
+    lens = [900, 60, 5, 64, 33]
+    wl = _custom(4, 40, 8, 128, lens)
+    s = Setup(wl, poison_unused=True)
+    tables = np.zeros((4, 5, 2), np.int32)
+    ne = np.array([2, 3, 1, 5], np.int32)
+    tables[0, :2] = [(0, 0), (1, 900)]
+    tables[1, :3] = [(3, 965), (2, 1029), (0, 0)]
+    tables[2, :1] = [(0, 500)]
+    tables[3, :5] = [(4, 2000), (1, 900), (0, 0), (2, 960), (3, 965)]
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(4, n, 40, 128, generator=g).to(wl.dtype)
+    out = torch.full((4, n, 40, 128), float("nan"), device="cuda")
+    ws = hw.alloc_workspace(s.pool, 4 * n, 40)
+    tb_dev, ne_dev = torch.from_numpy(tables).cuda(), torch.from_numpy(ne).cuda()
+    if path == MFMA_RUN:
+        plan = hw.alloc_plan(s.pool, 4, 40, chunk=n)
+        hw.hw_attn_plan(s.pool, tb_dev, ne_dev, plan, 40, chunk=n)
+        hw.hw_attn_run(s.pool, 0, q.cuda(), plan, wl.theta, out, ws)
+    else:
+        hw.hw_attn_chunk(s.pool, 0, q.cuda(), tb_dev, ne_dev, wl.theta, out, ws)
+    torch.cuda.synchronize()
+    ref, rc = oracle.attn_chunk(oracle.FORM_METHOD, q.double().numpy(), s.K[0].double().numpy(),
+                                s.V[0].double().numpy(), tables[..., 0].copy(),
+                                tables[..., 1].copy(), ne, np.array(lens, np.int32),
+                                np.asarray(s.pool.block_start, np.int64), wl.theta)
+    assert rc == 0
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, torch.bfloat16, f"chunk partial visibility n={n} path {path}")
+    assert hw.hw_pool_status(s.pool) == 0
+
+
 def test_chunk_of_one_equals_decode():
     wl = _custom(4, 40, 8, 128, [2000, 300, 31, 64, 5])
     s = Setup(wl)
