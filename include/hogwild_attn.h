@@ -409,7 +409,9 @@ hw_status hw_pool_status(const hw_pool* pool, int32_t* flags, int32_t clear, voi
  *                   serves faster take more tiles (the MFMA path, when
  *                   every visible block's rotated queries fit in LDS: at
  *                   most 6 visible blocks); results then vary in the last
- *                   bits from run to run.
+ *                   bits from run to run, and the per-tile counter atomics
+ *                   cost more than they balance (the 16K QwQ step's plan +
+ *                   run call: 30.2 against 19.9 us).
  * Returns HW_EINVAL for values out of range.
  */
 hw_status hw_set_tuning(int32_t path, int32_t units_per_head, int32_t balance);
